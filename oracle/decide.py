@@ -1,0 +1,78 @@
+"""Per-pass decisions (oracle; test infrastructure only).
+
+  * byte_choice: the greedy byte and its confidence from one row's logits;
+  * unmask_commit: confidence-threshold unmasking with the forced fallback,
+    or one-step filling;
+  * verify_accept: the greedy exact-match verification of a draft.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MASK = 256
+
+
+def byte_choice(z):
+    """Greedy byte and confidence of one row of 257 logits.
+
+    A masked slot is filled with a byte, so the [MASK] logit (id 256) takes
+    no part.  Confidence is the largest predicted probability (pytorch.kr
+    Fast-BLT summary, "block unmasking strategies": the maximum predicted
+    probability of a position is its confidence).  Ties go to the lowest
+    byte id.  Returns (byte, confidence, top-2 logit gap).
+    """
+    z = np.asarray(z, dtype=np.float64)[:256]
+    m = z.max()
+    b = int(np.flatnonzero(z == m)[0])
+    conf = 1.0 / np.exp(z - m).sum()
+    rest = np.delete(z, b)
+    return b, float(conf), float(m - rest.max())
+
+
+def unmask_commit(block, choice, conf, alpha, one_step=False):
+    """Commit block positions after one decoder pass.
+
+    block: current block tokens (256 = still masked); choice/conf: per block
+    position greedy byte and confidence from this pass.  Rule (pytorch.kr
+    summary, "block unmasking strategies"): every masked position whose
+    confidence exceeds alpha is committed at once; if none does, the single
+    most confident masked position is committed so decoding always advances
+    (ties to the lowest position).  One-step diffusion fills every masked
+    position in a single pass (the BLT-DV one-step draft).  Committed
+    positions stay committed.  Returns (new block, committed positions).
+    """
+    block = list(block)
+    masked = [i for i, t in enumerate(block) if t == MASK]
+    if not masked:
+        return block, []
+    if one_step:
+        chosen = masked
+    else:
+        chosen = [i for i in masked if conf[i] > alpha]
+        if not chosen:
+            best = max(conf[i] for i in masked)
+            chosen = [min(i for i in masked if conf[i] == best)]
+    for i in chosen:
+        block[i] = int(choice[i])
+    return block, chosen
+
+
+def verify_accept(draft, pred):
+    """Greedy exact-match verification.
+
+    draft: the r draft bytes x'_{l+1..l+r}; pred: the r+1 greedy predictions
+    y_l..y_{l+r}, pred[j] being the byte the causal pass predicts after
+    position l+j.  Walking i = l+1..l+r, a draft byte is accepted while it
+    equals the prediction made at the position before it; at the first
+    mismatch the prediction replaces it and the walk stops; if every draft
+    byte matches, the prediction after the last one is a free extra byte
+    (pytorch.kr summary, "BLT-S and BLT-DV": the shared verification steps).
+    Returns (accepted count a, the byte appended after them).
+    """
+    r = len(draft)
+    if len(pred) != r + 1:
+        raise ValueError("need r + 1 predictions")
+    a = 0
+    while a < r and int(draft[a]) == int(pred[a]):
+        a += 1
+    return a, int(pred[a])

@@ -1,0 +1,403 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a
+closed form, a textbook or library routine in a special case, brute force
+on tiny inputs, an invariant, or a value the pages print.  They are chosen
+so that a plausible slip (a dropped term, a wrong sign or index, a
+transposed operand) fails at least one of them.
+"""
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as Fnn
+
+import bltgen
+from oracle import cache, decide, loops, model, patcher, proxy
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+MICRO = bltgen.WORKLOADS[0].replace(n_layers=2, d_model=32, n_heads=2, d_ffn=64, d_global=16,
+                                    prompt_len=12, prompt_patches=5, n_gen=16)
+
+
+def micro(gains="random", **kw):
+    wl = MICRO.replace(**kw)
+    W = model.as64(bltgen.make_weights(wl, gains=gains))
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    inp["latents"] = inp["latents"].astype(np.float64)
+    return wl, W, inp
+
+
+# ---------------------------------------------------------------- attention
+def brute_attention(q, k, v, allow):
+    n, H, dh = q.shape
+    out = np.zeros_like(q)
+    for h in range(H):
+        for i in range(n):
+            js = [j for j in range(k.shape[0]) if allow[i, j]]
+            sc = [sum(q[i, h, e] * k[j, h, e] for e in range(dh)) / dh ** 0.5 for j in js]
+            mx = max(sc)
+            w = [np.exp(s - mx) for s in sc]
+            tot = sum(w)
+            for j, wj in zip(js, w):
+                out[i, h] += (wj / tot) * v[j, h]
+    return out
+
+
+def test_masked_attention_matches_brute_force():
+    rng = np.random.default_rng(1)
+    for n, m, H, dh in [(5, 7, 2, 4), (9, 9, 3, 2), (1, 4, 1, 8)]:
+        q, k, v = (rng.standard_normal((x, H, dh)) for x in (n, m, m))
+        allow = rng.random((n, m)) < 0.5
+        allow[np.arange(n), rng.integers(0, m, n)] = True
+        np.testing.assert_allclose(model.masked_attention(q, k, v, allow),
+                                   brute_attention(q, k, v, allow), rtol=1e-12, atol=1e-12)
+
+
+def test_masked_attention_matches_torch_sdpa():
+    rng = np.random.default_rng(2)
+    n, H, dh = 11, 3, 8
+    q, k, v = (rng.standard_normal((n, H, dh)) for _ in range(3))
+    allow = model.blt_d_mask(7, 4)
+    ref = Fnn.scaled_dot_product_attention(
+        torch.tensor(q).transpose(0, 1), torch.tensor(k).transpose(0, 1),
+        torch.tensor(v).transpose(0, 1), attn_mask=torch.tensor(allow)).transpose(0, 1).numpy()
+    np.testing.assert_allclose(model.masked_attention(q, k, v, allow), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_blt_d_mask_structure():
+    a = model.blt_d_mask(3, 2)
+    # prefix causal, prefix never reads the block; block reads prefix + whole block
+    assert a.tolist() == [
+        [1, 0, 0, 0, 0], [1, 1, 0, 0, 0], [1, 1, 1, 0, 0], [1, 1, 1, 1, 1], [1, 1, 1, 1, 1]]
+    c = model.blt_d_mask(3, 2, block_causal=True)
+    assert c.tolist() == np.tril(np.ones((5, 5), dtype=bool)).tolist()
+
+
+# ---------------------------------------------------------------- RoPE / norms
+def test_rope_is_complex_rotation_of_half_pairs():
+    rng = np.random.default_rng(3)
+    n, H, dh, theta = 6, 2, 8, 10000.0
+    x = rng.standard_normal((n, H, dh))
+    pos = np.array([0, 1, 5, 77, 1000, 4095])
+    got = model.rope(x, pos, theta)
+    half = dh // 2
+    z = x[..., :half] + 1j * x[..., half:]
+    for j in range(half):
+        z[..., j] *= np.exp(1j * pos[:, None] * theta ** (-2.0 * j / dh))
+    np.testing.assert_allclose(got, np.concatenate([z.real, z.imag], -1), atol=1e-12)
+
+
+def test_rope_identity_at_zero_and_relative():
+    rng = np.random.default_rng(4)
+    q = rng.standard_normal((1, 1, 16))
+    k = rng.standard_normal((1, 1, 16))
+    np.testing.assert_array_equal(model.rope(q, [0], 1e4), q)
+    s = [float((model.rope(q, [p + c], 1e4) * model.rope(k, [3 + c], 1e4)).sum())
+         for p, c in [(9, 0), (9, 17), (9, 1234)]]
+    assert np.allclose(s, s[0], atol=1e-10)
+
+
+def test_rms_norm_matches_torch_and_invariants():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((4, 32)) * 3
+    g = rng.uniform(0.5, 1.5, 32)
+    ref = Fnn.rms_norm(torch.tensor(x), (32,), weight=torch.tensor(g), eps=1e-5).numpy()
+    np.testing.assert_allclose(model.rms_norm(x, g, 1e-5), ref, rtol=1e-12)
+    u = model.rms_norm(x, np.ones(32), 0.0)
+    np.testing.assert_allclose(np.sqrt((u ** 2).mean(-1)), 1.0, rtol=1e-12)
+
+
+# ---------------------------------------------------------------- cross-attention
+def test_single_key_cross_attention_closed_form():
+    wl, W, inp = micro()
+    lw = W["layers"][1]
+    rng = np.random.default_rng(6)
+    h = rng.standard_normal((4, wl.d_model))
+    taus = [0, 3, 3, 1]
+    got = model.cross_attention(W, lw, h, inp["latents"], [[t] for t in taus], wl.n_heads)
+    for i, t in enumerate(taus):
+        ot = np.einsum("oi,i->o", W["w_lat"], inp["latents"][t])
+        want = np.einsum("oi,i->o", lw["wo_c"], np.einsum("oi,i->o", lw["wv_c"], ot))
+        np.testing.assert_allclose(got[i], want, rtol=1e-11, atol=1e-12)
+
+
+def test_multi_latent_cross_attention_matches_torch_sdpa():
+    wl, W, inp = micro()
+    lw = W["layers"][0]
+    rng = np.random.default_rng(7)
+    h = rng.standard_normal((3, wl.d_model))
+    sets = [[0, 1, 2], [2, 4, 5], [1, 2, 3]]
+    got = model.cross_attention(W, lw, h, inp["latents"], sets, wl.n_heads)
+    H, dh = wl.n_heads, wl.d_head
+    for i, s in enumerate(sets):
+        ot = inp["latents"][s] @ W["w_lat"].T
+        q = torch.tensor(h[i] @ lw["wq_c"].T).view(1, H, 1, dh)
+        k = torch.tensor(ot @ lw["wk_c"].T).view(len(s), H, dh).permute(1, 0, 2)[None]
+        v = torch.tensor(ot @ lw["wv_c"].T).view(len(s), H, dh).permute(1, 0, 2)[None]
+        a = Fnn.scaled_dot_product_attention(q, k, v).reshape(-1).numpy()
+        np.testing.assert_allclose(got[i], lw["wo_c"] @ a, rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------- full forward special cases
+def _zero(W, keys):
+    W = {k: v for k, v in W.items()}
+    W["layers"] = [{k: (np.zeros_like(v) if k in keys else v) for k, v in lw.items()}
+                   for lw in W["layers"]]
+    return W
+
+
+def _run_forward(W, wl, inp, toks, taus, allow):
+    return model.forward(W, wl, inp["latents"], toks, np.arange(len(toks)), [[t] for t in taus], allow)
+
+
+def test_forward_all_outputs_zero_is_head_of_embedding():
+    wl, W, inp = micro()
+    Wz = _zero(W, {"wo_c", "wo", "w2"})
+    toks = [3, 250, 256, 256]
+    z = _run_forward(Wz, wl, inp, toks, [0, 1, 1, 1], model.blt_d_mask(2, 2))
+    e = W["embed"][toks]
+    u = W["g_out"] * e / np.sqrt((e * e).mean(-1, keepdims=True) + wl.rms_eps)
+    np.testing.assert_allclose(z, np.einsum("vi,ri->rv", W["w_out"], u), rtol=1e-11, atol=1e-13)
+
+
+def test_forward_cross_only_closed_form():
+    wl, W, inp = micro()
+    Wz = _zero(W, {"wo", "w2"})
+    toks, taus = [7, 9, 256], [0, 2, 4]
+    z = _run_forward(Wz, wl, inp, toks, taus, model.blt_d_mask(2, 1))
+    for i, (t, tau) in enumerate(zip(toks, taus)):
+        h = W["embed"][t].copy()
+        ot = np.einsum("oi,i->o", W["w_lat"], inp["latents"][tau])
+        for lw in W["layers"]:
+            h += np.einsum("oi,i->o", lw["wo_c"], np.einsum("oi,i->o", lw["wv_c"], ot))
+        u = W["g_out"] * h / np.sqrt((h * h).mean() + wl.rms_eps)
+        np.testing.assert_allclose(z[i], np.einsum("vi,i->v", W["w_out"], u), rtol=1e-10, atol=1e-12)
+
+
+def test_forward_ffn_only_closed_form():
+    wl, W, inp = micro()
+    Wz = _zero(W, {"wo_c", "wo"})
+    toks = [1, 2, 256, 256]
+    z = _run_forward(Wz, wl, inp, toks, [0, 0, 0, 0], model.blt_d_mask(2, 2))
+    h = W["embed"][toks].copy()
+    for lw in W["layers"]:
+        u = lw["g_ffn"] * h / np.sqrt((h * h).mean(-1, keepdims=True) + wl.rms_eps)
+        a = np.einsum("fi,ri->rf", lw["w1"], u)
+        h = h + np.einsum("of,rf->ro", lw["w2"], a * torch.sigmoid(torch.tensor(a)).numpy())
+    u = W["g_out"] * h / np.sqrt((h * h).mean(-1, keepdims=True) + wl.rms_eps)
+    np.testing.assert_allclose(z, np.einsum("vi,ri->rv", W["w_out"], u), rtol=1e-10, atol=1e-12)
+
+
+def test_forward_one_self_attention_layer_matches_torch():
+    """One layer, cross-attention and FFN outputs zeroed: the layer reduces to
+    RMSNorm -> RoPE'd SDPA under the BLT-D mask -> W_o, checked against torch
+    routines and the complex form of RoPE."""
+    wl, W, inp = micro(n_layers=1)
+    Wz = _zero(W, {"wo_c", "w2"})
+    toks = [5, 6, 7, 256, 256, 256]
+    n_pre = 3
+    allow = model.blt_d_mask(n_pre, 3)
+    pos = np.array([40, 41, 42, 43, 44, 45])
+    z = model.forward(Wz, wl, inp["latents"], toks, pos, [[0]] * 6, allow)
+    lw = W["layers"][0]
+    d, H, dh = wl.d_model, wl.n_heads, wl.d_head
+    e = torch.tensor(W["embed"][toks])
+    u = Fnn.rms_norm(e, (d,), weight=torch.tensor(lw["g_attn"]), eps=wl.rms_eps)
+    qkv = Fnn.linear(u, torch.tensor(lw["wqkv"]))
+
+    def rot(x):
+        x = x.view(6, H, dh)
+        zc = torch.complex(x[..., :dh // 2], x[..., dh // 2:])
+        f = wl.rope_theta ** (-2.0 * torch.arange(dh // 2, dtype=torch.float64) / dh)
+        zc = zc * torch.polar(torch.ones(6, 1, dh // 2, dtype=torch.float64),
+                              torch.tensor(pos, dtype=torch.float64)[:, None, None] * f)
+        return torch.cat([zc.real, zc.imag], -1).transpose(0, 1)
+
+    q, k = rot(qkv[:, :d]), rot(qkv[:, d:2 * d])
+    v = qkv[:, 2 * d:].view(6, H, dh).transpose(0, 1)
+    a = Fnn.scaled_dot_product_attention(q, k, v, attn_mask=torch.tensor(allow))
+    h = e + Fnn.linear(a.transpose(0, 1).reshape(6, d), torch.tensor(lw["wo"]))
+    want = Fnn.linear(Fnn.rms_norm(h, (d,), weight=torch.tensor(W["g_out"]), eps=wl.rms_eps),
+                      torch.tensor(W["w_out"])).numpy()
+    np.testing.assert_allclose(z, want, rtol=1e-10, atol=1e-12)
+
+
+def test_mask_semantics_prefix_blind_to_block():
+    wl, W, inp = micro()
+    taus = [0, 1, 1, 2, 2, 2, 2]
+    base = [10, 20, 30, 256, 256, 256, 256]
+    alt = [10, 20, 30, 256, 77, 256, 256]
+    for causal in (False, True):
+        allow = model.blt_d_mask(3, 4, causal)
+        z0 = _run_forward(W, wl, inp, base, taus, allow)
+        z1 = _run_forward(W, wl, inp, alt, taus, allow)
+        np.testing.assert_array_equal(z0[:3], z1[:3])           # prefix never sees the block
+        if causal:
+            np.testing.assert_array_equal(z0[3], z1[3])          # earlier block row blind
+        else:
+            assert np.abs(z0[3] - z1[3]).max() > 1e-6           # bidirectional block
+
+
+def test_cached_forward_equals_no_cache():
+    wl, W, inp = micro()
+    rng = np.random.default_rng(8)
+    x = list(rng.integers(0, 256, 20))
+    taus = list(np.minimum(np.arange(20) // 3, 6))
+    for causal in (False, True):
+        c = cache.CachedDecoder(W, wl, inp["latents"], 64)
+        c.run(x[:9], 0, taus[:9], 9)
+        # pass with 3 append rows and a 4-row block (two masked)
+        blk = [256, 42, 256, 17]
+        z = c.run(x[9:12] + blk, 9, taus[9:12] + [5] * 4, 3, block_causal=causal)
+        full = _run_forward(W, wl, inp, x[:12] + blk, taus[:12] + [5] * 4, model.blt_d_mask(12, 4, causal))
+        np.testing.assert_allclose(z, full[9:], rtol=1e-10, atol=1e-12)
+        # block-only pass after the append
+        z = c.run(blk, 12, [5] * 4, 0, block_causal=causal)
+        np.testing.assert_allclose(z, full[12:], rtol=1e-10, atol=1e-12)
+        # rollback: recompute row 11 with another target, then append
+        t2 = taus[:11] + [6, 6, 6]
+        z = c.run(x[11:14], 11, t2[11:14], 3)
+        full2 = _run_forward(W, wl, inp, x[:14], t2, model.blt_d_mask(14, 0))
+        np.testing.assert_allclose(z, full2[11:], rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- decisions
+def test_byte_choice_ties_mask_and_confidence():
+    z = np.zeros(257)
+    z[[5, 9]] = 2.0
+    z[256] = 50.0                      # [MASK] logit never chosen
+    b, conf, gap = decide.byte_choice(z)
+    assert b == 5 and gap == 0.0
+    p = torch.softmax(torch.tensor(z[:256]), 0).numpy()
+    assert abs(conf - p.max()) < 1e-15
+    b, conf, _ = decide.byte_choice(np.zeros(257))
+    assert b == 0 and abs(conf - 1 / 256) < 1e-15
+
+
+def test_unmask_rules():
+    M = decide.MASK
+    blk, ch = decide.unmask_commit([M, 3, M, M], [9, 9, 8, 7], [0.7, 0.99, 0.71, 0.9], 0.7)
+    assert blk == [M, 3, 8, 7] and ch == [2, 3]          # strict '>' alpha, committed untouched
+    blk, ch = decide.unmask_commit([M, M, M], [1, 2, 3], [0.2, 0.5, 0.5], 0.7)
+    assert blk == [M, 2, M] and ch == [1]                 # fallback: most confident, lowest pos
+    blk, ch = decide.unmask_commit([M, 4, M], [1, 2, 3], [0.0, 0.0, 0.0], 0.7, one_step=True)
+    assert blk == [1, 4, 3]
+
+
+def test_verify_exhaustive_against_greedy_continuation():
+    """r <= 3, 2-symbol alphabet: the committed bytes are exactly the first
+    a + 1 bytes of the greedy continuation, and a is the longest draft prefix
+    equal to it (the exactness guarantee of greedy verification)."""
+    for r in range(1, 4):
+        for table in itertools.product([0, 1], repeat=2 ** (r + 1)):
+            f = lambda prefix: table[int("1" + "".join(map(str, prefix)), 2) % len(table)]
+            for draft in itertools.product([0, 1], repeat=r):
+                pred = [f(list(draft[:j])) for j in range(r + 1)]
+                a, nxt = decide.verify_accept(list(draft), pred)
+                greedy = []
+                for _ in range(r + 1):
+                    greedy.append(f(greedy))
+                assert list(draft[:a]) + [nxt] == greedy[:a + 1]
+                assert a == r or draft[a] != greedy[a]
+
+
+def test_verify_special_cases():
+    assert decide.verify_accept([4, 5, 6], [4, 5, 6, 7]) == (3, 7)   # all match + free byte
+    assert decide.verify_accept([9, 5, 6], [4, 5, 6, 7]) == (0, 4)   # first wrong -> correction
+
+
+# ---------------------------------------------------------------- patcher
+def test_splitmix64_reference_vector():
+    with open(os.path.join(GOLDEN, "splitmix64.json")) as f:
+        g = json.load(f)
+    assert [patcher.splitmix64_nth(g["seed"], i + 1) for i in range(3)] == [int(v, 16) for v in g["outputs"]]
+
+
+def test_targets_worked_example():
+    with open(os.path.join(GOLDEN, "targets_example.json")) as f:
+        g = json.load(f)
+    patch, ends = patcher.segment([0] * sum(g["patch_lengths"]), g["patch_lengths"], 0)
+    assert [patcher.causal_target(patch, ends, i) for i in range(len(patch))] == g["targets"]
+    assert patcher.last_target(patch) == g["last_target"]
+
+
+def test_patcher_rule_statistics_and_causality():
+    rng = np.random.default_rng(9)
+    x = list(rng.integers(0, 256, 4000))
+    patch, ends = patcher.segment(x, [1, 3], 12345)
+    lens = np.bincount(patch)
+    assert lens.max() <= 8 and 3.0 < lens[2:-1].mean() < 4.5
+    y = list(x)
+    y[3000] = (y[3000] + 1) % 256
+    p2, e2 = patcher.segment(y, [1, 3], 12345)
+    assert (e2[:3000] == ends[:3000]).all() and (p2[:3001] == patch[:3001]).all()
+
+
+# ---------------------------------------------------------------- loops
+@pytest.fixture(scope="module")
+def tiny():
+    wl = bltgen.WORKLOADS[0]
+    W = model.as64(bltgen.make_weights(wl, gains="random"))
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    inp["latents"] = inp["latents"].astype(np.float64)
+    return wl, W, inp
+
+
+def test_blt_s_equals_greedy_for_every_k(tiny):
+    wl, W, inp = tiny
+    g = loops.greedy(W, wl, inp, 48)
+    assert g.n_dec == 48
+    for k in (1, 2, 3, 5, 8):
+        s = loops.blt_s(W, wl, inp, 48, k)
+        assert s.out == g.out
+        assert s.n_dec == len(s.accept) * (k + 1) and s.n_eg == len(s.accept)
+
+
+def test_blt_d_block1_is_masked_row_greedy_for_any_alpha(tiny):
+    wl, W, inp = tiny
+    ref = loops.masked_row_greedy(W, wl, inp, 12)
+    for alpha in (0.0, 0.7, 1.0):
+        for causal in (False, True):
+            r = loops.blt_d(W, wl, inp, 12, 1, alpha, block_causal=causal)
+            assert r.out == ref and r.n_dec == 12 and r.n_eg == 12
+
+
+def test_blt_d_alpha_extremes(tiny):
+    wl, W, inp = tiny
+    r = loops.blt_d(W, wl, inp, 32, 4, 1.0)
+    assert r.n_dec == 32 and r.n_eg == 8                 # one commit per pass
+    lo = loops.blt_d(W, wl, inp, 32, 4, 1.0 / 512)
+    one = loops.blt_d(W, wl, inp, 32, 4, 0.7, one_step=True)
+    assert lo.out == one.out and lo.n_dec == 8 == one.n_dec
+
+
+def test_blt_d_peaked_head_commits_several_per_pass():
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    W = model.as64(bltgen.make_weights(wl))
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    r = loops.blt_d(W, wl, inp, 32, 4, 0.7, trace=True)
+    assert r.n_dec < 32 and max(len(p["chosen"]) for p in r.passes) > 1
+
+
+def test_blt_dv_counts(tiny):
+    wl, W, inp = tiny
+    r = loops.blt_dv(W, wl, inp, 24, 8, 0.7, one_step=True)
+    rounds = len(r.accept)
+    assert r.n_eg == 2 * rounds and r.n_dec == 2 * rounds
+    assert len(r.out) == 24
+
+
+# ---------------------------------------------------------------- proxy
+def test_proxy_worked_example():
+    with open(os.path.join(GOLDEN, "proxy_example.json")) as f:
+        g = json.load(f)
+    gb = proxy.proxy_gb_per_seq(g["n_dec"], g["n_eg"], 1, g["p_dec"], g["p_enc"], g["p_glob"])
+    assert float(gb) == g["gb"]
+
+
+def test_decoder_param_count():
+    assert proxy.decoder_params(bltgen.WORKLOADS[1]) == 153_637_888
