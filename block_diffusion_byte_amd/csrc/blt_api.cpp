@@ -1,0 +1,449 @@
+// C-ABI entry points: argument validation on the host, the library-owned
+// workspace, and the kernel sequence of one decoder pass.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "blt_ctx.h"
+
+using namespace blt;
+
+namespace {
+
+bool valid_cfg(const blt_config *c, std::string *why) {
+  auto bad = [&](const char *m) { *why = m; return false; };
+  if (!c) return bad("config is NULL");
+  if (c->dtype != BLT_F32 && c->dtype != BLT_BF16) return bad("dtype must be BLT_F32 or BLT_BF16");
+  if (c->vocab != kVocab) return bad("vocab must be 257 (256 bytes + [MASK])");
+  if (c->n_layers < 1 || c->d_model < 1 || c->n_heads < 1 || c->d_ffn < 1 || c->d_global < 1)
+    return bad("layer/width sizes must be positive");
+  if (c->d_model % c->n_heads) return bad("d_model must be a multiple of n_heads");
+  const int dh = c->d_model / c->n_heads;
+  if (dh != 32 && dh != 64 && dh != 128) return bad("head width must be 32, 64 or 128");
+  const int epc = c->dtype == BLT_BF16 ? 8 : 4;
+  const int q = 32 * epc;  // 4 waves x 8 lanes x one 16-byte chunk
+  if (c->d_model % q || c->d_ffn % q || c->d_global % q)
+    return bad("d_model, d_ffn and d_global must be multiples of 256 (bf16) or 128 (f32)");
+  if (c->dtype == BLT_BF16 && (c->d_model % 64 || c->d_ffn % 64 || c->d_global % 64))
+    return bad("bf16 widths must be multiples of 64");
+  if (c->max_batch < 1 || c->max_ctx < 1 || c->max_latents < 1 || c->max_rows < 1)
+    return bad("capacities must be positive");
+  if (c->max_block < 1 || c->max_block > kMaxBlock) return bad("max_block must be in 1..64");
+  if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta must be > 0");
+  if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return bad("rms_eps must be >= 0");
+  return true;
+}
+
+size_t esize(const blt_config &c) { return c.dtype == BLT_BF16 ? 2 : 4; }
+
+blt_status fail(blt_ctx *c, blt_status st, const std::string &m) {
+  if (c) c->err = m;
+  return st;
+}
+
+blt_status hip_fail(blt_ctx *c, hipError_t e, const char *where) {
+  if (c) c->err = std::string(where) + ": " + hipGetErrorString(e);
+  return BLT_EHIP;
+}
+
+#define HIP_TRY(ctx, expr)                                         \
+  do {                                                             \
+    hipError_t _e = (expr);                                        \
+    if (_e != hipSuccess) return hip_fail((ctx), _e, #expr);       \
+  } while (0)
+
+template <typename T>
+hipError_t dalloc(T **p, size_t n) {
+  return hipMalloc((void **)p, std::max<size_t>(n, 1) * sizeof(T));
+}
+
+}  // namespace
+
+namespace blt {
+
+// Copy this pass's descriptors into a pinned staging slot and then to the
+// device.  Slots rotate; a slot is reused only after its previous copy ended.
+blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
+                      const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs) {
+  StageSlot &sl = c->ring[c->ring_next];
+  c->ring_next = (c->ring_next + 1) % kRing;
+  if (sl.pending) {
+    HIP_TRY(c, hipEventSynchronize(sl.ev));
+    sl.pending = false;
+  }
+  char *p = (char *)sl.host;
+  const size_t rb = rows.size() * sizeof(RowDesc), sb = seqs.size() * sizeof(SeqDesc);
+  const size_t ob = offs ? offs->size() * sizeof(int64_t) : 0;
+  if (rb) memcpy(p, rows.data(), rb);
+  if (sb) memcpy(p + c->seq_off, seqs.data(), sb);
+  if (ob) memcpy(p + c->off_off, offs->data(), ob);
+  if (rb) HIP_TRY(c, hipMemcpyAsync(c->rows_d, p, rb, hipMemcpyHostToDevice, c->stream));
+  if (sb) HIP_TRY(c, hipMemcpyAsync(c->seqs_d, p + c->seq_off, sb, hipMemcpyHostToDevice, c->stream));
+  if (ob) HIP_TRY(c, hipMemcpyAsync(c->offs_d, p + c->off_off, ob, hipMemcpyHostToDevice, c->stream));
+  HIP_TRY(c, hipEventRecord(sl.ev, c->stream));
+  sl.pending = true;
+  return BLT_OK;
+}
+
+GemmArgs base_args(const blt_ctx *c) {
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.eps = c->cfg.rms_eps;
+  a.n_layers = c->cfg.n_layers;
+  a.max_lat = c->cfg.max_latents;
+  a.d = c->cfg.d_model;
+  return a;
+}
+
+// The kernel sequence of one decoder pass over `rows` (grouped by `seqs`).
+blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
+                    const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
+                    const int32_t *tokens_dev, bool unmask, float alpha, int one_step,
+                    int32_t *masked_left, int32_t *argmax_out, float *conf_out,
+                    float *logits_out) {
+  const blt_config &g = c->cfg;
+  const int R = (int)rows.size(), S = (int)seqs.size();
+  const int d = g.d_model, F = g.d_ffn, L = g.n_layers;
+  const bool bf = c->bf16;
+  blt_status bs = stage_pass(c, rows, seqs, nullptr);
+  if (bs != BLT_OK) return bs;
+  hipStream_t s = c->stream;
+  const float *cross = (const float *)st->cross;
+  HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, block_tok,
+                          tokens_dev, c->h, s));
+  KVGeom geo{L, g.n_heads, d / g.n_heads, g.max_ctx};
+  for (int l = 0; l < L; ++l) {
+    const blt_layer_weights &lw = c->layers[l];
+    GemmArgs a = base_args(c);
+    a.R = R;
+    a.rows = c->rows_d;
+    // q, k, v = W_qkv RMSNorm(h)
+    a.W = lw.wqkv; a.N = 3 * d; a.K = d;
+    a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_attn;
+    a.ep = EP_STORE_F32; a.out_f32 = c->qkv; a.ldo = 3 * d;
+    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
+    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, c->max_chunks, c->rows_d,
+                                R, c->part, c->xa, s));
+    // h += W_o a
+    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a.W = lw.wo; a.N = d; a.K = d;
+    a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
+    a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
+    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    // f = SiLU(W1 RMSNorm(h))
+    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a.W = lw.w1; a.N = F; a.K = d;
+    a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_ffn;
+    a.ep = EP_SILU_ACT; a.out_act = c->xa; a.ldo = F;
+    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    // h += W2 f (+ the next layer's cross-attention contribution)
+    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a.W = lw.w2; a.N = d; a.K = F;
+    a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = F;
+    a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
+    if (l + 1 < L) { a.cross = cross; a.cross_layer = l + 1; }
+    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+  }
+  GemmArgs a = base_args(c);
+  a.R = R; a.rows = c->rows_d;
+  a.W = c->w.w_out; a.N = kVocab; a.K = d;
+  a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
+  a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
+  HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, argmax_out, conf_out,
+                           logits_out, s));
+  if (unmask)
+    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, (int32_t *)block_tok, alpha,
+                             one_step, masked_left, s));
+  return BLT_OK;
+}
+
+}  // namespace blt
+
+extern "C" {
+
+blt_status blt_state_size(const blt_config *cfg, size_t *kv_bytes, size_t *cross_bytes) {
+  std::string why;
+  if (!valid_cfg(cfg, &why) || !kv_bytes || !cross_bytes) return BLT_EINVAL;
+  const size_t e = esize(*cfg);
+  *kv_bytes = (size_t)cfg->max_batch * cfg->n_layers * 2 * cfg->max_ctx * cfg->d_model * e;
+  *cross_bytes = (size_t)cfg->max_batch * cfg->max_latents * cfg->n_layers * cfg->d_model * sizeof(float);
+  return BLT_OK;
+}
+
+const char *blt_last_error(const blt_ctx *ctx) { return ctx ? ctx->err.c_str() : "NULL context"; }
+
+blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_stream, blt_ctx **out) {
+  std::string why;
+  if (!out) return BLT_EINVAL;
+  *out = nullptr;
+  if (!valid_cfg(cfg, &why)) {
+    if (cfg && (cfg->dtype != BLT_F32 && cfg->dtype != BLT_BF16)) return BLT_EDTYPE;
+    return BLT_EINVAL;
+  }
+  if (!w || !w->embed || !w->w_lat || !w->w_out || !w->g_out || !w->layers) return BLT_EINVAL;
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    const blt_layer_weights &lw = w->layers[l];
+    if (!lw.wv_c || !lw.wo_c || !lw.wqkv || !lw.wo || !lw.g_attn || !lw.g_ffn || !lw.w1 || !lw.w2)
+      return BLT_EINVAL;
+  }
+  blt_ctx *c = new (std::nothrow) blt_ctx();
+  if (!c) return BLT_EINVAL;
+  c->cfg = *cfg;
+  c->bf16 = cfg->dtype == BLT_BF16;
+  c->stream = (hipStream_t)hip_stream;
+  c->w = *w;
+  c->layers.assign(w->layers, w->layers + cfg->n_layers);
+  const int R = cfg->max_rows, d = cfg->d_model, F = cfg->d_ffn, H = cfg->n_heads;
+  const int dh = d / H;
+  c->max_chunks = (cfg->max_ctx + kAttnChunk - 1) / kAttnChunk;
+  const size_t e = esize(*cfg);
+  const size_t wide = (size_t)std::max(d, F);
+  hipError_t he = hipSuccess;
+  auto chk = [&](hipError_t x) { if (he == hipSuccess) he = x; };
+  chk(dalloc(&c->h, (size_t)R * d));
+  chk(dalloc(&c->qkv, (size_t)R * 3 * d));
+  chk(dalloc(&c->q, (size_t)R * d));
+  chk(dalloc(&c->part, (size_t)R * H * c->max_chunks * (dh + 2)));
+  chk(dalloc(&c->logits, (size_t)R * kVocab));
+  chk(dalloc(&c->rinv, (size_t)R));
+  chk(dalloc(&c->conf_ws, (size_t)R));
+  chk(dalloc(&c->argmax_ws, (size_t)R));
+  chk(hipMalloc(&c->xa, std::max<size_t>(1, (size_t)R * wide * e)));
+  chk(hipMalloc(&c->xb, std::max<size_t>(1, (size_t)R * std::max(d, cfg->d_global) * e)));
+  chk(dalloc(&c->rows_d, (size_t)R));
+  chk(dalloc(&c->seqs_d, (size_t)cfg->max_batch));
+  chk(dalloc(&c->offs_d, (size_t)R));
+  chk(dalloc(&c->rope_tab, (size_t)cfg->max_ctx * (dh / 2)));
+  c->seq_off = ((size_t)R * sizeof(RowDesc) + 255) & ~(size_t)255;
+  c->off_off = (c->seq_off + (size_t)cfg->max_batch * sizeof(SeqDesc) + 255) & ~(size_t)255;
+  const size_t stage = c->off_off + (size_t)R * sizeof(int64_t);
+  for (int i = 0; i < kRing && he == hipSuccess; ++i) {
+    chk(hipHostMalloc(&c->ring[i].host, stage, hipHostMallocDefault));
+    chk(hipEventCreateWithFlags(&c->ring[i].ev, hipEventDisableTiming));
+  }
+  if (he == hipSuccess) {
+    // RoPE angles pos * theta^(-2j/dh), evaluated in double precision.
+    std::vector<float2> tab((size_t)cfg->max_ctx * (dh / 2));
+    for (int p = 0; p < cfg->max_ctx; ++p)
+      for (int j = 0; j < dh / 2; ++j) {
+        const double ang = (double)p * pow((double)cfg->rope_theta, -2.0 * j / dh);
+        tab[(size_t)p * (dh / 2) + j] = make_float2((float)cos(ang), (float)sin(ang));
+      }
+    chk(hipMemcpy(c->rope_tab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice));
+  }
+  if (he != hipSuccess) {
+    blt_destroy(c);
+    return BLT_EHIP;
+  }
+  *out = c;
+  return BLT_OK;
+}
+
+blt_status blt_destroy(blt_ctx *c) {
+  if (!c) return BLT_EINVAL;
+  (void)hipStreamSynchronize(c->stream);
+  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws,
+                  c->xa, c->xb, c->rows_d, c->seqs_d, c->offs_d, c->rope_tab};
+  for (void *p : bufs)
+    if (p) (void)hipFree(p);
+  for (int i = 0; i < kRing; ++i) {
+    if (c->ring[i].host) (void)hipHostFree(c->ring[i].host);
+    if (c->ring[i].ev) (void)hipEventDestroy(c->ring[i].ev);
+  }
+  delete c;
+  return BLT_OK;
+}
+
+blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int32_t *slot,
+                           const int32_t *idx, const void *table, int64_t seq_stride) {
+  if (!c) return BLT_EINVAL;
+  const blt_config &g = c->cfg;
+  if (!st || !st->cross || n < 0 || (n > 0 && (!slot || !idx || !table)) || seq_stride < 0)
+    return fail(c, BLT_EINVAL, "blt_latents_put: bad argument");
+  for (int i = 0; i < n; ++i) {
+    if (slot[i] < 0 || slot[i] >= g.max_batch) return fail(c, BLT_EINVAL, "blt_latents_put: slot out of range");
+    if (idx[i] < 0 || idx[i] >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_latents_put: latent index beyond max_latents");
+  }
+  const int d = g.d_model, L = g.n_layers;
+  for (int i0 = 0; i0 < n; i0 += g.max_rows) {
+    const int m = std::min(g.max_rows, n - i0);
+    std::vector<int64_t> offs(2 * (size_t)m);
+    for (int i = 0; i < m; ++i) {
+      offs[i] = ((int64_t)slot[i0 + i] * seq_stride + idx[i0 + i]) * g.d_global;        // source row
+      offs[m + i] = (((int64_t)slot[i0 + i] * g.max_latents + idx[i0 + i]) * L) * d;     // cross row
+    }
+    // Both offset lists ride in the offsets buffer (2*m <= 2*max_rows entries).
+    std::vector<int64_t> src(offs.begin(), offs.begin() + m), dst(offs.begin() + m, offs.end());
+    std::vector<RowDesc> no_rows;
+    std::vector<SeqDesc> no_seqs;
+    blt_status bs = stage_pass(c, no_rows, no_seqs, &src);
+    if (bs != BLT_OK) return bs;
+    // o~ = W_lat o  -> xb
+    GemmArgs a = base_args(c);
+    a.R = m; a.W = c->w.w_lat; a.N = d; a.K = g.d_global;
+    a.pro = PRO_PLAIN; a.X = table; a.x_row_off = c->offs_d;
+    a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+    // The destination offsets replace the source offsets once W_lat has read them.
+    bs = stage_pass(c, no_rows, no_seqs, &dst);
+    if (bs != BLT_OK) return bs;
+    for (int l = 0; l < L; ++l) {
+      const blt_layer_weights &lw = c->layers[l];
+      a = base_args(c);
+      a.R = m; a.W = lw.wv_c; a.N = d; a.K = d;
+      a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
+      a.ep = EP_STORE_ACT; a.out_act = c->xa; a.ldo = d;
+      HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+      a = base_args(c);
+      a.R = m; a.W = lw.wo_c; a.N = d; a.K = d;
+      a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
+      a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = c->offs_d;
+      a.off_add = (int64_t)l * d;
+      HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+    }
+  }
+  return BLT_OK;
+}
+
+static blt_status check_slots(blt_ctx *c, int32_t batch, const int32_t *slot, const char *fn) {
+  const blt_config &g = c->cfg;
+  if (batch < 1 || batch > g.max_batch || !slot) return fail(c, BLT_EINVAL, std::string(fn) + ": bad batch or slot array");
+  std::vector<char> seen(g.max_batch, 0);
+  for (int b = 0; b < batch; ++b) {
+    if (slot[b] < 0 || slot[b] >= g.max_batch) return fail(c, BLT_EINVAL, std::string(fn) + ": slot out of range");
+    if (seen[slot[b]]) return fail(c, BLT_EINVAL, std::string(fn) + ": a slot appears twice in one pass");
+    seen[slot[b]] = 1;
+  }
+  return BLT_OK;
+}
+
+blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
+                         const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
+                         const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
+                         int32_t *argmax_out, float *conf_out, float *logits_out) {
+  if (!c) return BLT_EINVAL;
+  const blt_config &g = c->cfg;
+  static const char *fn = "blt_kv_append";
+  if (!st || !st->kv || !st->cross) return fail(c, BLT_EINVAL, "blt_kv_append: state is NULL");
+  blt_status bs = check_slots(c, batch, slot, fn);
+  if (bs != BLT_OK) return bs;
+  if (!start_pos || !n_rows || !lat_idx || n_max < 1 || (!bytes && !tokens_dev))
+    return fail(c, BLT_EINVAL, "blt_kv_append: NULL argument or n_max < 1");
+  std::vector<RowDesc> rows;
+  std::vector<SeqDesc> seqs;
+  for (int b = 0; b < batch; ++b) {
+    const int n = n_rows[b], s0 = start_pos[b];
+    if (n < 0 || n > n_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_kv_append: bad n_rows or start_pos");
+    if ((int64_t)s0 + n > g.max_ctx) return fail(c, BLT_ECAPACITY, "blt_kv_append: rows beyond max_ctx");
+    if (n == 0) continue;
+    if ((int64_t)rows.size() + n > g.max_rows) return fail(c, BLT_ECAPACITY, "blt_kv_append: more rows than max_rows");
+    SeqDesc sd{slot[b], (int)rows.size(), n, s0 + n, -1, -1, 0, slot[b]};
+    for (int j = 0; j < n; ++j) {
+      const int li = lat_idx[(size_t)b * n_max + j];
+      if (li < 0 || li >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_kv_append: latent index beyond max_latents");
+      const int dj = slot[b] * n_max + j;  // device arrays are indexed by slot
+      RowDesc rd{slot[b], s0 + j, bytes ? (int)bytes[(size_t)b * n_max + j] : kTokFromDev, dj, li,
+                 s0 + j + 1, dj, 0};
+      rows.push_back(rd);
+    }
+    seqs.push_back(sd);
+  }
+  if (rows.empty()) return BLT_OK;
+  return run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
+                  conf_out, logits_out);
+}
+
+blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
+                                 const int32_t *slot, const int32_t *start_pos,
+                                 const int32_t *n_append, int32_t n_append_max,
+                                 const uint8_t *append_bytes, const int32_t *append_lat,
+                                 int32_t *block_tok, int32_t B, const int32_t *block_lat,
+                                 float alpha, blt_unmask mode, blt_block_mask mask,
+                                 int32_t *argmax_out, float *conf_out, float *logits_out,
+                                 int32_t *masked_left) {
+  if (!c) return BLT_EINVAL;
+  const blt_config &g = c->cfg;
+  static const char *fn = "blt_decode_block_step";
+  if (!st || !st->kv || !st->cross) return fail(c, BLT_EINVAL, "blt_decode_block_step: state is NULL");
+  blt_status bs = check_slots(c, batch, slot, fn);
+  if (bs != BLT_OK) return bs;
+  if (!start_pos || !block_tok || !block_lat || !masked_left)
+    return fail(c, BLT_EINVAL, "blt_decode_block_step: NULL argument");
+  if (B < 1 || B > g.max_block) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: B outside 1..max_block");
+  if (mode != BLT_UNMASK_THRESHOLD && mode != BLT_UNMASK_ONE_STEP) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad unmask mode");
+  if (mask != BLT_BLOCK_BIDIR && mask != BLT_BLOCK_CAUSAL) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad block mask");
+  if (!isfinite(alpha)) return fail(c, BLT_EINVAL, "blt_decode_block_step: alpha must be finite");
+  if (n_append_max < 0 || (n_append_max > 0 && (!n_append || !append_bytes || !append_lat)))
+    return fail(c, BLT_EINVAL, "blt_decode_block_step: bad append arguments");
+  std::vector<RowDesc> rows;
+  std::vector<SeqDesc> seqs;
+  for (int b = 0; b < batch; ++b) {
+    const int na = n_append_max > 0 ? n_append[b] : 0, s0 = start_pos[b];
+    if (na < 0 || na > n_append_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad n_append or start_pos");
+    const int64_t end = (int64_t)s0 + na + B;
+    if (end > g.max_ctx) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: block beyond max_ctx");
+    if ((int64_t)rows.size() + na + B > g.max_rows) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: more rows than max_rows");
+    const int bl = block_lat[b];
+    if (bl < 0 || bl >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: latent index beyond max_latents");
+    SeqDesc sd{slot[b], (int)rows.size(), na + B, (int)end, slot[b] * B, (int)rows.size() + na, B,
+               slot[b]};
+    for (int j = 0; j < na; ++j) {
+      const int li = append_lat[(size_t)b * n_append_max + j];
+      if (li < 0 || li >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: latent index beyond max_latents");
+      rows.push_back(RowDesc{slot[b], s0 + j, (int)append_bytes[(size_t)b * n_append_max + j], 0, li,
+                             s0 + j + 1, -1, 0});
+    }
+    for (int j = 0; j < B; ++j) {
+      const int pos = s0 + na + j;
+      rows.push_back(RowDesc{slot[b], pos, kTokFromBlock, slot[b] * B + j, bl,
+                             mask == BLT_BLOCK_CAUSAL ? pos + 1 : (int)end, slot[b] * B + j, 0});
+    }
+    seqs.push_back(sd);
+  }
+  return run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, mode == BLT_UNMASK_ONE_STEP,
+                  masked_left, argmax_out, conf_out, logits_out);
+}
+
+blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int32_t r,
+                             const int32_t *draft, int32_t ld_draft, const int32_t *pred,
+                             int32_t ld_pred, int32_t *accept_len, int32_t *next_byte) {
+  if (!c) return BLT_EINVAL;
+  if (batch < 1 || batch > c->cfg.max_batch || r < 0 || !draft || !pred || !accept_len ||
+      !next_byte || ld_draft < r || ld_pred < r + 1)
+    return fail(c, BLT_EINVAL, "blt_verify_accept: bad argument");
+  std::vector<SeqDesc> seqs(batch);
+  for (int b = 0; b < batch; ++b) {
+    const int s = slot ? slot[b] : b;
+    if (s < 0 || s >= c->cfg.max_batch) return fail(c, BLT_EINVAL, "blt_verify_accept: slot out of range");
+    seqs[b] = SeqDesc{s, 0, 0, 0, 0, 0, 0, s};
+  }
+  std::vector<RowDesc> no_rows;
+  blt_status bs = stage_pass(c, no_rows, seqs, nullptr);
+  if (bs != BLT_OK) return bs;
+  HIP_TRY(c, launch_verify(batch, c->seqs_d, r, draft, ld_draft, pred, ld_pred, accept_len,
+                           next_byte, c->stream));
+  return BLT_OK;
+}
+
+blt_status blt_bw_model(const blt_counts *cn, const blt_params *p, uint64_t *bytes_total,
+                        double *gb_per_seq) {
+  if (!cn || !p || !bytes_total || cn->n_seq == 0) return BLT_EINVAL;
+  uint64_t a, b, eg, sum, tot;
+  if (__builtin_mul_overflow(cn->n_dec, p->p_dec, &a)) return BLT_EINVAL;
+  if (__builtin_add_overflow(p->p_enc, p->p_glob, &eg)) return BLT_EINVAL;
+  if (__builtin_mul_overflow(cn->n_encglob, eg, &b)) return BLT_EINVAL;
+  if (__builtin_add_overflow(a, b, &sum)) return BLT_EINVAL;
+  if (__builtin_mul_overflow(sum, (uint64_t)p->bytes_per_param, &tot)) return BLT_EINVAL;
+  *bytes_total = tot;
+  if (gb_per_seq) *gb_per_seq = (double)tot / 1e9 / (double)cn->n_seq;
+  return BLT_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,103 @@
+// Internal declarations shared by the HIP kernels (kernels.hip) and the
+// C-ABI host code (blt_api.cpp, session.cpp).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/blt.h"
+
+namespace blt {
+
+constexpr int kVocab = 257;
+constexpr int kMask = 256;
+constexpr int kAttnChunk = 256;     // keys per split-K attention chunk (aligned to absolute positions)
+constexpr int kMaxBlock = 64;       // block rows per sequence handled by one wave in unmask
+constexpr int kGemvRows = 16;       // rows per GEMV row block; passes with R >= 16 use MFMA (bf16)
+
+// Token source codes in RowDesc::tok (values >= 0 are literal token ids).
+constexpr int kTokFromBlock = -1;   // block_tok[blk]
+constexpr int kTokFromDev = -2;     // tokens_dev[blk]
+
+// One row of a decoder pass.
+struct RowDesc {
+  int32_t slot;   // state slot (sequence)
+  int32_t pos;    // absolute byte position (RoPE and KV row)
+  int32_t tok;    // token id or a kTokFrom* code
+  int32_t blk;    // index into block_tok / tokens_dev for the kTokFrom* codes
+  int32_t lat;    // latent index read by the cross-attention
+  int32_t kend;   // the row attends cache rows [0, kend)
+  int32_t oidx;   // index into the caller's per-row outputs, -1 for none
+  int32_t pad;
+};
+
+// One sequence of a decoder pass.
+struct SeqDesc {
+  int32_t slot;
+  int32_t row0, nrows;   // its rows in the pass
+  int32_t kmax;          // max kend over its rows
+  int32_t blk0;          // first block_tok entry of its block (-1: no block)
+  int32_t blk_row0;      // pass row of its first block row
+  int32_t nblk;          // block rows
+  int32_t out_b;         // index of the sequence in the caller's batch
+};
+
+enum Epilogue { EP_STORE_F32 = 0, EP_RESID = 1, EP_SILU_ACT = 2, EP_STORE_ACT = 3, EP_ROWOFF_F32 = 4 };
+enum Prologue { PRO_PLAIN = 0, PRO_NORM = 1 };
+
+// y[r][o] = sum_i W[o][i] * x[r][i] for r < R, o < N.
+struct GemmArgs {
+  const void *W;
+  int N, K;
+  int R;
+  int pro;
+  const void *X;           // PRO_PLAIN: activations, row r at X + (x_row_off ? x_row_off[r] : r * ldx)
+  int64_t ldx;
+  const int64_t *x_row_off;
+  const float *H;          // PRO_NORM: x = act(gain * H[r] / rms(H[r]))
+  int64_t ldh;
+  const void *gain;
+  float eps;
+  int ep;
+  float *out_f32;
+  void *out_act;
+  int64_t ldo;
+  const int64_t *row_off;  // EP_ROWOFF_F32: out_f32[row_off[r] + off_add + o]
+  int64_t off_add;
+  // EP_RESID: resid[r * ldo + o] += y (+ cross[slot][lat][cross_layer][o] when cross != null)
+  float *resid;
+  const float *cross;
+  const RowDesc *rows;
+  int cross_layer, n_layers, max_lat, d;
+};
+
+struct KVGeom {
+  int n_layers, n_heads, d_head, max_ctx;
+};
+
+// Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.
+hipError_t launch_gemm(bool bf16, const GemmArgs &a, float *rinv_ws, void *xnorm_ws,
+                       hipStream_t s);
+hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
+                        int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
+                        const int32_t *tokens_dev, float *h, hipStream_t s);
+hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
+                          const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
+                          hipStream_t s);
+hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
+                            const SeqDesc *seqs, int n_seq, int max_chunks, const RowDesc *rows,
+                            int R, float *part, void *a_out, hipStream_t s);
+hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
+                         float *conf_ws, int32_t *argmax_out, float *conf_out,
+                         float *logits_out, hipStream_t s);
+hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
+                         const float *conf_ws, int32_t *block_tok, float alpha, int one_step,
+                         int32_t *masked_left, hipStream_t s);
+hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,
+                         int ld_draft, const int32_t *pred, int ld_pred, int32_t *accept_len,
+                         int32_t *next_byte, hipStream_t s);
+
+}  // namespace blt

@@ -1,0 +1,254 @@
+/*
+ * blt.h -- C ABI of the MI355X (gfx950) Fast-BLT local byte decoder step.
+ *
+ * The library runs the local byte decoder of a Byte Latent Transformer as
+ * described in the pytorch.kr Fast-BLT summary ("Fast Byte Latent
+ * Transformer (Fast-BLT) 연구 소개"): per layer a cross-attention read of the
+ * global model's patch latents added to the residual stream, then a decoder
+ * transformer layer (section on the BLT architecture, the layer equation);
+ * the BLT-D block of [MASK] positions attended bidirectionally over a causal
+ * clean prefix (section "BLT-D attention mask"); confidence-threshold
+ * unmasking (section "block unmasking strategies"); and the greedy
+ * exact-match verification shared by BLT-S and BLT-DV (section "BLT-S and
+ * BLT-DV").  The parameter-load bandwidth proxy follows the wangzhan123.com
+ * Fast-BLT article, section six.
+ *
+ * Conventions for every entry point:
+ *  - "device" pointers are HIP device memory owned by the caller (e.g.
+ *    PyTorch tensors); "host" pointers are ordinary host memory, read before
+ *    the call returns.  The library never frees caller memory.
+ *  - Calls that launch GPU work are asynchronous on the stream given to
+ *    blt_create; their device outputs are valid once that stream has
+ *    synchronised.  A context is not thread-safe: one context per stream.
+ *  - Arguments are validated on the host before anything is enqueued; a
+ *    rejected call enqueues nothing.  Errors never abort or throw across the
+ *    ABI: the return code says what failed and blt_last_error() gives text.
+ *  - Matrices are row-major [out][in] (the weight of y = W x has W[o][i] at
+ *    o * in + i), in the context's dtype: float32 (BLT_F32) or bfloat16
+ *    (BLT_BF16).  Norm gains are in the same dtype.
+ *  - Token ids are 0..255 for bytes and 256 for [MASK].
+ *  - Per-sequence host arrays are indexed by the position b of the sequence
+ *    in the call (0..batch-1).  Per-sequence DEVICE arrays are indexed by the
+ *    sequence's state slot, so a caller can keep one buffer per slot while
+ *    sequences join or leave passes: e.g. block_tok[slot*B + j].  They must
+ *    hold max_batch sequences.
+ */
+#ifndef BLT_H
+#define BLT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BLT_OK = 0,
+  BLT_EINVAL = -1,     /* bad argument: NULL, out of range, inconsistent sizes */
+  BLT_ECAPACITY = -2,  /* a size exceeds a capacity fixed in blt_config */
+  BLT_EDTYPE = -3,     /* unsupported dtype */
+  BLT_EHIP = -4        /* a HIP runtime call failed (message in blt_last_error) */
+} blt_status;
+
+typedef enum { BLT_F32 = 0, BLT_BF16 = 1 } blt_dtype;
+
+/* How a decode step commits masked block positions (block unmasking
+ * strategies): THRESHOLD commits every masked position whose confidence
+ * (largest byte probability) is > alpha, and the single most confident one
+ * (lowest position on ties) when none is; ONE_STEP commits every masked
+ * position in one pass (the one-step diffusion draft of BLT-DV). */
+typedef enum { BLT_UNMASK_THRESHOLD = 0, BLT_UNMASK_ONE_STEP = 1 } blt_unmask;
+
+/* Self-attention inside the block: bidirectional (diffusion mode) or causal
+ * (the same weights run autoregressively). */
+typedef enum { BLT_BLOCK_BIDIR = 0, BLT_BLOCK_CAUSAL = 1 } blt_block_mask;
+
+typedef struct {
+  int32_t n_layers, d_model, n_heads, d_ffn;
+  int32_t vocab;        /* must be 257: 256 bytes + [MASK] */
+  int32_t d_global;     /* width of the global model's latents */
+  int32_t max_batch;    /* sequence slots held by a state */
+  int32_t max_ctx;      /* KV rows per sequence (prefix + one block) */
+  int32_t max_latents;  /* latent (patch) slots per sequence */
+  int32_t max_rows;     /* rows of one decoder pass, summed over its sequences */
+  int32_t max_block;    /* largest block size B (and verify window) */
+  blt_dtype dtype;
+  float rope_theta;     /* RoPE base, e.g. 10000 */
+  float rms_eps;        /* RMSNorm epsilon, e.g. 1e-5 */
+} blt_config;
+
+/* Per-layer decoder weights (device).  Cross-attention reads exactly one
+ * latent per row, so its softmax is identically 1 and only the value and
+ * output projections reach the output; the query/key projections are not
+ * taken. */
+typedef struct {
+  const void *wv_c;    /* [d][d]  cross-attention value projection        */
+  const void *wo_c;    /* [d][d]  cross-attention output projection       */
+  const void *wqkv;    /* [3d][d] self-attention q (rows 0..d-1), k, v    */
+  const void *wo;      /* [d][d]  self-attention output projection        */
+  const void *g_attn;  /* [d]     RMSNorm gain before self-attention      */
+  const void *g_ffn;   /* [d]     RMSNorm gain before the FFN             */
+  const void *w1;      /* [F][d]  FFN up projection (SiLU after it)       */
+  const void *w2;      /* [d][F]  FFN down projection                     */
+} blt_layer_weights;
+
+typedef struct {
+  const void *embed;   /* [257][d] byte + [MASK] embedding (device)      */
+  const void *w_lat;   /* [d][d_global] latent projection (device)       */
+  const void *w_out;   /* [257][d] byte head (device)                    */
+  const void *g_out;   /* [d] final RMSNorm gain (device)                */
+  const blt_layer_weights *layers; /* host array of n_layers entries    */
+} blt_weights;
+
+/* Caller-owned decode state (device), sized by blt_state_size:
+ *   kv    : keys (after RoPE) and values of cached rows,
+ *           [max_batch][n_layers][2][n_heads][max_ctx][d_model/n_heads], dtype;
+ *   cross : per-latent cross-attention contributions W_o^c W_v^c W_lat o_m,
+ *           [max_batch][max_latents][n_layers][d_model], float32.
+ * Rows beyond a sequence's committed length hold scratch (the current
+ * block's keys and values) and are overwritten by later calls. */
+typedef struct {
+  void *kv;
+  void *cross;
+} blt_state;
+
+typedef struct blt_ctx blt_ctx; /* opaque, library-owned */
+
+/* Bytes the caller must allocate for blt_state.kv and blt_state.cross. */
+blt_status blt_state_size(const blt_config *cfg, size_t *kv_bytes, size_t *cross_bytes);
+
+/* Create a context bound to `hip_stream` (a hipStream_t, 0 = null stream)
+ * and to the weights, which must stay alive and unchanged while the context
+ * lives.  Allocates the library's workspace on the current device. */
+blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_stream,
+                      blt_ctx **out);
+blt_status blt_destroy(blt_ctx *ctx);
+const char *blt_last_error(const blt_ctx *ctx);
+
+/* Make latents available to the decoder (one encoder/global pass delivers
+ * them).  For entry i: latent vector o = table + (slot[i] * seq_stride +
+ * idx[i]) * d_global (device, dtype), written as latent idx[i] of sequence
+ * slot[i]: cross[slot][idx][l] = W_o^c_l W_v^c_l W_lat o for every layer l.
+ * slot, idx: host arrays of n entries. */
+blt_status blt_latents_put(blt_ctx *ctx, const blt_state *st, int32_t n, const int32_t *slot,
+                           const int32_t *idx, const void *table, int64_t seq_stride);
+
+/* One decoder pass over clean rows only (prefill, autoregressive steps,
+ * BLT-S drafts and the causal verification pass of BLT-S / BLT-DV).
+ * For sequence b of the batch: rows start_pos[b] .. start_pos[b]+n_rows[b]-1
+ * of state slot slot[b] are computed causally over the cached prefix
+ * [0, start_pos[b]) and each other, and their keys/values are written to the
+ * cache (a start_pos below the previous length overwrites: rollback).
+ * Row j of sequence b has token bytes[b*n_max+j] (host) -- or, if `bytes` is
+ * NULL, tokens_dev[slot[b]*n_max+j] (device int32, e.g. the argmax of a
+ * previous pass) -- and reads latent lat_idx[b*n_max+j] (host).
+ * Outputs (device, nullable): argmax_out[slot[b]*n_max+j] (greedy byte of the
+ * row: lowest id among the largest of logits 0..255), conf_out (its
+ * probability), logits_out[(slot[b]*n_max+j)*257 + v] (float32).  At most
+ * max_rows rows in total; a sequence with n_rows[b] = 0 is skipped. */
+blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const int32_t *slot,
+                         const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
+                         const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
+                         int32_t *argmax_out, float *conf_out, float *logits_out);
+
+/* One BLT-D decoder pass (pytorch.kr summary, "BLT-D inference" and
+ * "BLT-D attention mask").  For sequence b: n_append[b] clean rows at
+ * start_pos[b].. (tokens append_bytes[b*n_append_max+j], latents
+ * append_lat[...], host) are appended to the cache as in blt_kv_append; then
+ * B block rows at the following positions, tokens block_tok[slot[b]*B+j]
+ * (device int32, 256 = [MASK]) and latent block_lat[b] (host), read every
+ * cached row and every block row (BIDIR) or the block rows up to themselves
+ * (CAUSAL).  Block rows are not kept as clean rows (their cache rows are
+ * scratch).  Then every still-masked block position is decided by `mode` /
+ * `alpha` and block_tok is updated in place; masked_left[slot[b]] (device)
+ * receives the number of [MASK]s left.  Optional device outputs for block
+ * rows: argmax_out/conf_out [slot[b]*B+j], logits_out [(slot[b]*B+j)*257+v]. */
+blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batch,
+                                 const int32_t *slot, const int32_t *start_pos,
+                                 const int32_t *n_append, int32_t n_append_max,
+                                 const uint8_t *append_bytes, const int32_t *append_lat,
+                                 int32_t *block_tok, int32_t B, const int32_t *block_lat,
+                                 float alpha, blt_unmask mode, blt_block_mask mask,
+                                 int32_t *argmax_out, float *conf_out, float *logits_out,
+                                 int32_t *masked_left);
+
+/* Greedy exact-match verification (pytorch.kr summary, "BLT-S and BLT-DV").
+ * For sequence slot s = slot[b] (slot NULL: s = b): draft[s*ld_draft+j]
+ * (device int32, j < r) holds the draft bytes x'_{l+1..l+r}; pred[s*ld_pred+j]
+ * (device int32, j <= r) the greedy bytes y_l..y_{l+r} of the causal pass over
+ * rows l..l+r.  accept_len[s] = number of leading j with draft[j] == pred[j];
+ * next_byte[s] = pred[accept_len[s]]: the correction at the first mismatch,
+ * or the free byte when the whole draft matched (device outputs). */
+blt_status blt_verify_accept(blt_ctx *ctx, int32_t batch, const int32_t *slot, int32_t r,
+                             const int32_t *draft, int32_t ld_draft, const int32_t *pred,
+                             int32_t ld_pred, int32_t *accept_len, int32_t *next_byte);
+
+/* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
+ * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),
+ * gb_per_seq = bytes_total / 1e9 / n_seq.  Host-only, exact integers;
+ * BLT_EINVAL on NULL, n_seq = 0 or 64-bit overflow. */
+typedef struct { uint64_t n_dec, n_encglob, n_seq; } blt_counts;
+typedef struct { uint64_t p_dec, p_enc, p_glob; uint32_t bytes_per_param; } blt_params;
+blt_status blt_bw_model(const blt_counts *c, const blt_params *p, uint64_t *bytes_total,
+                        double *gb_per_seq);
+
+/* ------------------------------------------------------------------------
+ * Decode sessions: native host drivers of the four decoding policies over
+ * the calls above (greedy BLT, BLT-D, BLT-S, BLT-DV), with the pass
+ * counters of the efficiency metrics (decoder passes and encoder/global
+ * passes per output sequence).  The encoder and global model are not part of
+ * this library: an encoder/global pass makes the requested latents of the
+ * caller's latent table available (blt_latents_put) and is counted.
+ * Patch boundaries of generated bytes come from a seeded stand-in rule: a
+ * new patch starts after byte x_i iff the current patch holds 8 bytes or the
+ * (1 + 256*x_{i-1} + x_i)-th SplitMix64 output from the sequence's salt is 0
+ * modulo 4.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  BLT_POLICY_GREEDY = 0,
+  BLT_POLICY_BLT_D = 1,
+  BLT_POLICY_BLT_S = 2,
+  BLT_POLICY_BLT_DV = 3
+} blt_policy;
+
+typedef struct {
+  blt_policy policy;
+  int32_t block;            /* B (BLT-D, BLT-DV) or draft window k (BLT-S) */
+  float alpha;              /* confidence threshold */
+  blt_unmask unmask;
+  blt_block_mask block_mask;
+  int32_t n_gen;            /* bytes to generate per sequence */
+} blt_policy_args;
+
+typedef struct blt_session blt_session;
+
+/* batch sequences in slots 0..batch-1.  Host inputs per sequence b:
+ * prompts[b] (prompt_len[b] bytes), patch_lens[b] (n_patches[b] patch
+ * lengths summing to prompt_len[b]; the prompt's last patch is complete),
+ * salt[b].  latent_table: device [batch][n_latents][d_global] (dtype) holding
+ * latent m of sequence b at (b * n_latents + m) * d_global. */
+blt_status blt_session_create(blt_ctx *ctx, const blt_state *st, int32_t batch,
+                              const uint8_t *const *prompts, const int32_t *prompt_len,
+                              const int32_t *const *patch_lens, const int32_t *n_patches,
+                              const uint64_t *salt, const void *latent_table, int32_t n_latents,
+                              blt_session **out);
+/* Prefill: latents of the prompt's patches and the cache of prompt rows
+ * 0..N-2 (the last prompt byte is the first row the policy computes).
+ * Counted apart from the decode counters. */
+blt_status blt_session_prefill(blt_session *s);
+/* Run a policy from the prefilled state until n_gen bytes per sequence are
+ * committed.  May be called again: each call restarts from the prompt. */
+blt_status blt_session_generate(blt_session *s, const blt_policy_args *args);
+/* Generated bytes of sequence b (up to cap), decoder and encoder/global
+ * passes of the last generate call, and the accepted draft lengths summed
+ * over verification rounds (BLT-S, BLT-DV). */
+blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int32_t cap,
+                              int32_t *n_out, uint64_t *n_dec, uint64_t *n_encglob,
+                              uint64_t *n_rounds, uint64_t *n_accepted);
+blt_status blt_session_destroy(blt_session *s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* BLT_H */

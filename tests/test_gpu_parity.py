@@ -1,0 +1,224 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle.
+
+Teacher-forced replays run every pass of an oracle trace on the GPU from the
+oracle's own state (same rows, same block tokens) and compare logits within
+the tolerance of the path (fp32: 1e-4 relative to the row's largest logit;
+bf16: 2e-2 absolute) and every decision whose oracle margin is outside the
+rounding band.  Session tests run the native decode drivers free-running and
+compare bytes and pass counts exactly (fp32) or against the GPU itself
+(BLT-S must reproduce greedy decoding byte for byte).
+"""
+import numpy as np
+import pytest
+
+import bltgen
+from oracle import loops
+from tests.gpu_util import decoder_for, oracle_inputs, replay_and_compare, say
+
+pytestmark = pytest.mark.gpu
+
+MINI_BF16 = bltgen.WORKLOADS[1].replace(n_layers=2, d_model=256, n_heads=4, d_ffn=1024,
+                                        d_global=512, prompt_len=300, prompt_patches=80,
+                                        n_gen=40, block=4)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import block_diffusion_byte_amd as blt
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    blt.lib()
+    yield
+
+
+def _replay(wl, policy, n_gen, gains="random", **kw):
+    w = bltgen.make_weights(wl, gains=gains)
+    W, inp, inp64 = oracle_inputs(wl, w)
+    if policy == "blt_d":
+        run = loops.blt_d(W, wl, inp64, n_gen, kw["B"], kw["alpha"], kw.get("one_step", False),
+                          kw.get("causal", False), trace=True)
+    elif policy == "blt_s":
+        run = loops.blt_s(W, wl, inp64, n_gen, kw["k"], trace=True)
+    elif policy == "blt_dv":
+        run = loops.blt_dv(W, wl, inp64, n_gen, kw["B"], kw["alpha"], kw.get("one_step", True),
+                           trace=True)
+    else:
+        run = loops.greedy(W, wl, inp64, n_gen, trace=True)
+    wl2 = wl.replace(block=max(wl.block, kw.get("B", 0), kw.get("k", 0)))
+    dec = decoder_for(wl2, w, max_batch=1, max_rows=64)
+    try:
+        worst, comp, skip = replay_and_compare(dec, wl2, inp, run, kw.get("alpha", 0.0),
+                                               kw.get("one_step", policy == "blt_dv"), wl.dtype)
+    finally:
+        dec.close()
+    say(f"{wl.name} {policy}: {len(run.passes)} passes, worst logit err {worst:.3g}, "
+        f"{comp} decisions compared, {skip} near-ties skipped")
+    assert comp > 0
+    return worst
+
+
+def test_tiny_fp32_blt_d_teacher_forced():
+    wl = bltgen.WORKLOADS[0]
+    _replay(wl, "blt_d", wl.n_gen, B=4, alpha=0.7)
+
+
+def test_tiny_fp32_blt_d_causal_block_teacher_forced():
+    wl = bltgen.WORKLOADS[0]
+    _replay(wl, "blt_d", 24, B=4, alpha=0.7, causal=True)
+
+
+def test_tiny_fp32_peaked_multi_commit_teacher_forced():
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    _replay(wl, "blt_d", 48, gains="ones", B=4, alpha=0.7)
+
+
+def test_tiny_fp32_blt_s_teacher_forced():
+    wl = bltgen.WORKLOADS[0]
+    _replay(wl, "blt_s", 32, k=8)
+
+
+def test_tiny_fp32_blt_dv_teacher_forced():
+    wl = bltgen.WORKLOADS[0]
+    _replay(wl, "blt_dv", 24, B=8, alpha=0.7, one_step=True)
+
+
+def test_mini_bf16_block16_mfma_teacher_forced():
+    # 16 block rows plus the appended clean rows: the projections run on MFMA
+    wl = MINI_BF16.replace(block=16, alpha=0.9)
+    _replay(wl, "blt_d", 32, B=16, alpha=0.9)
+
+
+def test_mini_bf16_blt_s_teacher_forced():
+    _replay(MINI_BF16, "blt_s", 24, k=8)
+
+
+def test_mini_bf16_blt_dv_teacher_forced():
+    wl = MINI_BF16.replace(block=8)
+    _replay(wl, "blt_dv", 24, B=8, alpha=0.7, one_step=True)
+
+
+# ---------------------------------------------------------------- sessions
+def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_rows=64):
+    import torch
+    import block_diffusion_byte_amd as blt
+    dec = decoder_for(wl.replace(block=block), w, max_batch=len(inps), max_rows=max_rows)
+    table = torch.from_numpy(np.stack([i["latents"] for i in inps])).to("cuda:0", dec.torch_dtype)
+    sess = blt.blt_session_create(dec.ctx, dec.state, [i["prompt"] for i in inps],
+                                  [i["prompt_patches"] for i in inps], [i["salt"] for i in inps],
+                                  table, wl.n_latents)
+    try:
+        blt.blt_session_prefill(dec.ctx, sess)
+        blt.blt_session_generate(dec.ctx, sess, policy, block, alpha, n_gen, unmask, mask)
+        res = [blt.blt_session_result(sess, b, n_gen) for b in range(len(inps))]
+    finally:
+        blt.blt_session_destroy(sess)
+        dec.close()
+    return res
+
+
+@pytest.mark.parametrize("policy", ["greedy", "blt_d", "blt_s", "blt_dv"])
+def test_tiny_fp32_sessions_match_oracle_exactly(policy):
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    w = bltgen.make_weights(wl, gains="random")
+    n_gen = 40
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        if policy == "greedy":
+            refs.append(loops.greedy(W, wl, inp64, n_gen))
+        elif policy == "blt_d":
+            refs.append(loops.blt_d(W, wl, inp64, n_gen, 4, 0.7))
+        elif policy == "blt_s":
+            refs.append(loops.blt_s(W, wl, inp64, n_gen, 8))
+        else:
+            refs.append(loops.blt_dv(W, wl, inp64, n_gen, 8, 0.7, one_step=True))
+    pid = {"greedy": blt.BLT_POLICY_GREEDY, "blt_d": blt.BLT_POLICY_BLT_D,
+           "blt_s": blt.BLT_POLICY_BLT_S, "blt_dv": blt.BLT_POLICY_BLT_DV}[policy]
+    block = {"greedy": 1, "blt_d": 4, "blt_s": 8, "blt_dv": 8}[policy]
+    unmask = blt.BLT_UNMASK_ONE_STEP if policy == "blt_dv" else blt.BLT_UNMASK_THRESHOLD
+    got = _session(wl, w, inps, pid, n_gen, block, 0.7, unmask)
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
+        if r.accept:
+            assert g["rounds"] == len(r.accept) and g["accepted"] == sum(r.accept)
+    say(f"{policy}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
+
+
+def test_tiny_fp32_peaked_session_multi_commit_exact():
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    w = bltgen.make_weights(wl)
+    W, inp, inp64 = oracle_inputs(wl, w)
+    ref = loops.blt_d(W, wl, inp64, 48, 4, 0.7)
+    got = _session(wl, w, [inp], blt.BLT_POLICY_BLT_D, 48, 4, 0.7)[0]
+    assert list(got["out"]) == ref.out and (got["n_dec"], got["n_eg"]) == (ref.n_dec, ref.n_eg)
+    assert ref.n_dec < 48
+    say(f"peaked BLT-D: {ref.n_dec} passes for 48 bytes")
+
+
+def test_blt_s_equals_greedy_on_gpu_full_size():
+    """BLT-S with k=8 at the 1B-class decoder shape (4096-byte Zipf prompt,
+    2048 bytes) reproduces greedy decoding byte for byte on the GPU."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[3]
+    w = bltgen.make_weights(wl)
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    n_gen = wl.n_gen
+    g = _session(wl, w, [inp], blt.BLT_POLICY_GREEDY, n_gen, 8, 0.0, max_rows=1024)[0]
+    s = _session(wl, w, [inp], blt.BLT_POLICY_BLT_S, n_gen, 8, 0.0, max_rows=1024)[0]
+    assert g["out"] == s["out"] and len(s["out"]) == n_gen
+    assert g["n_dec"] == n_gen
+    assert s["n_dec"] == s["rounds"] * 9 and s["n_eg"] == s["rounds"]
+    say(f"BLT-S k=8: {n_gen} bytes identical to greedy; decoder passes {s['n_dec']} vs {g['n_dec']}, "
+        f"encoder/global passes {s['n_eg']} vs {g['n_eg']}, mean accepted {s['accepted'] / s['rounds']:.2f}")
+
+
+def test_pass_is_deterministic():
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = MINI_BF16
+    w = bltgen.make_weights(wl)
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    outs = []
+    for _ in range(2):
+        dec = decoder_for(wl, w, max_batch=1, max_rows=64)
+        table = torch.from_numpy(inp["latents"]).to("cuda:0", dec.torch_dtype)
+        blt.blt_latents_put(dec.ctx, dec.state, [0] * 20, list(range(20)), table, 0)
+        z = torch.zeros(64 * 257, device="cuda:0")
+        blt.blt_kv_append(dec.ctx, dec.state, [0], [0], [40], 40, [min(i // 4, 19) for i in range(40)],
+                          bytes_=inp["prompt"][:40], logits_out=z)
+        torch.cuda.synchronize()
+        outs.append(z.cpu().numpy())
+        dec.close()
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_argument_errors_enqueue_nothing():
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    w = bltgen.make_weights(wl)
+    dec = decoder_for(wl, w, max_batch=2, max_rows=16)
+    bt = torch.full((8,), 256, dtype=torch.int32, device="cuda:0")
+    ml = torch.zeros(2, dtype=torch.int32, device="cuda:0")
+    try:
+        cases = [
+            (dict(B=5), blt.BLT_ECAPACITY),                        # B > max_block
+            (dict(start=[wl.max_ctx - 2]), blt.BLT_ECAPACITY),     # block beyond max_ctx
+            (dict(lat=[wl.n_latents]), blt.BLT_ECAPACITY),         # latent out of range
+            (dict(slot=[0, 0], start=[0, 0], lat=[0, 0]), blt.BLT_EINVAL),  # duplicate slot
+            (dict(alpha=float("nan")), blt.BLT_EINVAL),
+        ]
+        for kw, code in cases:
+            with pytest.raises(blt.BltError) as ei:
+                blt.blt_decode_block_step(dec.ctx, dec.state, kw.get("slot", [0]), kw.get("start", [0]),
+                                          bt, kw.get("B", 4), kw.get("lat", [0]), kw.get("alpha", 0.7),
+                                          masked_left=ml)
+            assert ei.value.status == code
+        with pytest.raises(blt.BltError):
+            blt.blt_kv_append(dec.ctx, dec.state, [0], [0], [17], 17, [0] * 17, bytes_=[1] * 17)
+    finally:
+        dec.close()
