@@ -36,6 +36,10 @@ bool valid_cfg(const blt_config *c, std::string *why) {
   if (c->max_block < 1 || c->max_block > kMaxBlock) return bad("max_block must be in 1..64");
   if (!(c->rope_theta > 0.f) || !isfinite(c->rope_theta)) return bad("rope_theta must be > 0");
   if (!(c->rms_eps >= 0.f) || !isfinite(c->rms_eps)) return bad("rms_eps must be >= 0");
+  if (!gemv_supported(c->dtype == BLT_BF16, c->d_model) || !gemv_supported(c->dtype == BLT_BF16, c->d_ffn) ||
+      !gemv_supported(c->dtype == BLT_BF16, c->d_global))
+    return bad("d_model, d_ffn, d_global: unsupported width (multiple of 256/128 with 1,2,3,4,6,8,12,16,24 chunks per lane)");
+  if (c->max_ctx > kAttnChunk * kMaxChunks) return bad("max_ctx above 16384");
   return true;
 }
 
@@ -117,6 +121,9 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
   HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, block_tok,
                           tokens_dev, c->h, s));
   KVGeom geo{L, g.n_heads, d / g.n_heads, g.max_ctx};
+  int kmax = 0;
+  for (const SeqDesc &sd : seqs) kmax = std::max(kmax, sd.kmax);
+  const int grid_chunks = (kmax + kAttnChunk - 1) / kAttnChunk;
   for (int l = 0; l < L; ++l) {
     const blt_layer_weights &lw = c->layers[l];
     GemmArgs a = base_args(c);
@@ -126,10 +133,17 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
     a.W = lw.wqkv; a.N = 3 * d; a.K = d;
     a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_attn;
     a.ep = EP_STORE_F32; a.out_f32 = c->qkv; a.ldo = 3 * d;
-    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
-    HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
-    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, c->max_chunks, c->rows_d,
-                                R, c->part, c->xa, s));
+    if (gemv_path(bf, R)) {
+      // RoPE and the KV write happen in the projection's epilogue
+      a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
+      a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = g.max_ctx; a.layer = l;
+      HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    } else {
+      HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+      HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
+    }
+    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, grid_chunks, c->max_chunks,
+                                c->rows_d, R, c->part, c->xa, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.wo; a.N = d; a.K = d;
@@ -202,7 +216,8 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   c->layers.assign(w->layers, w->layers + cfg->n_layers);
   const int R = cfg->max_rows, d = cfg->d_model, F = cfg->d_ffn, H = cfg->n_heads;
   const int dh = d / H;
-  c->max_chunks = (cfg->max_ctx + kAttnChunk - 1) / kAttnChunk;
+  // chunk stride of the attention partials, a multiple of 4 for float4 merges
+  c->max_chunks = (((cfg->max_ctx + kAttnChunk - 1) / kAttnChunk) + 3) & ~3;
   const size_t e = esize(*cfg);
   const size_t wide = (size_t)std::max(d, F);
   hipError_t he = hipSuccess;
@@ -215,6 +230,8 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(dalloc(&c->rinv, (size_t)R));
   chk(dalloc(&c->conf_ws, (size_t)R));
   chk(dalloc(&c->argmax_ws, (size_t)R));
+  chk(dalloc(&c->counters, (size_t)cfg->max_batch * H));
+  if (he == hipSuccess) chk(hipMemset(c->counters, 0, (size_t)cfg->max_batch * H * sizeof(int)));
   chk(hipMalloc(&c->xa, std::max<size_t>(1, (size_t)R * wide * e)));
   chk(hipMalloc(&c->xb, std::max<size_t>(1, (size_t)R * std::max(d, cfg->d_global) * e)));
   chk(dalloc(&c->rows_d, (size_t)R));
@@ -249,7 +266,7 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
 blt_status blt_destroy(blt_ctx *c) {
   if (!c) return BLT_EINVAL;
   (void)hipStreamSynchronize(c->stream);
-  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws,
+  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws, c->counters,
                   c->xa, c->xb, c->rows_d, c->seqs_d, c->offs_d, c->rope_tab};
   for (void *p : bufs)
     if (p) (void)hipFree(p);

@@ -33,6 +33,7 @@ struct blt_ctx {
   float *rinv = nullptr;      // [R]
   float *conf_ws = nullptr;   // [R]
   int32_t *argmax_ws = nullptr;
+  int *counters = nullptr;    // attention merge counters [max_batch][H], kept at zero
   void *xa = nullptr;         // GEMM activations [R][max(d, F)]
   void *xb = nullptr;         // GEMM activations [R][max(d, d_global)]
   blt::RowDesc *rows_d = nullptr;

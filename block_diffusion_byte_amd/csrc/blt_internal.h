@@ -14,7 +14,8 @@ namespace blt {
 
 constexpr int kVocab = 257;
 constexpr int kMask = 256;
-constexpr int kAttnChunk = 256;     // keys per split-K attention chunk (aligned to absolute positions)
+constexpr int kAttnChunk = 128;     // keys per split-K attention chunk (aligned to absolute positions)
+constexpr int kMaxChunks = 128;     // chunks per sequence the fused merge handles (max_ctx <= 16384)
 constexpr int kMaxBlock = 64;       // block rows per sequence handled by one wave in unmask
 constexpr int kGemvRows = 16;       // rows per GEMV row block; passes with R >= 16 use MFMA (bf16)
 
@@ -72,7 +73,17 @@ struct GemmArgs {
   const float *cross;
   const RowDesc *rows;
   int cross_layer, n_layers, max_lat, d;
+  // QKV projection with RoPE and the KV-cache write fused into the epilogue
+  // (GEMV path): outputs are taken in (j, j + d_head/2) pairs of each head.
+  int qkv_rope;
+  const float2 *rope_tab;
+  float *q_out;
+  void *kv;
+  int n_heads, d_head, max_ctx, layer;
 };
+
+// Does a pass of R rows take the GEMV path (else the MFMA GEMM)?
+inline bool gemv_path(bool bf16, int R) { return !bf16 || R < kGemvRows; }
 
 struct KVGeom {
   int n_layers, n_heads, d_head, max_ctx;
@@ -88,8 +99,9 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
                           hipStream_t s);
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int max_chunks, const RowDesc *rows,
-                            int R, float *part, void *a_out, hipStream_t s);
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
+                            const RowDesc *rows, int R, float *part, void *a_out, hipStream_t s);
+bool gemv_supported(bool bf16, int K);
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, int32_t *argmax_out, float *conf_out,
                          float *logits_out, hipStream_t s);

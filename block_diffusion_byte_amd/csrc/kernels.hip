@@ -31,10 +31,13 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);                                              // nearest, ties to even
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);   // v_cvt_pk_bf16_f32: nearest, ties to even
+}
+__device__ __forceinline__ uint32_t f2bf2(float lo, float hi) {
+  bf16x2_t v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <bool BF> struct Act;
@@ -85,40 +88,6 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Load the 16-byte chunk `c` of activation row `rr`, applying the RMSNorm
-// prologue when requested.
-template <bool BF>
-__device__ __forceinline__ uint4 load_x_chunk(const GemmArgs &a, int rr, int c, float rinv) {
-  using T = typename Act<BF>::T;
-  constexpr int EPC = Act<BF>::EPC;
-  if (a.pro == PRO_PLAIN) {
-    const T *row = (const T *)a.X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx);
-    return *(const uint4 *)(row + (int64_t)c * EPC);
-  }
-  const float *hr = a.H + (int64_t)rr * a.ldh + (int64_t)c * EPC;
-  const T *g = (const T *)a.gain + (int64_t)c * EPC;
-  uint4 gv = *(const uint4 *)g;
-  if constexpr (BF) {
-    float4 h0 = *(const float4 *)hr, h1 = *(const float4 *)(hr + 4);
-    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
-    const float hv[8] = {h0.x, h0.y, h0.z, h0.w, h1.x, h1.y, h1.z, h1.w};
-    uint32_t o[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float g0 = __uint_as_float(gw[i] << 16), g1 = __uint_as_float(gw[i] & 0xffff0000u);
-      uint32_t lo = f2bf(g0 * hv[2 * i] * rinv), hi = f2bf(g1 * hv[2 * i + 1] * rinv);
-      o[i] = lo | (hi << 16);
-    }
-    return make_uint4(o[0], o[1], o[2], o[3]);
-  } else {
-    float4 h0 = *(const float4 *)hr;
-    return make_uint4(__float_as_uint(__uint_as_float(gv.x) * h0.x * rinv),
-                      __float_as_uint(__uint_as_float(gv.y) * h0.y * rinv),
-                      __float_as_uint(__uint_as_float(gv.z) * h0.z * rinv),
-                      __float_as_uint(__uint_as_float(gv.w) * h0.w * rinv));
-  }
-}
-
 template <bool BF>
 __device__ __forceinline__ void epilogue(const GemmArgs &a, int r, int o, float y) {
   using T = typename Act<BF>::T;
@@ -150,89 +119,207 @@ __device__ __forceinline__ void epilogue(const GemmArgs &a, int r, int o, float 
 // ---------------------------------------------------------------------------
 // GEMV for passes of a few rows (weight-streaming bound).
 //
-// A workgroup (4 waves) owns 8 output rows.  Lanes are grouped by 8: group g
-// of every wave reads output row o0+g, 128 contiguous bytes per load, so
-// each load instruction of a wave streams 8 full cache lines.  The K axis is
-// split into 4 contiguous quarters, one per wave; inside a quarter lane s of
-// a group takes the 16-byte chunks s, s+8, s+16, ... in ascending order.
-// Partial sums are reduced in the group by xor-shuffles (1, 2, 4) and then
-// over the 4 waves in wave order.  That order depends on K only.
-// Activations are staged in LDS (all groups of a wave read the same chunk:
-// broadcast), in tiles of at most kTQ chunks per quarter; the tile size only
-// decides when activations are staged, never the accumulation order.
-template <bool BF, int RB>
+// A workgroup is 4 waves sharing RPW = 64/G output rows: the G lanes of a
+// group read 16*G contiguous bytes of their row per load instruction.  The K
+// axis is split into four contiguous quarters, one per wave, and lane s of a
+// group takes the chunks s, s+G, s+2G, ... (NC of them) of its quarter.  All
+// of a lane's weight chunks are loaded at kernel entry, before activations are
+// staged, so the whole weight slice is in flight at once.  Partial sums are
+// reduced over the group by xor-shuffles and then over the 4 waves in wave
+// order: the order depends on K and G only, never on the number of rows, so
+// a row's result does not depend on the rows it shares a pass with.
+// Activation rows are staged in LDS, RB rows at a time; with the RMSNorm
+// prologue the staged values are gain*h and the row's 1/rms scales the dot
+// product afterwards.
+__device__ __forceinline__ int qkv_rope_row(const GemmArgs &a, int i) {
+  // Output i of the QKV+RoPE GEMV: consecutive outputs pair (j, j + dh/2) of
+  // one head so both halves of a rotation land in the same workgroup.
+  const int half = a.d_head >> 1, p = i >> 1, which = i & 1;
+  const int hd = a.d >> 1, sec = p / hd, pp = p - sec * hd, hh = pp / half, j = pp - hh * half;
+  return sec * a.d + hh * a.d_head + j + which * half;
+}
+
+// Epilogue of the fused QKV projection: RoPE on q and k of one (j, j+dh/2)
+// pair at the row's position, q kept in f32, k and v written to the cache.
+template <bool BF>
+__device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0, float y0, float y1) {
+  using T = typename Act<BF>::T;
+  const RowDesc rd = a.rows[r];
+  const int half = a.d_head >> 1, p = i0 >> 1;
+  const int hd = a.d >> 1, sec = p / hd, pp = p - sec * hd, hh = pp / half, j = pp - hh * half;
+  const int lo = hh * a.d_head + j;
+  if (sec == 0) {
+    const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
+    a.q_out[(int64_t)r * a.d + lo] = y0 * cs.x - y1 * cs.y;
+    a.q_out[(int64_t)r * a.d + lo + half] = y1 * cs.x + y0 * cs.y;
+    return;
+  }
+  const int64_t plane = (int64_t)a.max_ctx * a.d_head;
+  int64_t base = ((((int64_t)rd.slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh) * plane +
+                 (int64_t)rd.pos * a.d_head + j;
+  T *kv = (T *)a.kv;
+  if (sec == 1) {
+    const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
+    kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
+    kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
+  } else {
+    kv[base] = from_f<T>(y0);
+    kv[base + half] = from_f<T>(y1);
+  }
+}
+
+// Raw activation data of one 16-byte staged chunk: the chunk itself (plain
+// input) or the f32 residual values it is made from (RMSNorm prologue).
+template <bool BF, int PRO> struct StageRaw;
+template <bool BF> struct StageRaw<BF, PRO_PLAIN> { uint4 v; };
+template <> struct StageRaw<true, PRO_NORM> { float4 h0, h1; };
+template <> struct StageRaw<false, PRO_NORM> { float4 h0; };
+
+template <bool BF, int PRO>
+__device__ __forceinline__ void stage_load(const GemmArgs &a, int rr, int c, StageRaw<BF, PRO> &st) {
+  using T = typename Act<BF>::T;
+  constexpr int EPC = Act<BF>::EPC;
+  if constexpr (PRO == PRO_PLAIN) {
+    const T *row = (const T *)a.X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx);
+    st.v = *(const uint4 *)(row + (int64_t)c * EPC);
+  } else {
+    const float *hr = a.H + (int64_t)rr * a.ldh + (int64_t)c * EPC;
+    st.h0 = *(const float4 *)hr;
+    if constexpr (BF) st.h1 = *(const float4 *)(hr + 4);
+  }
+}
+
+// The staged chunk (gain * h for the RMSNorm prologue) and the sum of
+// squares of its residual values, accumulated in element order.
+template <bool BF, int PRO>
+__device__ __forceinline__ uint4 stage_value(const StageRaw<BF, PRO> &st, uint4 gv, float &ss) {
+  if constexpr (PRO == PRO_PLAIN) {
+    return st.v;
+  } else if constexpr (BF) {
+    const float hv[8] = {st.h0.x, st.h0.y, st.h0.z, st.h0.w, st.h1.x, st.h1.y, st.h1.z, st.h1.w};
+    const uint32_t gw[4] = {gv.x, gv.y, gv.z, gv.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ss = fmaf(hv[2 * i], hv[2 * i], ss);
+      ss = fmaf(hv[2 * i + 1], hv[2 * i + 1], ss);
+      o[i] = f2bf2(__uint_as_float(gw[i] << 16) * hv[2 * i],
+                   __uint_as_float(gw[i] & 0xffff0000u) * hv[2 * i + 1]);
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+  } else {
+    ss = fmaf(st.h0.x, st.h0.x, ss);
+    ss = fmaf(st.h0.y, st.h0.y, ss);
+    ss = fmaf(st.h0.z, st.h0.z, ss);
+    ss = fmaf(st.h0.w, st.h0.w, ss);
+    return make_uint4(__float_as_uint(__uint_as_float(gv.x) * st.h0.x),
+                      __float_as_uint(__uint_as_float(gv.y) * st.h0.y),
+                      __float_as_uint(__uint_as_float(gv.z) * st.h0.z),
+                      __float_as_uint(__uint_as_float(gv.w) * st.h0.w));
+  }
+}
+
+template <bool BF, int G, int NC, int RB, int PRO>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
   constexpr int EPC = Act<BF>::EPC;
-  constexpr int kTQ = RB <= 8 ? 64 : 32;
-  __shared__ uint4 xs[RB * 4 * kTQ];
-  __shared__ float red[4][RB][8];
-  __shared__ float rinv_s[RB];
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 3, s = lane & 7;
-  const int o = blockIdx.x * 8 + g;
-  const bool o_ok = o < a.N;
-  const int KC = a.K / EPC, Q = KC / 4, TQ = Q < kTQ ? Q : kTQ;
-  const uint4 *wrow = (const uint4 *)((const char *)a.W + (int64_t)(o_ok ? o : 0) * a.K * (BF ? 2 : 4)) + w * Q;
+  constexpr int RPW = 64 / G;
+  constexpr int Q = NC * G, KC = 4 * Q;      // chunks per wave quarter, per row
+  constexpr int K = KC * EPC;
+  constexpr int CPT = (KC + 255) / 256;      // staged chunks per thread per row
+  extern __shared__ uint4 xs[];              // [RB][KC] staged activation rows
+  __shared__ float red[4][RB][RPW];
+  __shared__ float ssq[4][RB];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane / G, s = lane - g * G;
+  const int i = blockIdx.x * RPW + g;        // this group's output (logical index)
+  const int ic = min(i, a.N - 1);
+  const int orow = a.qkv_rope ? qkv_rope_row(a, ic) : ic;
+  const uint4 *wrow = (const uint4 *)a.W + (int64_t)orow * KC + w * Q + s;
+  uint4 gv[CPT];
+  StageRaw<BF, PRO> raw[RB][CPT];
+  uint4 wv[NC];
+  int rb = 0, nr = min(RB, a.R);
+  // Activation loads first (small, cache-resident), then the weight slice:
+  // waiting for the activations leaves every weight load in flight.
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = min(tid + 256 * k, KC - 1);
+    if constexpr (PRO == PRO_NORM) gv[k] = *(const uint4 *)((const typename Act<BF>::T *)a.gain + c * EPC);
+#pragma unroll
+    for (int r = 0; r < RB; ++r) stage_load<BF, PRO>(a, min(r, nr - 1), c, raw[r][k]);
+  }
+#pragma unroll
+  for (int u = 0; u < NC; ++u) wv[u] = wrow[u * G];
 
-  for (int rb = 0; rb < a.R; rb += RB) {
-    const int nr = min(RB, a.R - rb);
-    if (a.pro == PRO_NORM) {
-      for (int r = w; r < nr; r += 4) {
-        const float *hr = a.H + (int64_t)(rb + r) * a.ldh;
-        float ss = 0.f;
-        for (int k = lane; k < a.K; k += 64) ss = fmaf(hr[k], hr[k], ss);
-        ss = wave_sum(ss);
-        if (lane == 0) rinv_s[r] = 1.f / sqrtf(ss / (float)a.K + a.eps);
-      }
-      __syncthreads();
-    }
-    float acc[RB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r) acc[r] = 0.f;
-
-    for (int t0 = 0; t0 < Q; t0 += TQ) {
-      const int tq = min(TQ, Q - t0);
-      for (int i = tid; i < nr * 4 * tq; i += 256) {
-        const int r = i / (4 * tq), rem = i - r * 4 * tq, ww = rem / tq, j = rem - ww * tq;
-        xs[(r * 4 + ww) * kTQ + j] =
-            load_x_chunk<BF>(a, rb + r, ww * Q + t0 + j, a.pro == PRO_NORM ? rinv_s[r] : 1.f);
-      }
-      __syncthreads();
-      if (o_ok) {
-        uint4 wv[kTQ / 8];
-#pragma unroll
-        for (int u = 0; u < kTQ / 8; ++u) {
-          const int j = s + 8 * u;
-          if (j < tq) wv[u] = wrow[t0 + j];
-        }
-#pragma unroll
-        for (int u = 0; u < kTQ / 8; ++u) {
-          const int j = s + 8 * u;
-          if (j < tq) {
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-              if (r < nr) acc[r] = dot_chunk<BF>(wv[u], xs[(r * 4 + w) * kTQ + j], acc[r]);
-          }
-        }
-      }
-      __syncthreads();
-    }
+  while (true) {
+    // Thread tid stages chunks tid, tid+256, ... of every row: the same
+    // chunks for every row, so each row's sum of squares has one order.
+    float ssr[RB];
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
-      float v = acc[r];
-      v += __shfl_xor(v, 1, 64);
-      v += __shfl_xor(v, 2, 64);
-      v += __shfl_xor(v, 4, 64);
-      if (s == 0 && r < nr) red[w][r][g] = v;
+      ssr[r] = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float ssk = 0.f;                     // squares of this chunk, in element order
+        const uint4 v = stage_value<BF, PRO>(raw[r][k], gv[k], ssk);
+        const bool valid = tid + 256 * k < KC; // clamped duplicates add nothing
+        ssr[r] += valid ? ssk : 0.f;
+        if (valid) xs[r * KC + tid + 256 * k] = v;
+      }
     }
-    __syncthreads();
-    for (int i = tid; i < nr * 8; i += 256) {
-      const int r = i >> 3, gg = i & 7, oo = blockIdx.x * 8 + gg;
-      if (oo < a.N) {
-        const float y = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
-        epilogue<BF>(a, rb + r, oo, y);
+    if constexpr (PRO == PRO_NORM) {
+#pragma unroll
+      for (int r = 0; r < RB; ++r) {
+        const float v = wave_sum(ssr[r]);
+        if (lane == 0) ssq[w][r] = v;
       }
     }
     __syncthreads();
+    // one row at a time keeps only NC staged chunks live next to the weights
+    for (int r = 0; r < nr; ++r) {
+      float v = 0.f;
+#pragma unroll
+      for (int u = 0; u < NC; ++u) v = dot_chunk<BF>(wv[u], xs[r * KC + w * Q + s + u * G], v);
+#pragma unroll
+      for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
+      if (s == 0) red[w][r][g] = v;
+    }
+    __syncthreads();
+    if (a.qkv_rope) {
+      for (int t = tid; t < nr * (RPW / 2); t += 256) {
+        const int r = t / (RPW / 2), gg = 2 * (t - r * (RPW / 2));
+        const int i0 = blockIdx.x * RPW + gg;
+        if (i0 + 1 < a.N) {
+          float y0 = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
+          float y1 = ((red[0][r][gg + 1] + red[1][r][gg + 1]) + red[2][r][gg + 1]) + red[3][r][gg + 1];
+          if constexpr (PRO == PRO_NORM) {
+            const float rinv = 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
+            y0 *= rinv;
+            y1 *= rinv;
+          }
+          qkv_rope_store<BF>(a, rb + r, i0, y0, y1);
+        }
+      }
+    } else {
+      for (int t = tid; t < nr * RPW; t += 256) {
+        const int r = t / RPW, gg = t - r * RPW, oo = blockIdx.x * RPW + gg;
+        if (oo < a.N) {
+          float y = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
+          if constexpr (PRO == PRO_NORM)
+            y *= 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
+          epilogue<BF>(a, rb + r, oo, y);
+        }
+      }
+    }
+    rb += RB;
+    if (rb >= a.R) break;
+    nr = min(RB, a.R - rb);
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = min(tid + 256 * k, KC - 1);
+#pragma unroll
+      for (int r = 0; r < RB; ++r) stage_load<BF, PRO>(a, rb + min(r, nr - 1), c, raw[r][k]);
+    }
   }
 }
 
@@ -373,142 +460,226 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
 }
 
 // ---------------------------------------------------------------------------
-// Split-K attention.  Workgroup (chunk c, head h, sequence b) owns keys
-// [c*256, c*256+256) of that sequence and every row of it in the pass; row r
-// reads keys [0, kend_r).  Thread t holds key c*256+t in registers, scores are
-// staged in LDS, the softmax statistics of the chunk are (max, sum), and
-// P.V is summed by (dim, key-partition) threads.  Output per (row, head,
-// chunk): the unnormalised o[dh], m, l.
+// Split-K attention with the merge fused into the last workgroup.
+//
+// Workgroup (chunk c, head h, sequence b) owns keys [c*128, c*128+128) of
+// that sequence, for every row of the sequence in the pass; row r reads keys
+// [0, kend_r).  The K and V rows of the chunk (contiguous in the head-major
+// cache) are fetched with fully coalesced 16-byte loads and staged in LDS.
+// Scores: two threads per key, each owning half of the head dims, combined
+// by one xor-shuffle.  Softmax statistics of the chunk are (max, sum); P.V is
+// summed by (dim, key-partition) threads.  Each chunk writes (o[dh], m, l)
+// per row; the last workgroup of the (sequence, head) -- found with a device
+// counter -- merges the chunks in chunk order and writes the attention
+// output as a GEMM activation.
+constexpr int kCK = kAttnChunk;
+
 template <bool BF, int DH>
-__global__ __launch_bounds__(256) void k_attn_partial(const float *q, const void *kvp, KVGeom g,
-                                                      int layer, const SeqDesc *seqs,
-                                                      const RowDesc *rows, float *part,
-                                                      int max_chunks) {
+__global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, KVGeom g, int layer,
+                                              const SeqDesc *seqs, const RowDesc *rows, float *part,
+                                              int max_chunks) {
   using T = typename Act<BF>::T;
-  constexpr int CK = kAttnChunk, RG = 16, NP = 256 / DH, KPP = CK / NP;
-  __shared__ float qs[RG][DH];
-  __shared__ float ps[RG][CK];
-  __shared__ float op[NP][RG][DH];
+  constexpr int RG = 16;                              // rows per row group
+  constexpr int ROWB = DH * (int)sizeof(T);           // bytes of one key row
+  constexpr int LDB = ROWB + 16;                      // padded LDS row stride (bytes)
+  constexpr int CPR = ROWB / 16;                      // 16-byte chunks per key row
+  constexpr int HCH = CPR / 2;                        // chunks per half row
+  constexpr int NP = 256 / DH, KPP = kCK / NP;        // P.V key partitions
+  constexpr int PER = kCK * CPR / 256;                // K (and V) chunks per thread
+  constexpr int QPT = RG * DH / 256;                  // q elements per thread
+  __shared__ __align__(16) char ks[kCK * LDB];        // K rows, then P.V partials
+  __shared__ __align__(16) char vsm[kCK * LDB];       // V rows
+  __shared__ __align__(16) T qs[RG][DH];
+  __shared__ __align__(16) float ps[RG][kCK];         // scores, then probabilities
   __shared__ float redm[RG][4], reds[RG][4];
+  __shared__ int kends[RG];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
-  const int key0 = c * CK;
-  if (key0 >= sd.kmax) return;
+  const int key0 = c * kCK;
+  const int n_chunks = (sd.kmax + kCK - 1) / kCK;
+  if (c >= n_chunks) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
-  const T *Kb = (const T *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
-  const T *Vb = Kb + (int64_t)g.n_heads * plane;
-  const int j = key0 + t;
-  float kr[DH];
-  if (j < sd.kmax) {
-    const uint4 *kp = (const uint4 *)(Kb + (int64_t)j * DH);
-    constexpr int EPC = Act<BF>::EPC;
+  const char *Kb = (const char *)((const T *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane) + (int64_t)key0 * ROWB;
+  const char *Vb = Kb + (int64_t)g.n_heads * plane * (int64_t)sizeof(T);
+  const int nkeys = min(kCK, sd.kmax - key0);
+
+  // small loads first (q and kend of the first row group), then the chunk's
+  // K and V rows with fully coalesced 16-byte loads; indices are clamped so
+  // the loads are unconditional
+  int nr = min(RG, sd.nrows);
+  float qv[QPT];
 #pragma unroll
-    for (int u = 0; u < DH / EPC; ++u) {
-      const uint4 v = kp[u];
-      if constexpr (BF) {
-        const uint32_t vv[4] = {v.x, v.y, v.z, v.w};
+  for (int k = 0; k < QPT; ++k) {
+    const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;
+    qv[k] = q[(int64_t)(sd.row0 + min(r, nr - 1)) * d + h * DH + ee];
+  }
+  const int my_kend = rows[sd.row0 + min(t & (RG - 1), nr - 1)].kend;
+  uint4 kr[PER], vr[PER];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          kr[u * 8 + 2 * i] = __uint_as_float(vv[i] << 16);
-          kr[u * 8 + 2 * i + 1] = __uint_as_float(vv[i] & 0xffff0000u);
-        }
-      } else {
-        kr[u * 4 + 0] = __uint_as_float(v.x);
-        kr[u * 4 + 1] = __uint_as_float(v.y);
-        kr[u * 4 + 2] = __uint_as_float(v.z);
-        kr[u * 4 + 3] = __uint_as_float(v.w);
-      }
-    }
-  } else {
+  for (int u = 0; u < PER; ++u) {
+    const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
+    const int64_t off = (int64_t)min(key, nkeys - 1) * ROWB + cc * 16;
+    kr[u] = *(const uint4 *)(Kb + off);
+    vr[u] = *(const uint4 *)(Vb + off);
+  }
 #pragma unroll
-    for (int e = 0; e < DH; ++e) kr[e] = 0.f;
+  for (int k = 0; k < QPT; ++k) {
+    const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;
+    qs[r][ee] = from_f<T>(qv[k]);
+  }
+  if (t < RG) kends[t] = my_kend;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
+    *(uint4 *)(ks + key * LDB + cc * 16) = kr[u];
+    *(uint4 *)(vsm + key * LDB + cc * 16) = vr[u];
   }
   const float scale = 1.f / sqrtf((float)DH);
-  const int e = t % DH, kp = t / DH;
+  const int kk = t >> 1, hf = t & 1;                  // score phase: key kk, half hf
+  const int e = t % DH, kp = t / DH;                  // P.V phase: dim e, partition kp
+  __syncthreads();
+  // this thread's V column over its key partition stays in registers
+  float vcol[KPP];
+#pragma unroll
+  for (int j = 0; j < KPP; ++j) vcol[j] = to_f(*(const T *)(vsm + (kp * KPP + j) * LDB + e * (int)sizeof(T)));
 
-  for (int rg = 0; rg < sd.nrows; rg += RG) {
-    const int nr = min(RG, sd.nrows - rg);
-    for (int i = t; i < nr * DH; i += 256) {
-      const int r = i / DH, ee = i - r * DH;
-      qs[r][ee] = q[(int64_t)(sd.row0 + rg + r) * d + h * DH + ee];
+  for (int rg = 0;;) {
+    uint4 kh[HCH];
+#pragma unroll
+    for (int u = 0; u < HCH; ++u) kh[u] = *(const uint4 *)(ks + kk * LDB + (hf * HCH + u) * 16);
+    // scores of every row: two threads per key, one xor-shuffle
+    for (int r = 0; r < nr; ++r) {
+      float acc = 0.f;
+#pragma unroll
+      for (int u = 0; u < HCH; ++u)
+        acc = dot_chunk<BF>(kh[u], *(const uint4 *)((const char *)&qs[r][0] + (hf * HCH + u) * 16), acc);
+      acc += __shfl_xor(acc, 1, 64);
+      if (hf == 0) ps[r][kk] = (key0 + kk < kends[r]) ? acc * scale : -INFINITY;
     }
     __syncthreads();
-    for (int r = 0; r < nr; ++r) {
-      const int kend = rows[sd.row0 + rg + r].kend;
-      float s = -INFINITY;
-      if (j < kend) {
-        float acc = 0.f;
+    {
+      // softmax statistics: 16 threads per row, 8 keys each, 16-lane xor trees
+      const int r = t >> 4, sl = t & 15;
+      float sv[kCK / 16];
+      float m = -INFINITY;
 #pragma unroll
-        for (int ee = 0; ee < DH; ++ee) acc = fmaf(qs[r][ee], kr[ee], acc);
-        s = acc * scale;
+      for (int j = 0; j < kCK / 16; ++j) {
+        sv[j] = ps[r][sl * (kCK / 16) + j];
+        m = fmaxf(m, sv[j]);
       }
-      ps[r][t] = s;
-      const float m = wave_max(s);
-      if (lane == 0) redm[r][w] = m;
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+      float l = 0.f;
+#pragma unroll
+      for (int j = 0; j < kCK / 16; ++j) {
+        const float p = (sv[j] == -INFINITY) ? 0.f : expf(sv[j] - m);
+        l += p;
+        if (r < nr) ps[r][sl * (kCK / 16) + j] = p;
+      }
+#pragma unroll
+      for (int x = 1; x < 16; x <<= 1) l += __shfl_xor(l, x, 64);
+      if (sl == 0) {
+        redm[r][0] = m;
+        reds[r][0] = l;
+      }
     }
-    __syncthreads();
+    __syncthreads();                                  // K rows are free: reuse for partials
+    float *op = (float *)ks;                          // [NP][RG][DH]
     for (int r = 0; r < nr; ++r) {
-      const float m = fmaxf(fmaxf(redm[r][0], redm[r][1]), fmaxf(redm[r][2], redm[r][3]));
-      const float s = ps[r][t];
-      const float p = (s == -INFINITY) ? 0.f : expf(s - m);
-      ps[r][t] = p;
-      const float sum = wave_sum(p);
-      if (lane == 0) reds[r][w] = sum;
+      float o = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPP; j += 4) {
+        const float4 p4 = *(const float4 *)&ps[r][kp * KPP + j];
+        o = fmaf(p4.x, vcol[j], o);
+        o = fmaf(p4.y, vcol[j + 1], o);
+        o = fmaf(p4.z, vcol[j + 2], o);
+        o = fmaf(p4.w, vcol[j + 3], o);
+      }
+      op[(kp * RG + r) * DH + e] = o;
     }
-    __syncthreads();
-    float o[RG];
-#pragma unroll
-    for (int r = 0; r < RG; ++r) o[r] = 0.f;
-    for (int jj = kp * KPP; jj < (kp + 1) * KPP; ++jj) {
-      const int jg = key0 + jj;
-      if (jg >= sd.kmax) break;
-      const float v = to_f(Vb[(int64_t)jg * DH + e]);
-#pragma unroll
-      for (int r = 0; r < RG; ++r)
-        if (r < nr) o[r] = fmaf(ps[r][jj], v, o[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < RG; ++r)
-      if (r < nr) op[kp][r][e] = o[r];
     __syncthreads();
     for (int i = t; i < nr * DH; i += 256) {
       const int r = i / DH, ee = i - r * DH;
       const int row = sd.row0 + rg + r;
-      if (rows[row].kend <= key0) continue;
+      if (kends[r] <= key0) continue;
       float acc = 0.f;
 #pragma unroll
-      for (int pp = 0; pp < NP; ++pp) acc += op[pp][r][ee];
-      float *dst = part + (((int64_t)row * g.n_heads + h) * max_chunks + c) * (DH + 2);
-      dst[ee] = acc;
+      for (int pp = 0; pp < NP; ++pp) acc += op[(pp * RG + r) * DH + ee];
+      float *dst = part + ((int64_t)row * g.n_heads + h) * (DH + 2) * max_chunks + c;
+      dst[(int64_t)ee * max_chunks] = acc;
       if (ee == 0) {
-        dst[DH] = fmaxf(fmaxf(redm[r][0], redm[r][1]), fmaxf(redm[r][2], redm[r][3]));
-        dst[DH + 1] = ((reds[r][0] + reds[r][1]) + reds[r][2]) + reds[r][3];
+        dst[(int64_t)DH * max_chunks] = redm[r][0];
+        dst[(int64_t)(DH + 1) * max_chunks] = reds[r][0];
       }
+    }
+    rg += RG;
+    if (rg >= sd.nrows) break;
+    // next row group: its q rows and kends; the K rows come back from registers
+    __syncthreads();
+    nr = min(RG, sd.nrows - rg);
+#pragma unroll
+    for (int k = 0; k < QPT; ++k) {
+      const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;
+      qs[r][ee] = from_f<T>(q[(int64_t)(sd.row0 + rg + min(r, nr - 1)) * d + h * DH + ee]);
+    }
+    if (t < RG) kends[t] = rows[sd.row0 + rg + min(t, nr - 1)].kend;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
+      *(uint4 *)(ks + key * LDB + cc * 16) =
+          *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
     }
     __syncthreads();
   }
+
 }
 
-// Merge the chunks of (row, head) in chunk order and write the attention
-// output as a GEMM activation.
+
+
+
+// Merge of the chunk partials of (row, head) in chunk order, 32 chunks at a
+// time with a running max; the partial of chunk c sits at [row][h][e][c], so
+// one float4 load fetches four chunks.
 template <bool BF, int DH>
-__global__ void k_attn_merge(const float *part, const RowDesc *rows, int n_heads, int max_chunks,
-                             void *a_out) {
+__global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
+                                                   int n_heads, int max_chunks, void *a_out) {
   using T = typename Act<BF>::T;
-  const int r = blockIdx.x, h = blockIdx.y, e = threadIdx.x;
-  const int nc = (rows[r].kend + kAttnChunk - 1) / kAttnChunk;
-  const float *base = part + ((int64_t)r * n_heads + h) * max_chunks * (DH + 2);
-  float m = -INFINITY;
-  for (int c = 0; c < nc; ++c) m = fmaxf(m, base[c * (DH + 2) + DH]);
-  float l = 0.f, o = 0.f;
-  for (int c = 0; c < nc; ++c) {
-    const float f = expf(base[c * (DH + 2) + DH] - m);
-    l = fmaf(base[c * (DH + 2) + DH + 1], f, l);
-    o = fmaf(base[c * (DH + 2) + e], f, o);
+  __shared__ float fw[kMaxChunks];
+  const int row = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
+  const int nc = (rows[row].kend + kCK - 1) / kCK;
+  const float *pb = part + ((int64_t)row * n_heads + h) * (DH + 2) * max_chunks;
+  const float *pm = pb + (int64_t)DH * max_chunks, *pl = pm + max_chunks;
+  // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
+  const int c0 = min(l, nc - 1), c1 = min(l + 64, nc - 1);
+  const float m0 = pm[c0], m1 = pm[c1], l0 = pl[c0], l1 = pl[c1];
+  const bool ok0 = l < nc, ok1 = l + 64 < nc;
+  const float M = wave_max(fmaxf(ok0 ? m0 : -INFINITY, ok1 ? m1 : -INFINITY));
+  const float f0 = ok0 ? expf(m0 - M) : 0.f, f1 = ok1 ? expf(m1 - M) : 0.f;
+  const float L = wave_sum(l0 * f0 + l1 * f1);
+  fw[l] = f0;
+  fw[l + 64] = f1;
+  __syncthreads();
+  // O[e] = sum_c o_c[e] f_c in chunk order; 4 chunks per float4 load
+  for (int e = l; e < DH; e += 64) {
+    const float *po = pb + (int64_t)e * max_chunks;
+    float O = 0.f;
+    for (int cb = 0; cb < nc; cb += 32) {
+      float4 ov[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) ov[u] = *(const float4 *)(po + min(cb + 4 * u, max_chunks - 4));
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int cc = cb + 4 * u;
+        O = fmaf(cc + 0 < nc ? ov[u].x : 0.f, fw[min(cc + 0, kMaxChunks - 1)], O);
+        O = fmaf(cc + 1 < nc ? ov[u].y : 0.f, fw[min(cc + 1, kMaxChunks - 1)], O);
+        O = fmaf(cc + 2 < nc ? ov[u].z : 0.f, fw[min(cc + 2, kMaxChunks - 1)], O);
+        O = fmaf(cc + 3 < nc ? ov[u].w : 0.f, fw[min(cc + 3, kMaxChunks - 1)], O);
+      }
+    }
+    ((T *)a_out)[(int64_t)row * n_heads * DH + h * DH + e] = from_f<T>(O / L);
   }
-  ((T *)a_out)[(int64_t)r * n_heads * DH + h * DH + e] = from_f<T>(o / l);
 }
 
 // ---------------------------------------------------------------------------
@@ -593,18 +764,69 @@ __global__ void k_verify(int batch, const SeqDesc *seqs, int r, const int32_t *d
   next_byte[s] = pr[a];
 }
 
-template <bool BF>
-hipError_t gemv_dispatch(const GemmArgs &a, hipStream_t s) {
-  const dim3 grid((a.N + 7) / 8);
-  if (a.R <= 1) hipLaunchKernelGGL((k_gemv<BF, 1>), grid, dim3(256), 0, s, a);
-  else if (a.R <= 2) hipLaunchKernelGGL((k_gemv<BF, 2>), grid, dim3(256), 0, s, a);
-  else if (a.R <= 4) hipLaunchKernelGGL((k_gemv<BF, 4>), grid, dim3(256), 0, s, a);
-  else if (a.R <= 8) hipLaunchKernelGGL((k_gemv<BF, 8>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_gemv<BF, 16>), grid, dim3(256), 0, s, a);
+template <bool BF, int G, int NC, int RB, int PRO>
+hipError_t gemv_launch(const GemmArgs &a, hipStream_t s) {
+  constexpr int KC = 4 * NC * G;
+  if (a.K != KC * Act<BF>::EPC) return hipErrorInvalidValue;
+  const size_t lds = (size_t)RB * KC * 16;
+  static bool attr = false;
+  if (!attr) {
+    // allow dynamic LDS up to the 160 KB of a gfx950 CU, less the static part
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, (const void *)k_gemv<BF, G, NC, RB, PRO>);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute((const void *)k_gemv<BF, G, NC, RB, PRO>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024 - (int)fa.sharedSizeBytes);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  constexpr int RPW = 64 / G;
+  hipLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO>), dim3((a.N + RPW - 1) / RPW), dim3(256), lds, s, a);
   return hipGetLastError();
 }
 
+// Lanes per output row: 16 for narrow matrices (more workgroups), else 8.
+template <bool BF> int gemv_lanes(const GemmArgs &a) {
+  constexpr int EPC = Act<BF>::EPC;
+  return (!a.qkv_rope && a.N <= 2048 && a.K % (EPC * 64) == 0) ? 16 : 8;
+}
+
+template <bool BF, int G, int NC>
+hipError_t gemv_rows(const GemmArgs &a, hipStream_t s) {
+  // rows per block: 4 for up to 4 rows, else blocks of 8
+  if (a.pro == PRO_NORM) {
+    if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_NORM>(a, s);
+    return gemv_launch<BF, G, NC, 8, PRO_NORM>(a, s);
+  }
+  if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_PLAIN>(a, s);
+  return gemv_launch<BF, G, NC, 8, PRO_PLAIN>(a, s);
+}
+
+template <bool BF>
+hipError_t gemv_dispatch(const GemmArgs &a, hipStream_t s) {
+  constexpr int EPC = Act<BF>::EPC;
+  const int G = gemv_lanes<BF>(a), NC = a.K / (EPC * G * 4);
+#define BLT_GEMV_CASE(g, nc) \
+  if (G == g && NC == nc) return gemv_rows<BF, g, nc>(a, s);
+  BLT_GEMV_CASE(8, 1) BLT_GEMV_CASE(8, 2) BLT_GEMV_CASE(8, 3) BLT_GEMV_CASE(8, 4)
+  BLT_GEMV_CASE(8, 6) BLT_GEMV_CASE(8, 8) BLT_GEMV_CASE(8, 12) BLT_GEMV_CASE(8, 16)
+  BLT_GEMV_CASE(16, 1) BLT_GEMV_CASE(16, 2) BLT_GEMV_CASE(16, 3) BLT_GEMV_CASE(16, 4)
+  BLT_GEMV_CASE(16, 6) BLT_GEMV_CASE(16, 8) BLT_GEMV_CASE(16, 12)
+#undef BLT_GEMV_CASE
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+bool gemv_supported(bool bf16, int K) {
+  // chunk counts instantiated by gemv_dispatch for 8 lanes per row
+  const int epc = bf16 ? 8 : 4;
+  if (K % (32 * epc)) return false;
+  const int nc = K / (32 * epc);
+  return nc == 1 || nc == 2 || nc == 3 || nc == 4 || nc == 6 || nc == 8 || nc == 12 || nc == 16 ||
+         nc == 24;  // 24: only as a 16-lane matrix (12 chunks per lane)
+}
 
 hipError_t launch_gemm(bool bf16, const GemmArgs &a, float * /*rinv_ws*/, void *xnorm_ws,
                        hipStream_t s) {
@@ -651,33 +873,29 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
-                        int n_seq, int max_chunks, const RowDesc *rows, int R, float *part,
-                        void *a_out, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn_partial<BF, DH>), dim3(max_chunks, g.n_heads, n_seq), dim3(256), 0, s,
-                     q, kv, g, layer, seqs, rows, part, max_chunks);
-  hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(DH), 0, s, part, rows,
+                        int n_seq, int grid_chunks, int max_chunks, const RowDesc *rows, int R,
+                        float *part, void *a_out, hipStream_t s) {
+  hipLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s, q, kv,
+                     g, layer, seqs, rows, part, max_chunks);
+  hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
                      g.n_heads, max_chunks, a_out);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int max_chunks, const RowDesc *rows,
-                            int R, float *part, void *a_out, hipStream_t s) {
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
+                            const RowDesc *rows, int R, float *part, void *a_out, hipStream_t s) {
+#define BLT_ATTN(dh)                                                                              \
+  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,  \
+                                  part, a_out, s);                                                \
+  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,      \
+                              part, a_out, s);
   switch (g.d_head) {
-    case 32:
-      if (bf16) attn_launch<true, 32>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      else attn_launch<false, 32>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      break;
-    case 64:
-      if (bf16) attn_launch<true, 64>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      else attn_launch<false, 64>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      break;
-    case 128:
-      if (bf16) attn_launch<true, 128>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      else attn_launch<false, 128>(q, kv, g, layer, seqs, n_seq, max_chunks, rows, R, part, a_out, s);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case 32: BLT_ATTN(32) break;
+    case 64: BLT_ATTN(64) break;
+    case 128: BLT_ATTN(128) break;
+    default: return hipErrorInvalidValue;
   }
+#undef BLT_ATTN
   return hipGetLastError();
 }
 

@@ -70,7 +70,7 @@ def masked_attention(q, k, v, allow):
     step = max(1, int(2e7 // max(1, H * m)))             # bound the score tensor
     for i0 in range(0, n, step):
         i1 = min(n, i0 + step)
-        qh = q[i0:i1].transpose(1, 0, 2)                  # [H, r, dh]
+        qh = np.ascontiguousarray(q[i0:i1].transpose(1, 0, 2))   # [H, r, dh]
         s = (qh @ kt) / np.sqrt(dh)                       # [H, r, m]
         s = np.where(allow[None, i0:i1, :], s, -np.inf)
         s = s - s.max(axis=-1, keepdims=True)
