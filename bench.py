@@ -23,6 +23,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+PROFILE_MD = os.path.join(ROOT, "profiles", "k_attn_bltd4_bf16_b1_ctx4096.md")
+KERNELS_SRC = os.path.join(ROOT, "block_diffusion_byte_amd", "csrc", "kernels.hip")
+
+
+def measured_traffic(workload_index):
+    """HBM bytes per attention launch from the committed rocprofv3 PMC summary
+    (FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when the summary
+    is for another workload or the kernel source changed since it was taken."""
+    import hashlib
+    if workload_index != 1 or not os.path.exists(PROFILE_MD):
+        return None
+    fields = {}
+    for line in open(PROFILE_MD):
+        if ":" in line and not line.startswith(("#", "-", "|", "`")):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    src = hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()
+    if fields.get("kernels_hip_sha256") != src:
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -33,7 +56,10 @@ def parse():
     ap.add_argument("--workload", type=int, default=1, help="index of the workload (0..4)")
     ap.add_argument("--cpu-bytes", type=int, default=None,
                     help="bytes the CPU oracle decodes for the baseline (default: per workload)")
-    ap.add_argument("--cpu-ctx", type=int, default=1024, help="context bytes of the CPU sample")
+    ap.add_argument("--cpu-ctx", type=int, default=2048, help="context bytes of the CPU sample")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB ten times (the "
+                         "reference kernel for scaling HBM traffic counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--profile", action="store_true",
                     help="also time kernel families with HIP events in a second pass")
@@ -86,6 +112,18 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        x = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        y = torch.empty_like(x)
+        x.fill_(1)
+        for _ in range(10):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                          "launches": 10}))
+        return
+
     import bltgen
     import block_diffusion_byte_amd as blt
     from oracle import proxy
@@ -123,6 +161,21 @@ def main():
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Same steps again with the attention kernel bracketed by HIP events on the
+    # library's stream: its average launch duration and algorithmic bytes.
+    blt.blt_profile_enable(dec.ctx, blt.BLT_PROF_ATTENTION)
+    blt.blt_profile_read(dec.ctx, reset=True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed_prof = time.perf_counter() - t1
+    launches, kern_ms, kern_bytes = blt.blt_profile_read(dec.ctx, reset=True)
+    blt.blt_profile_enable(dec.ctx, blt.BLT_PROF_OFF)
+    avg_us = 1e3 * kern_ms / max(launches, 1)
+    bytes_per_launch = kern_bytes / max(launches, 1)
+    achieved = bytes_per_launch / (avg_us * 1e-6) / 1e9
     res = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
     total_bytes = sum(r["n"] for r in res) * args.steps
     n_dec = sum(r["n_dec"] for r in res)
@@ -149,6 +202,11 @@ def main():
                    "heads": wl.n_heads, "ffn": wl.d_ffn, "d_global": wl.d_global,
                    "prompt_bytes": wl.prompt_len, "latents": wl.prompt_patches,
                    "bytes_generated": wl.n_gen},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
+                     "kernel": "k_attn (split-K attention partials)",
+                     "launches": launches, "avg_us": avg_us, "bytes_per_launch": bytes_per_launch,
+                     "ms_per_step_with_events": 1e3 * elapsed_prof / args.steps},
         "counters": {"decoder_passes_per_seq": n_dec / wl.batch,
                      "encglob_passes_per_seq": n_eg / wl.batch,
                      "proxy_gb_per_seq_counted_params": gb_counted,
@@ -156,7 +214,7 @@ def main():
                      "prefill_s": t_prefill},
     }
     if not args.no_cpu:
-        n_cpu = args.cpu_bytes or {0: 64, 1: 16, 2: 16, 3: 16, 4: 8}[args.workload]
+        n_cpu = args.cpu_bytes or {0: 64, 1: 128, 2: 128, 3: 128, 4: 48}[args.workload]
         out["cpu_baseline"] = cpu_baseline(wl, w, n_cpu, args.cpu_ctx)
     blt.blt_session_destroy(sess)
     dec.close()

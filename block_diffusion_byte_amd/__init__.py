@@ -25,6 +25,7 @@ BLT_F32, BLT_BF16 = 0, 1
 BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP = 0, 1
 BLT_BLOCK_BIDIR, BLT_BLOCK_CAUSAL = 0, 1
 BLT_POLICY_GREEDY, BLT_POLICY_BLT_D, BLT_POLICY_BLT_S, BLT_POLICY_BLT_DV = 0, 1, 2, 3
+BLT_PROF_OFF, BLT_PROF_ATTENTION = 0, 1
 MASK = 256
 VOCAB = 257
 
@@ -32,7 +33,7 @@ EXPORTS = [
     "blt_state_size", "blt_create", "blt_destroy", "blt_last_error", "blt_latents_put",
     "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
-    "blt_session_destroy",
+    "blt_session_destroy", "blt_profile_enable", "blt_profile_read",
 ]
 
 
@@ -105,6 +106,8 @@ def lib():
             "blt_session_generate": [P, P],
             "blt_session_result": [P, I32, P, I32, P, P, P, P, P],
             "blt_session_destroy": [P],
+            "blt_profile_enable": [P, I32],
+            "blt_profile_read": [P, P, P, P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -207,6 +210,17 @@ def blt_verify_accept(ctx, r, draft, ld_draft, pred, ld_pred, accept_len, next_b
     _check("blt_verify_accept", lib().blt_verify_accept(
         ctx, batch, sp, r, _ptr(draft), ld_draft, _ptr(pred), ld_pred, _ptr(accept_len),
         _ptr(next_byte)), ctx)
+
+
+def blt_profile_enable(ctx, family):
+    _check("blt_profile_enable", lib().blt_profile_enable(ctx, family), ctx)
+
+
+def blt_profile_read(ctx, reset=False):
+    n, ms, by = C.c_uint64(), C.c_double(), C.c_double()
+    _check("blt_profile_read", lib().blt_profile_read(ctx, C.byref(n), C.byref(ms), C.byref(by),
+                                                      1 if reset else 0), ctx)
+    return n.value, ms.value, by.value
 
 
 def blt_bw_model(n_dec, n_encglob, n_seq, p_dec, p_enc, p_glob, bytes_per_param=2):

@@ -94,6 +94,34 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
   return BLT_OK;
 }
 
+// Next event pair of the profiling pool (collecting first when it is full).
+blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1) {
+  *ev0 = *ev1 = nullptr;
+  if (c->prof_used == c->prof_pool.size()) {
+    blt_status bs = prof_collect(c);
+    if (bs != BLT_OK) return bs;
+  }
+  ProfRec &r = c->prof_pool[c->prof_used++];
+  r.bytes = bytes;
+  *ev0 = r.ev0;
+  *ev1 = r.ev1;
+  return BLT_OK;
+}
+
+blt_status prof_collect(blt_ctx *c) {
+  if (c->prof_used == 0) return BLT_OK;
+  HIP_TRY(c, hipStreamSynchronize(c->stream));
+  for (size_t i = 0; i < c->prof_used; ++i) {
+    float ms = 0.f;
+    HIP_TRY(c, hipEventElapsedTime(&ms, c->prof_pool[i].ev0, c->prof_pool[i].ev1));
+    c->prof_ms += ms;
+    c->prof_bytes += c->prof_pool[i].bytes;
+    c->prof_launches += 1;
+  }
+  c->prof_used = 0;
+  return BLT_OK;
+}
+
 GemmArgs base_args(const blt_ctx *c) {
   GemmArgs a;
   memset(&a, 0, sizeof(a));
@@ -142,8 +170,16 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
       HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
       HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
     }
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (c->prof_family == BLT_PROF_ATTENTION) {
+      // algorithmic bytes: the K and V rows the pass's rows must read
+      double kvb = 0;
+      for (const SeqDesc &sd : seqs) kvb += (double)sd.kmax * 2.0 * d * (bf ? 2 : 4);
+      blt_status pb = prof_next(c, kvb, &e0, &e1);
+      if (pb != BLT_OK) return pb;
+    }
     HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, grid_chunks, c->max_chunks,
-                                c->rows_d, R, c->part, c->xa, s));
+                                c->rows_d, R, c->part, c->xa, e0, e1, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.wo; a.N = d; a.K = d;
@@ -216,8 +252,7 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   c->layers.assign(w->layers, w->layers + cfg->n_layers);
   const int R = cfg->max_rows, d = cfg->d_model, F = cfg->d_ffn, H = cfg->n_heads;
   const int dh = d / H;
-  // chunk stride of the attention partials, a multiple of 4 for float4 merges
-  c->max_chunks = (((cfg->max_ctx + kAttnChunk - 1) / kAttnChunk) + 3) & ~3;
+  c->max_chunks = (cfg->max_ctx + kAttnChunk - 1) / kAttnChunk;
   const size_t e = esize(*cfg);
   const size_t wide = (size_t)std::max(d, F);
   hipError_t he = hipSuccess;
@@ -273,6 +308,10 @@ blt_status blt_destroy(blt_ctx *c) {
   for (int i = 0; i < kRing; ++i) {
     if (c->ring[i].host) (void)hipHostFree(c->ring[i].host);
     if (c->ring[i].ev) (void)hipEventDestroy(c->ring[i].ev);
+  }
+  for (ProfRec &r : c->prof_pool) {
+    if (r.ev0) (void)hipEventDestroy(r.ev0);
+    if (r.ev1) (void)hipEventDestroy(r.ev1);
   }
   delete c;
   return BLT_OK;
@@ -446,6 +485,37 @@ blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int
   if (bs != BLT_OK) return bs;
   HIP_TRY(c, launch_verify(batch, c->seqs_d, r, draft, ld_draft, pred, ld_pred, accept_len,
                            next_byte, c->stream));
+  return BLT_OK;
+}
+
+blt_status blt_profile_enable(blt_ctx *c, int32_t family) {
+  if (!c) return BLT_EINVAL;
+  if (family != BLT_PROF_OFF && family != BLT_PROF_ATTENTION)
+    return fail(c, BLT_EINVAL, "blt_profile_enable: unknown kernel family");
+  if (family != BLT_PROF_OFF && c->prof_pool.empty()) {
+    c->prof_pool.resize(4096);
+    for (ProfRec &r : c->prof_pool) {
+      HIP_TRY(c, hipEventCreate(&r.ev0));
+      HIP_TRY(c, hipEventCreate(&r.ev1));
+    }
+  }
+  blt_status bs = prof_collect(c);
+  c->prof_family = family;
+  return bs;
+}
+
+blt_status blt_profile_read(blt_ctx *c, uint64_t *launches, double *total_ms, double *bytes,
+                            int32_t reset) {
+  if (!c || !launches || !total_ms || !bytes) return BLT_EINVAL;
+  blt_status bs = prof_collect(c);
+  if (bs != BLT_OK) return bs;
+  *launches = c->prof_launches;
+  *total_ms = c->prof_ms;
+  *bytes = c->prof_bytes;
+  if (reset) {
+    c->prof_launches = 0;
+    c->prof_ms = c->prof_bytes = 0;
+  }
   return BLT_OK;
 }
 

@@ -10,6 +10,12 @@ namespace blt {
 
 constexpr int kRing = 8;  // pinned staging slots for per-pass descriptors
 
+// Event pairs bracketing launches of one kernel family (profiling aid).
+struct ProfRec {
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  double bytes = 0;
+};
+
 struct StageSlot {
   void *host = nullptr;
   hipEvent_t ev = nullptr;
@@ -45,11 +51,19 @@ struct blt_ctx {
   int ring_next = 0;
   size_t seq_off = 0, off_off = 0;
   std::string err;
+  // profiling: family being timed, event pool, pending and accumulated figures
+  int prof_family = 0;
+  std::vector<blt::ProfRec> prof_pool;
+  size_t prof_used = 0;
+  uint64_t prof_launches = 0;
+  double prof_ms = 0, prof_bytes = 0;
 };
 
 namespace blt {
 blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
                       const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs);
+blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1);
+blt_status prof_collect(blt_ctx *c);
 blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
                     const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int one_step,

@@ -98,9 +98,11 @@ hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const 
 hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
                           hipStream_t s);
+// ev0/ev1 (nullable) are recorded right before and after the partials kernel.
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            const RowDesc *rows, int R, float *part, void *a_out, hipStream_t s);
+                            const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
+                            hipEvent_t ev1, hipStream_t s);
 bool gemv_supported(bool bf16, int K);
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, int32_t *argmax_out, float *conf_out,

@@ -15,6 +15,7 @@
 // not depend on the other rows of its pass: the GEMV path splits K over
 // lanes and waves identically for any row count, and attention splits keys
 // into chunks aligned to absolute positions merged in chunk order.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <math.h>
 
@@ -148,8 +149,8 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
   const int half = a.d_head >> 1, p = i0 >> 1;
   const int hd = a.d >> 1, sec = p / hd, pp = p - sec * hd, hh = pp / half, j = pp - hh * half;
   const int lo = hh * a.d_head + j;
+  const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
   if (sec == 0) {
-    const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
     a.q_out[(int64_t)r * a.d + lo] = y0 * cs.x - y1 * cs.y;
     a.q_out[(int64_t)r * a.d + lo + half] = y1 * cs.x + y0 * cs.y;
     return;
@@ -159,7 +160,6 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
                  (int64_t)rd.pos * a.d_head + j;
   T *kv = (T *)a.kv;
   if (sec == 1) {
-    const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
     kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
     kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
@@ -607,11 +607,11 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, K
       float acc = 0.f;
 #pragma unroll
       for (int pp = 0; pp < NP; ++pp) acc += op[(pp * RG + r) * DH + ee];
-      float *dst = part + ((int64_t)row * g.n_heads + h) * (DH + 2) * max_chunks + c;
-      dst[(int64_t)ee * max_chunks] = acc;
+      float *dst = part + (((int64_t)row * g.n_heads + h) * max_chunks + c) * (DH + 2);
+      dst[ee] = acc;
       if (ee == 0) {
-        dst[(int64_t)DH * max_chunks] = redm[r][0];
-        dst[(int64_t)(DH + 1) * max_chunks] = reds[r][0];
+        dst[DH] = redm[r][0];
+        dst[DH + 1] = reds[r][0];
       }
     }
     rg += RG;
@@ -649,11 +649,11 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   __shared__ float fw[kMaxChunks];
   const int row = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const int nc = (rows[row].kend + kCK - 1) / kCK;
-  const float *pb = part + ((int64_t)row * n_heads + h) * (DH + 2) * max_chunks;
-  const float *pm = pb + (int64_t)DH * max_chunks, *pl = pm + max_chunks;
+  const float *pb = part + ((int64_t)row * n_heads + h) * max_chunks * (DH + 2);
   // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
   const int c0 = min(l, nc - 1), c1 = min(l + 64, nc - 1);
-  const float m0 = pm[c0], m1 = pm[c1], l0 = pl[c0], l1 = pl[c1];
+  const float m0 = pb[c0 * (DH + 2) + DH], m1 = pb[c1 * (DH + 2) + DH];
+  const float l0 = pb[c0 * (DH + 2) + DH + 1], l1 = pb[c1 * (DH + 2) + DH + 1];
   const bool ok0 = l < nc, ok1 = l + 64 < nc;
   const float M = wave_max(fmaxf(ok0 ? m0 : -INFINITY, ok1 ? m1 : -INFINITY));
   const float f0 = ok0 ? expf(m0 - M) : 0.f, f1 = ok1 ? expf(m1 - M) : 0.f;
@@ -661,22 +661,17 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   fw[l] = f0;
   fw[l + 64] = f1;
   __syncthreads();
-  // O[e] = sum_c o_c[e] f_c in chunk order; 4 chunks per float4 load
+  // O[e] = sum_c o_c[e] f_c in chunk order; the lanes of a chunk read one
+  // contiguous row of the partials, 32 chunks in flight at a time
   for (int e = l; e < DH; e += 64) {
-    const float *po = pb + (int64_t)e * max_chunks;
     float O = 0.f;
     for (int cb = 0; cb < nc; cb += 32) {
-      float4 ov[8];
+      float ov[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) ov[u] = *(const float4 *)(po + min(cb + 4 * u, max_chunks - 4));
+      for (int u = 0; u < 32; ++u) ov[u] = pb[min(cb + u, nc - 1) * (DH + 2) + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int cc = cb + 4 * u;
-        O = fmaf(cc + 0 < nc ? ov[u].x : 0.f, fw[min(cc + 0, kMaxChunks - 1)], O);
-        O = fmaf(cc + 1 < nc ? ov[u].y : 0.f, fw[min(cc + 1, kMaxChunks - 1)], O);
-        O = fmaf(cc + 2 < nc ? ov[u].z : 0.f, fw[min(cc + 2, kMaxChunks - 1)], O);
-        O = fmaf(cc + 3 < nc ? ov[u].w : 0.f, fw[min(cc + 3, kMaxChunks - 1)], O);
-      }
+      for (int u = 0; u < 32; ++u)
+        O = fmaf(cb + u < nc ? ov[u] : 0.f, fw[min(cb + u, kMaxChunks - 1)], O);
     }
     ((T *)a_out)[(int64_t)row * n_heads * DH + h * DH + e] = from_f<T>(O / L);
   }
@@ -874,21 +869,28 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
                         int n_seq, int grid_chunks, int max_chunks, const RowDesc *rows, int R,
-                        float *part, void *a_out, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s, q, kv,
-                     g, layer, seqs, rows, part, max_chunks);
+                        float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+  if (ev0) {
+    // events stamped by the dispatch itself at the kernel's start and end
+    hipExtLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s,
+                          ev0, ev1, 0, q, kv, g, layer, seqs, rows, part, max_chunks);
+  } else {
+    hipLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s, q,
+                       kv, g, layer, seqs, rows, part, max_chunks);
+  }
   hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
                      g.n_heads, max_chunks, a_out);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            const RowDesc *rows, int R, float *part, void *a_out, hipStream_t s) {
+                            const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
+                            hipEvent_t ev1, hipStream_t s) {
 #define BLT_ATTN(dh)                                                                              \
   if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,  \
-                                  part, a_out, s);                                                \
+                                  part, a_out, ev0, ev1, s);                                      \
   else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,      \
-                              part, a_out, s);
+                              part, a_out, ev0, ev1, s);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;

@@ -184,6 +184,19 @@ blt_status blt_verify_accept(blt_ctx *ctx, int32_t batch, const int32_t *slot, i
                              const int32_t *draft, int32_t ld_draft, const int32_t *pred,
                              int32_t ld_pred, int32_t *accept_len, int32_t *next_byte);
 
+/* Kernel timing with HIP events on the context's stream (profiling aid).
+ * While a family is enabled, every launch of it is bracketed by an event
+ * pair.  blt_profile_read synchronises the stream and returns the launches
+ * timed so far, their summed duration and the algorithmic bytes they must
+ * move: for BLT_PROF_ATTENTION, the key and value rows of the cache that the
+ * pass's rows read (sum over sequences of kmax * 2 * d_model * element size;
+ * kmax = the largest key count of the sequence's rows).  reset != 0 clears
+ * the totals.  Enabling or disabling collects pending events first. */
+typedef enum { BLT_PROF_OFF = 0, BLT_PROF_ATTENTION = 1 } blt_prof_family;
+blt_status blt_profile_enable(blt_ctx *ctx, int32_t family);
+blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, double *bytes,
+                            int32_t reset);
+
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
  * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),
  * gb_per_seq = bytes_total / 1e9 / n_seq.  Host-only, exact integers;
