@@ -61,8 +61,8 @@ def parse():
                     help="only run a plain device-to-device copy of MIB MiB ten times (the "
                          "reference kernel for scaling HBM traffic counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--profile", action="store_true",
-                    help="also time kernel families with HIP events in a second pass")
+    ap.add_argument("--no-graphs", action="store_true",
+                    help="launch every decoder pass directly instead of replaying HIP graphs")
     return ap.parse_args()
 
 
@@ -137,6 +137,8 @@ def main():
                       d_ffn=wl.d_ffn, d_global=wl.d_global, dtype=wl.dtype, max_batch=wl.batch,
                       max_ctx=wl.max_ctx, max_latents=wl.n_latents, max_rows=max_rows,
                       max_block=wl.block, rope_theta=wl.rope_theta, rms_eps=wl.rms_eps, device=dev)
+    if args.no_graphs:
+        blt.blt_graphs_enable(dec.ctx, False)
     table = torch.empty((wl.batch, wl.n_latents, wl.d_global), dtype=dec.torch_dtype, device=dev)
     for b, inp in enumerate(inps):
         table[b].copy_(torch.from_numpy(inp["latents"]))

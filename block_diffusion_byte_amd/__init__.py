@@ -33,7 +33,7 @@ EXPORTS = [
     "blt_state_size", "blt_create", "blt_destroy", "blt_last_error", "blt_latents_put",
     "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
-    "blt_session_destroy", "blt_profile_enable", "blt_profile_read",
+    "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
 ]
 
 
@@ -108,6 +108,7 @@ def lib():
             "blt_session_destroy": [P],
             "blt_profile_enable": [P, I32],
             "blt_profile_read": [P, P, P, P, I32],
+            "blt_graphs_enable": [P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -210,6 +211,10 @@ def blt_verify_accept(ctx, r, draft, ld_draft, pred, ld_pred, accept_len, next_b
     _check("blt_verify_accept", lib().blt_verify_accept(
         ctx, batch, sp, r, _ptr(draft), ld_draft, _ptr(pred), ld_pred, _ptr(accept_len),
         _ptr(next_byte)), ctx)
+
+
+def blt_graphs_enable(ctx, enable):
+    _check("blt_graphs_enable", lib().blt_graphs_enable(ctx, 1 if enable else 0), ctx)
 
 
 def blt_profile_enable(ctx, family):

@@ -71,7 +71,9 @@ hipError_t dalloc(T **p, size_t n) {
 namespace blt {
 
 // Copy this pass's descriptors into a pinned staging slot and then to the
-// device.  Slots rotate; a slot is reused only after its previous copy ended.
+// device buffer of the same layout (sequences, rows, row offsets): one copy
+// carries the sequences and the rows.  Slots rotate; a slot is reused only
+// after its previous copy ended.
 blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
                       const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs) {
   StageSlot &sl = c->ring[c->ring_next];
@@ -83,12 +85,16 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
   char *p = (char *)sl.host;
   const size_t rb = rows.size() * sizeof(RowDesc), sb = seqs.size() * sizeof(SeqDesc);
   const size_t ob = offs ? offs->size() * sizeof(int64_t) : 0;
-  if (rb) memcpy(p, rows.data(), rb);
-  if (sb) memcpy(p + c->seq_off, seqs.data(), sb);
+  if (sb) memcpy(p, seqs.data(), sb);
+  if (rb) memcpy(p + c->row_off, rows.data(), rb);
   if (ob) memcpy(p + c->off_off, offs->data(), ob);
-  if (rb) HIP_TRY(c, hipMemcpyAsync(c->rows_d, p, rb, hipMemcpyHostToDevice, c->stream));
-  if (sb) HIP_TRY(c, hipMemcpyAsync(c->seqs_d, p + c->seq_off, sb, hipMemcpyHostToDevice, c->stream));
-  if (ob) HIP_TRY(c, hipMemcpyAsync(c->offs_d, p + c->off_off, ob, hipMemcpyHostToDevice, c->stream));
+  if (rb)
+    HIP_TRY(c, hipMemcpyAsync(c->desc_d, p, c->row_off + rb, hipMemcpyHostToDevice, c->stream));
+  else if (sb)
+    HIP_TRY(c, hipMemcpyAsync(c->desc_d, p, sb, hipMemcpyHostToDevice, c->stream));
+  if (ob)
+    HIP_TRY(c, hipMemcpyAsync((char *)c->desc_d + c->off_off, p + c->off_off, ob,
+                              hipMemcpyHostToDevice, c->stream));
   HIP_TRY(c, hipEventRecord(sl.ev, c->stream));
   sl.pending = true;
   return BLT_OK;
@@ -132,26 +138,29 @@ GemmArgs base_args(const blt_ctx *c) {
   return a;
 }
 
-// The kernel sequence of one decoder pass over `rows` (grouped by `seqs`).
-blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
-                    const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
-                    const int32_t *tokens_dev, bool unmask, float alpha, int one_step,
-                    int32_t *masked_left, int32_t *argmax_out, float *conf_out,
-                    float *logits_out) {
+// Arguments of the kernel sequence of one pass besides the staged descriptors.
+struct PassLaunch {
+  int R, S, grid_chunks;
+  const blt_state *st;
+  const int32_t *block_tok, *tokens_dev;
+  bool unmask;
+  float alpha;
+  int one_step;
+  int32_t *masked_left, *argmax_out;
+  float *conf_out, *logits_out;
+  const std::vector<SeqDesc> *seqs;  // for the profiling byte counts
+};
+
+// The kernel sequence of one decoder pass over the staged rows, on stream s.
+blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
   const blt_config &g = c->cfg;
-  const int R = (int)rows.size(), S = (int)seqs.size();
-  const int d = g.d_model, F = g.d_ffn, L = g.n_layers;
+  const int R = p.R, S = p.S, d = g.d_model, F = g.d_ffn, L = g.n_layers;
   const bool bf = c->bf16;
-  blt_status bs = stage_pass(c, rows, seqs, nullptr);
-  if (bs != BLT_OK) return bs;
-  hipStream_t s = c->stream;
+  const blt_state *st = p.st;
   const float *cross = (const float *)st->cross;
-  HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, block_tok,
-                          tokens_dev, c->h, s));
-  KVGeom geo{L, g.n_heads, d / g.n_heads, g.max_ctx};
-  int kmax = 0;
-  for (const SeqDesc &sd : seqs) kmax = std::max(kmax, sd.kmax);
-  const int grid_chunks = (kmax + kAttnChunk - 1) / kAttnChunk;
+  HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, p.block_tok,
+                          p.tokens_dev, c->h, s));
+  KVGeom geo{L, g.n_heads, d / g.n_heads, kv_rows(g.max_ctx)};
   for (int l = 0; l < L; ++l) {
     const blt_layer_weights &lw = c->layers[l];
     GemmArgs a = base_args(c);
@@ -164,7 +173,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
     if (gemv_path(bf, R)) {
       // RoPE and the KV write happen in the projection's epilogue
       a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
-      a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = g.max_ctx; a.layer = l;
+      a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = kv_rows(g.max_ctx); a.layer = l;
       HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
     } else {
       HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
@@ -174,11 +183,11 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
     if (c->prof_family == BLT_PROF_ATTENTION) {
       // algorithmic bytes: the K and V rows the pass's rows must read
       double kvb = 0;
-      for (const SeqDesc &sd : seqs) kvb += (double)sd.kmax * 2.0 * d * (bf ? 2 : 4);
+      for (const SeqDesc &sd : *p.seqs) kvb += (double)sd.kmax * 2.0 * d * (bf ? 2 : 4);
       blt_status pb = prof_next(c, kvb, &e0, &e1);
       if (pb != BLT_OK) return pb;
     }
-    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, grid_chunks, c->max_chunks,
+    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, c->max_chunks,
                                 c->rows_d, R, c->part, c->xa, e0, e1, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
@@ -206,11 +215,73 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
   a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
   HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
-  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, argmax_out, conf_out,
-                           logits_out, s));
-  if (unmask)
-    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, (int32_t *)block_tok, alpha,
-                             one_step, masked_left, s));
+  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, p.argmax_out,
+                           p.conf_out, p.logits_out, s));
+  if (p.unmask)
+    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, (int32_t *)p.block_tok,
+                             p.alpha, p.one_step, p.masked_left, s));
+  return BLT_OK;
+}
+
+void drop_graphs(blt_ctx *c) {
+  for (auto &kv : c->graph_cache)
+    if (kv.second.exec) (void)hipGraphExecDestroy(kv.second.exec);
+  c->graph_cache.clear();
+}
+
+// One decoder pass over `rows` (grouped by `seqs`): the descriptors are
+// staged, then the kernel sequence is launched directly or, for a pass shape
+// seen before, replayed from a cached graph (captured on the context's own
+// capture stream, launched on its stream).
+blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
+                    const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
+                    const int32_t *tokens_dev, bool unmask, float alpha, int one_step,
+                    int32_t *masked_left, int32_t *argmax_out, float *conf_out,
+                    float *logits_out) {
+  blt_status bs = stage_pass(c, rows, seqs, nullptr);
+  if (bs != BLT_OK) return bs;
+  int kmax = 0;
+  for (const SeqDesc &sd : seqs) kmax = std::max(kmax, sd.kmax);
+  PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk, st,
+               block_tok, tokens_dev, unmask, alpha, one_step, masked_left, argmax_out, conf_out,
+               logits_out, &seqs};
+  if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
+  // chunk-grid buckets of 4 keep the number of distinct graphs small; the
+  // chunks past a sequence's kmax leave at once
+  p.grid_chunks = std::min((p.grid_chunks + 3) / 4 * 4, c->max_chunks);
+  PassKey key;
+  memset(&key, 0, sizeof(key));
+  key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.unmask = unmask;
+  key.one_step = one_step;
+  memcpy(&key.alpha_bits, &alpha, sizeof(float));
+  key.kv = st->kv; key.cross = st->cross; key.block_tok = block_tok; key.tokens_dev = tokens_dev;
+  key.masked_left = masked_left; key.argmax_out = argmax_out; key.conf_out = conf_out;
+  key.logits_out = logits_out;
+  auto it = c->graph_cache.find(key);
+  if (it == c->graph_cache.end()) {
+    // first sighting: launch directly (also prepares every kernel's attributes)
+    if (c->graph_cache.size() >= kMaxGraphs) drop_graphs(c);
+    c->graph_cache.emplace(key, GraphEntry{});
+    return enqueue_pass(c, p, c->stream);
+  }
+  GraphEntry &ge = it->second;
+  if (!ge.exec) {
+    HIP_TRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
+    const blt_status ls = enqueue_pass(c, p, c->cap_stream);
+    hipGraph_t graph = nullptr;
+    const hipError_t ee = hipStreamEndCapture(c->cap_stream, &graph);
+    if (ls != BLT_OK || ee != hipSuccess) {
+      if (graph) (void)hipGraphDestroy(graph);
+      return ls != BLT_OK ? ls : hip_fail(c, ee, "hipStreamEndCapture");
+    }
+    const hipError_t ie = hipGraphInstantiate(&ge.exec, graph, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(graph);
+    if (ie != hipSuccess) {
+      ge.exec = nullptr;
+      return hip_fail(c, ie, "hipGraphInstantiate");
+    }
+  }
+  HIP_TRY(c, hipGraphLaunch(ge.exec, c->stream));
   return BLT_OK;
 }
 
@@ -222,7 +293,7 @@ blt_status blt_state_size(const blt_config *cfg, size_t *kv_bytes, size_t *cross
   std::string why;
   if (!valid_cfg(cfg, &why) || !kv_bytes || !cross_bytes) return BLT_EINVAL;
   const size_t e = esize(*cfg);
-  *kv_bytes = (size_t)cfg->max_batch * cfg->n_layers * 2 * cfg->max_ctx * cfg->d_model * e;
+  *kv_bytes = (size_t)cfg->max_batch * cfg->n_layers * 2 * kv_rows(cfg->max_ctx) * cfg->d_model * e;
   *cross_bytes = (size_t)cfg->max_batch * cfg->max_latents * cfg->n_layers * cfg->d_model * sizeof(float);
   return BLT_OK;
 }
@@ -265,17 +336,19 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(dalloc(&c->rinv, (size_t)R));
   chk(dalloc(&c->conf_ws, (size_t)R));
   chk(dalloc(&c->argmax_ws, (size_t)R));
-  chk(dalloc(&c->counters, (size_t)cfg->max_batch * H));
-  if (he == hipSuccess) chk(hipMemset(c->counters, 0, (size_t)cfg->max_batch * H * sizeof(int)));
   chk(hipMalloc(&c->xa, std::max<size_t>(1, (size_t)R * wide * e)));
   chk(hipMalloc(&c->xb, std::max<size_t>(1, (size_t)R * std::max(d, cfg->d_global) * e)));
-  chk(dalloc(&c->rows_d, (size_t)R));
-  chk(dalloc(&c->seqs_d, (size_t)cfg->max_batch));
-  chk(dalloc(&c->offs_d, (size_t)R));
   chk(dalloc(&c->rope_tab, (size_t)cfg->max_ctx * (dh / 2)));
-  c->seq_off = ((size_t)R * sizeof(RowDesc) + 255) & ~(size_t)255;
-  c->off_off = (c->seq_off + (size_t)cfg->max_batch * sizeof(SeqDesc) + 255) & ~(size_t)255;
+  chk(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
+  c->row_off = ((size_t)cfg->max_batch * sizeof(SeqDesc) + 255) & ~(size_t)255;
+  c->off_off = (c->row_off + (size_t)R * sizeof(RowDesc) + 255) & ~(size_t)255;
   const size_t stage = c->off_off + (size_t)R * sizeof(int64_t);
+  chk(hipMalloc(&c->desc_d, stage));
+  if (he == hipSuccess) {
+    c->seqs_d = (SeqDesc *)c->desc_d;
+    c->rows_d = (RowDesc *)((char *)c->desc_d + c->row_off);
+    c->offs_d = (int64_t *)((char *)c->desc_d + c->off_off);
+  }
   for (int i = 0; i < kRing && he == hipSuccess; ++i) {
     chk(hipHostMalloc(&c->ring[i].host, stage, hipHostMallocDefault));
     chk(hipEventCreateWithFlags(&c->ring[i].ev, hipEventDisableTiming));
@@ -301,8 +374,10 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
 blt_status blt_destroy(blt_ctx *c) {
   if (!c) return BLT_EINVAL;
   (void)hipStreamSynchronize(c->stream);
-  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws, c->counters,
-                  c->xa, c->xb, c->rows_d, c->seqs_d, c->offs_d, c->rope_tab};
+  drop_graphs(c);
+  if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
+  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws,
+                  c->xa, c->xb, c->desc_d, c->rope_tab};
   for (void *p : bufs)
     if (p) (void)hipFree(p);
   for (int i = 0; i < kRing; ++i) {
@@ -335,7 +410,7 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
       offs[i] = ((int64_t)slot[i0 + i] * seq_stride + idx[i0 + i]) * g.d_global;        // source row
       offs[m + i] = (((int64_t)slot[i0 + i] * g.max_latents + idx[i0 + i]) * L) * d;     // cross row
     }
-    // Both offset lists ride in the offsets buffer (2*m <= 2*max_rows entries).
+    // source offsets for W_lat, then (restaged) destination offsets
     std::vector<int64_t> src(offs.begin(), offs.begin() + m), dst(offs.begin() + m, offs.end());
     std::vector<RowDesc> no_rows;
     std::vector<SeqDesc> no_seqs;
@@ -502,6 +577,13 @@ blt_status blt_profile_enable(blt_ctx *c, int32_t family) {
   blt_status bs = prof_collect(c);
   c->prof_family = family;
   return bs;
+}
+
+blt_status blt_graphs_enable(blt_ctx *c, int32_t enable) {
+  if (!c) return BLT_EINVAL;
+  if (!enable) drop_graphs(c);
+  c->graphs = enable != 0;
+  return BLT_OK;
 }
 
 blt_status blt_profile_read(blt_ctx *c, uint64_t *launches, double *total_ms, double *bytes,

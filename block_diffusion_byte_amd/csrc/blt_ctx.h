@@ -1,7 +1,10 @@
 // The library-owned context behind the opaque blt_ctx handle.
 #pragma once
 
+#include <string.h>
+
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "blt_internal.h"
@@ -22,6 +25,28 @@ struct StageSlot {
   bool pending = false;
 };
 
+// Everything the kernel sequence of a decoder pass depends on besides the
+// staged descriptors: passes with equal keys replay one HIP graph.
+struct PassKey {
+  int R, S, grid_chunks, unmask, one_step;
+  uint32_t alpha_bits;
+  const void *kv, *cross, *block_tok, *tokens_dev, *masked_left, *argmax_out, *conf_out,
+      *logits_out;
+  bool operator==(const PassKey &o) const { return memcmp(this, &o, sizeof(PassKey)) == 0; }
+};
+struct PassKeyHash {
+  size_t operator()(const PassKey &k) const {
+    const unsigned char *p = (const unsigned char *)&k;
+    uint64_t h = 1469598103934665603ull;  // FNV-1a over the key bytes
+    for (size_t i = 0; i < sizeof(PassKey); ++i) h = (h ^ p[i]) * 1099511628211ull;
+    return (size_t)h;
+  }
+};
+struct GraphEntry {
+  hipGraphExec_t exec = nullptr;  // instantiated on the second sighting of a key
+};
+constexpr size_t kMaxGraphs = 256;
+
 }  // namespace blt
 
 struct blt_ctx {
@@ -39,18 +64,22 @@ struct blt_ctx {
   float *rinv = nullptr;      // [R]
   float *conf_ws = nullptr;   // [R]
   int32_t *argmax_ws = nullptr;
-  int *counters = nullptr;    // attention merge counters [max_batch][H], kept at zero
   void *xa = nullptr;         // GEMM activations [R][max(d, F)]
   void *xb = nullptr;         // GEMM activations [R][max(d, d_global)]
-  blt::RowDesc *rows_d = nullptr;
+  void *desc_d = nullptr;      // per-pass descriptors: sequences, rows, row offsets
   blt::SeqDesc *seqs_d = nullptr;
+  blt::RowDesc *rows_d = nullptr;
   int64_t *offs_d = nullptr;
   float2 *rope_tab = nullptr; // (cos, sin) [max_ctx][dh/2]
   int max_chunks = 0;
   blt::StageSlot ring[blt::kRing];
   int ring_next = 0;
-  size_t seq_off = 0, off_off = 0;
+  size_t row_off = 0, off_off = 0;  // byte offsets in desc_d and the staging slots
   std::string err;
+  // replay of decoder passes from cached HIP graphs (captured on cap_stream)
+  bool graphs = false;
+  hipStream_t cap_stream = nullptr;
+  std::unordered_map<blt::PassKey, blt::GraphEntry, blt::PassKeyHash> graph_cache;
   // profiling: family being timed, event pool, pending and accumulated figures
   int prof_family = 0;
   std::vector<blt::ProfRec> prof_pool;

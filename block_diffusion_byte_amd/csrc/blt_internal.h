@@ -79,14 +79,18 @@ struct GemmArgs {
   const float2 *rope_tab;
   float *q_out;
   void *kv;
-  int n_heads, d_head, max_ctx, layer;
+  int n_heads, d_head, max_ctx, layer;   // max_ctx: cache rows, kv_rows(cfg.max_ctx)
 };
+
+// Cache rows per sequence and head: max_ctx rounded up to whole attention
+// chunks, so a chunk's loads never leave its plane.
+inline int kv_rows(int max_ctx) { return (max_ctx + kAttnChunk - 1) / kAttnChunk * kAttnChunk; }
 
 // Does a pass of R rows take the GEMV path (else the MFMA GEMM)?
 inline bool gemv_path(bool bf16, int R) { return !bf16 || R < kGemvRows; }
 
 struct KVGeom {
-  int n_layers, n_heads, d_head, max_ctx;
+  int n_layers, n_heads, d_head, max_ctx;  // max_ctx: cache rows, kv_rows(cfg.max_ctx)
 };
 
 // Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.

@@ -78,33 +78,79 @@ template <> __device__ __forceinline__ float dot_chunk<false>(uint4 w, uint4 x, 
   return acc;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+// Cross-lane exchange inside 16-lane rows through DPP operand modifiers (a
+// VALU operand, no LDS round trip).  Applied in this order, the four moves
+// pair lane i with i^1, i^2, then the other quad and the other half of its
+// row: after step k every lane of an aligned group of 2^k lanes holds the
+// group's reduction, bit-identical across the group (+ and max commute).
+constexpr int kDppXor1 = 0xB1;         // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;         // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;  // lane i <- lane 7-i of its 8 lanes
+constexpr int kDppMirror = 0x140;      // lane i <- lane 15-i of its 16 lanes
+
+template <int CTRL> __device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL> __device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, true);
+}
+
+// Sum / max over aligned groups of G lanes (G = 1, 2, 4, 8, 16).
+template <int G> __device__ __forceinline__ float group_sum(float v) {
+  if constexpr (G >= 2) v += dpp_f<kDppXor1>(v);
+  if constexpr (G >= 4) v += dpp_f<kDppXor2>(v);
+  if constexpr (G >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f<kDppMirror>(v);
   return v;
 }
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+template <int G> __device__ __forceinline__ float group_max(float v) {
+  if constexpr (G >= 2) v = fmaxf(v, dpp_f<kDppXor1>(v));
+  if constexpr (G >= 4) v = fmaxf(v, dpp_f<kDppXor2>(v));
+  if constexpr (G >= 8) v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  if constexpr (G >= 16) v = fmaxf(v, dpp_f<kDppMirror>(v));
   return v;
 }
 
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Whole-wave sum / max, wave-uniform result: 16-lane rows, then the four
+// row totals in a fixed order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = group_sum<16>(v);
+  return (lane_f(v, 0) + lane_f(v, 16)) + (lane_f(v, 32) + lane_f(v, 48));
+}
+__device__ __forceinline__ float wave_max(float v) {
+  v = group_max<16>(v);
+  return fmaxf(fmaxf(lane_f(v, 0), lane_f(v, 16)), fmaxf(lane_f(v, 32), lane_f(v, 48)));
+}
+
+// The residual-update operands of output o of row r: the current residual
+// and (with a cross table) the next layer's cross-attention contribution.
+struct ResidEpi {
+  float h, c;
+};
+
+__device__ __forceinline__ ResidEpi resid_operands(const GemmArgs &a, int r, int o) {
+  ResidEpi e{a.resid[(int64_t)r * a.ldo + o], 0.f};
+  if (a.cross) {
+    const RowDesc rd = a.rows[r];
+    e.c = a.cross[(((int64_t)rd.slot * a.max_lat + rd.lat) * a.n_layers + a.cross_layer) * a.d + o];
+  }
+  return e;
+}
+
 template <bool BF>
-__device__ __forceinline__ void epilogue(const GemmArgs &a, int r, int o, float y) {
+__device__ __forceinline__ void epilogue(const GemmArgs &a, int r, int o, float y, const ResidEpi &re) {
   using T = typename Act<BF>::T;
   switch (a.ep) {
     case EP_STORE_F32:
       a.out_f32[(int64_t)r * a.ldo + o] = y;
       break;
-    case EP_RESID: {
-      float c = 0.f;
-      if (a.cross) {
-        const RowDesc rd = a.rows[r];
-        c = a.cross[(((int64_t)rd.slot * a.max_lat + rd.lat) * a.n_layers + a.cross_layer) * a.d + o];
-      }
-      a.resid[(int64_t)r * a.ldo + o] += y + c;
+    case EP_RESID:
+      a.resid[(int64_t)r * a.ldo + o] = re.h + (y + (a.cross ? re.c : 0.f));
       break;
-    }
     case EP_SILU_ACT:
       ((T *)a.out_act)[(int64_t)r * a.ldo + o] = from_f<T>(y / (1.f + expf(-y)));
       break;
@@ -140,31 +186,47 @@ __device__ __forceinline__ int qkv_rope_row(const GemmArgs &a, int i) {
   return sec * a.d + hh * a.d_head + j + which * half;
 }
 
+// Position, slot and rotation (cos, sin) of one output pair of the fused
+// QKV projection: what its epilogue needs besides the two dot products.
+struct QkvEpi {
+  int pos, slot;
+  float2 cs;
+};
+
+// Column j (within its head half) of the pair whose first output is i0.
+__device__ __forceinline__ int qkv_pair_j(const GemmArgs &a, int i0) {
+  const int half = a.d_head >> 1, p = i0 >> 1, hd = a.d >> 1;
+  const int pp = p - (p / hd) * hd;
+  return pp - (pp / half) * half;
+}
+
 // Epilogue of the fused QKV projection: RoPE on q and k of one (j, j+dh/2)
 // pair at the row's position, q kept in f32, k and v written to the cache.
 template <bool BF>
-__device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0, float y0, float y1) {
+__device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0, float y0, float y1,
+                                               const QkvEpi &e) {
   using T = typename Act<BF>::T;
-  const RowDesc rd = a.rows[r];
   const int half = a.d_head >> 1, p = i0 >> 1;
   const int hd = a.d >> 1, sec = p / hd, pp = p - sec * hd, hh = pp / half, j = pp - hh * half;
   const int lo = hh * a.d_head + j;
-  const float2 cs = a.rope_tab[(int64_t)rd.pos * half + j];
+  const float2 cs = e.cs;
   if (sec == 0) {
     a.q_out[(int64_t)r * a.d + lo] = y0 * cs.x - y1 * cs.y;
     a.q_out[(int64_t)r * a.d + lo + half] = y1 * cs.x + y0 * cs.y;
     return;
   }
   const int64_t plane = (int64_t)a.max_ctx * a.d_head;
-  int64_t base = ((((int64_t)rd.slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh) * plane +
-                 (int64_t)rd.pos * a.d_head + j;
+  const int64_t head = (((int64_t)e.slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
   T *kv = (T *)a.kv;
   if (sec == 1) {
+    const int64_t base = head * plane + (int64_t)e.pos * a.d_head + j;
     kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
     kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
-    kv[base] = from_f<T>(y0);
-    kv[base + half] = from_f<T>(y1);
+    // V is stored transposed: [dim][position]
+    const int64_t vb = head * plane + (int64_t)j * a.max_ctx + e.pos;
+    kv[vb] = from_f<T>(y0);
+    kv[vb + (int64_t)half * a.max_ctx] = from_f<T>(y1);
   }
 }
 
@@ -234,21 +296,51 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
   const int ic = min(i, a.N - 1);
   const int orow = a.qkv_rope ? qkv_rope_row(a, ic) : ic;
   const uint4 *wrow = (const uint4 *)a.W + (int64_t)orow * KC + w * Q + s;
+  static_assert(RB * RPW <= 256, "one epilogue item per thread and row block");
   uint4 gv[CPT];
   StageRaw<BF, PRO> raw[RB][CPT];
   uint4 wv[NC];
   int rb = 0, nr = min(RB, a.R);
-  // Activation loads first (small, cache-resident), then the weight slice:
-  // waiting for the activations leaves every weight load in flight.
+  // Activation loads first (small, cache-resident), then the epilogue
+  // operands of this thread's output item, then the weight slice: waiting
+  // for the activations leaves every weight load in flight.  Loads that
+  // need a loaded row descriptor go out after the weights, so that the dot
+  // products never wait for them.
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
     const int c = min(tid + 256 * k, KC - 1);
     if constexpr (PRO == PRO_NORM) gv[k] = *(const uint4 *)((const typename Act<BF>::T *)a.gain + c * EPC);
 #pragma unroll
-    for (int r = 0; r < RB; ++r) stage_load<BF, PRO>(a, min(r, nr - 1), c, raw[r][k]);
+    for (int r = 0; r < RB; ++r)
+      if (r < 4 || r < nr) stage_load<BF, PRO>(a, min(r, nr - 1), c, raw[r][k]);  // uniform skip
   }
+  // epilogue item of this thread: (row er, output pair ep0) for the fused
+  // QKV projection, (row er, output eo) otherwise; clamped so loads are safe
+  const int er = a.qkv_rope ? tid / (RPW / 2) : tid / RPW;
+  const int erc = min(er, nr - 1);
+  const int ep0 = blockIdx.x * RPW + 2 * (tid - er * (RPW / 2));
+  const int eo = blockIdx.x * RPW + (tid - er * RPW), eoc = min(eo, a.N - 1);
+  // Unconditional loads through uniform pointer selects (the weights stand
+  // in for unused operands), so no branch forces an early wait.
+  const bool need_row = a.qkv_rope || (a.ep == EP_RESID && a.cross);
+  const int4 *rowp = need_row ? (const int4 *)(a.rows + erc) : (const int4 *)a.W;
+  const int4 rlo = rowp[0], rhi = rowp[1];        // slot pos tok blk | lat kend oidx pad
+  const float *resp = a.ep == EP_RESID ? a.resid + (int64_t)erc * a.ldo + eoc : (const float *)a.W;
+  ResidEpi re{*resp, 0.f};
 #pragma unroll
   for (int u = 0; u < NC; ++u) wv[u] = wrow[u * G];
+  // keep every use of the loaded descriptors below the weight loads
+  __builtin_amdgcn_sched_barrier(0);
+  QkvEpi qe{rlo.y, rlo.x, make_float2(1.f, 0.f)};
+  {
+    const int64_t ci = (((int64_t)rlo.x * a.max_lat + rhi.x) * a.n_layers + a.cross_layer) * a.d + eoc;
+    const int64_t ti = (int64_t)rlo.y * (a.d_head >> 1) + qkv_pair_j(a, min(ep0, a.N - 2));
+    const float2 *csp = a.qkv_rope ? a.rope_tab + ti : (const float2 *)a.W;
+    const float *crp = a.ep == EP_RESID && a.cross ? a.cross + ci : (const float *)a.W;
+    // consumed only by the epilogue of the matching kind
+    qe.cs = *csp;
+    re.c = *crp;
+  }
 
   while (true) {
     // Thread tid stages chunks tid, tid+256, ... of every row: the same
@@ -257,6 +349,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
 #pragma unroll
     for (int r = 0; r < RB; ++r) {
       ssr[r] = 0.f;
+      if (r >= 4 && r >= nr) continue;       // uniform: rows past the pass
 #pragma unroll
       for (int k = 0; k < CPT; ++k) {
         float ssk = 0.f;                     // squares of this chunk, in element order
@@ -269,45 +362,62 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
     if constexpr (PRO == PRO_NORM) {
 #pragma unroll
       for (int r = 0; r < RB; ++r) {
+        if (r >= 4 && r >= nr) continue;
         const float v = wave_sum(ssr[r]);
         if (lane == 0) ssq[w][r] = v;
       }
     }
     __syncthreads();
-    // one row at a time keeps only NC staged chunks live next to the weights
-    for (int r = 0; r < nr; ++r) {
-      float v = 0.f;
+    // RQ rows at a time: independent accumulation chains and reductions
+    // overlap, while only RQ*NC staged chunks are live next to the weights
+    // (rows past the last are clamped re-reads whose results are dropped)
+    constexpr int RQ = NC <= 4 ? 4 : (NC <= 8 ? 2 : 1);
+    for (int r0 = 0; r0 < nr; r0 += RQ) {
+      float v[RQ];
 #pragma unroll
-      for (int u = 0; u < NC; ++u) v = dot_chunk<BF>(wv[u], xs[r * KC + w * Q + s + u * G], v);
+      for (int j = 0; j < RQ; ++j) v[j] = 0.f;
 #pragma unroll
-      for (int m = 1; m < G; m <<= 1) v += __shfl_xor(v, m, 64);
-      if (s == 0) red[w][r][g] = v;
+      for (int u = 0; u < NC; ++u)
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+          v[j] = dot_chunk<BF>(wv[u], xs[min(r0 + j, nr - 1) * KC + w * Q + s + u * G], v[j]);
+#pragma unroll
+      for (int j = 0; j < RQ; ++j) v[j] = group_sum<G>(v[j]);
+      if (s == 0) {
+#pragma unroll
+        for (int j = 0; j < RQ; ++j)
+          if (r0 + j < nr) red[w][r0 + j][g] = v[j];
+      }
     }
     __syncthreads();
+    // one epilogue item per thread; the first row block uses the operands
+    // loaded at entry, later blocks load their own
     if (a.qkv_rope) {
-      for (int t = tid; t < nr * (RPW / 2); t += 256) {
-        const int r = t / (RPW / 2), gg = 2 * (t - r * (RPW / 2));
-        const int i0 = blockIdx.x * RPW + gg;
-        if (i0 + 1 < a.N) {
-          float y0 = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
-          float y1 = ((red[0][r][gg + 1] + red[1][r][gg + 1]) + red[2][r][gg + 1]) + red[3][r][gg + 1];
-          if constexpr (PRO == PRO_NORM) {
-            const float rinv = 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
-            y0 *= rinv;
-            y1 *= rinv;
-          }
-          qkv_rope_store<BF>(a, rb + r, i0, y0, y1);
+      const int r = er, gg = 2 * (tid - er * (RPW / 2)), i0 = ep0;
+      if (r < nr && i0 + 1 < a.N) {
+        float y0 = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
+        float y1 = ((red[0][r][gg + 1] + red[1][r][gg + 1]) + red[2][r][gg + 1]) + red[3][r][gg + 1];
+        if constexpr (PRO == PRO_NORM) {
+          const float rinv = 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
+          y0 *= rinv;
+          y1 *= rinv;
         }
+        if (rb > 0) {
+          const RowDesc rd = a.rows[rb + r];
+          qe.pos = rd.pos;
+          qe.slot = rd.slot;
+          qe.cs = a.rope_tab[(int64_t)rd.pos * (a.d_head >> 1) + qkv_pair_j(a, i0)];
+        }
+        qkv_rope_store<BF>(a, rb + r, i0, y0, y1, qe);
       }
     } else {
-      for (int t = tid; t < nr * RPW; t += 256) {
-        const int r = t / RPW, gg = t - r * RPW, oo = blockIdx.x * RPW + gg;
-        if (oo < a.N) {
-          float y = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
-          if constexpr (PRO == PRO_NORM)
-            y *= 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
-          epilogue<BF>(a, rb + r, oo, y);
-        }
+      const int r = er, gg = tid - er * RPW, oo = eo;
+      if (r < nr && oo < a.N) {
+        float y = ((red[0][r][gg] + red[1][r][gg]) + red[2][r][gg]) + red[3][r][gg];
+        if constexpr (PRO == PRO_NORM)
+          y *= 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)K + a.eps);
+        if (rb > 0 && a.ep == EP_RESID) re = resid_operands(a, rb + r, oo);
+        epilogue<BF>(a, rb + r, oo, y, re);
       }
     }
     rb += RB;
@@ -318,7 +428,8 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
     for (int k = 0; k < CPT; ++k) {
       const int c = min(tid + 256 * k, KC - 1);
 #pragma unroll
-      for (int r = 0; r < RB; ++r) stage_load<BF, PRO>(a, rb + min(r, nr - 1), c, raw[r][k]);
+      for (int r = 0; r < RB; ++r)
+        if (r < 4 || r < nr) stage_load<BF, PRO>(a, rb + min(r, nr - 1), c, raw[r][k]);
     }
   }
 }
@@ -384,7 +495,9 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wr + i * 16 + 4 * (l >> 4) + v;
         const int n = n0 + wc + j * 16 + (l & 15);
-        if (m < a.R && n < a.N) epilogue<true>(a, m, n, acc[i][j][v]);
+        if (m < a.R && n < a.N)
+          epilogue<true>(a, m, n, acc[i][j][v],
+                         a.ep == EP_RESID ? resid_operands(a, m, n) : ResidEpi{0.f, 0.f});
       }
 }
 
@@ -451,63 +564,248 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
     const float k1 = src[d + lo], k2 = src[d + hi];
     const int64_t kb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + hh) * plane +
                        (int64_t)rd.pos * dh;
-    const int64_t vb = kb + (int64_t)g.n_heads * plane;
+    // V transposed: [dim][position] of the head's V plane
+    const int64_t vb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 1) * g.n_heads + hh) * plane + rd.pos;
     kv[kb + j] = from_f<T>(k1 * cs.x - k2 * cs.y);
     kv[kb + j + half] = from_f<T>(k2 * cs.x + k1 * cs.y);
-    kv[vb + j] = from_f<T>(src[2 * d + lo]);
-    kv[vb + j + half] = from_f<T>(src[2 * d + hi]);
+    kv[vb + (int64_t)j * g.max_ctx] = from_f<T>(src[2 * d + lo]);
+    kv[vb + (int64_t)(j + half) * g.max_ctx] = from_f<T>(src[2 * d + hi]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Split-K attention with the merge fused into the last workgroup.
+// Split-K attention partials.
+//
+// Cache layout per (sequence, layer, head): K as [position][d_head] and V
+// transposed, [d_head][max_ctx], so that both products below read their
+// operands straight from HBM with 8- or 16-byte loads.
 //
 // Workgroup (chunk c, head h, sequence b) owns keys [c*128, c*128+128) of
 // that sequence, for every row of the sequence in the pass; row r reads keys
-// [0, kend_r).  The K and V rows of the chunk (contiguous in the head-major
-// cache) are fetched with fully coalesced 16-byte loads and staged in LDS.
-// Scores: two threads per key, each owning half of the head dims, combined
-// by one xor-shuffle.  Softmax statistics of the chunk are (max, sum); P.V is
-// summed by (dim, key-partition) threads.  Each chunk writes (o[dh], m, l)
-// per row; the last workgroup of the (sequence, head) -- found with a device
-// counter -- merges the chunks in chunk order and writes the attention
-// output as a GEMM activation.
+// [0, kend_r).  For each row it writes the chunk's unnormalised output
+// o = sum_k exp(s_k - m) v_k with m = max_k s_k and l = sum_k exp(s_k - m).
+// Keys past a row's kend contribute exact zeros, so a row's partials depend
+// only on its own query and keys (never on the other rows of the pass).
 constexpr int kCK = kAttnChunk;
 
-template <bool BF, int DH>
-__global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, KVGeom g, int layer,
-                                              const SeqDesc *seqs, const RowDesc *rows, float *part,
-                                              int max_chunks) {
-  using T = typename Act<BF>::T;
+// bfloat16: each wave takes 32 keys of the chunk and up to 16 rows at a time.
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16:
+// a lane then holds 4 keys of each of the two 16-key tiles for one row,
+// which is exactly the A-operand layout P[row][k-slot] of the P.V product
+// (k-slot 8q+i of lane group q is key 4q+i of tile 0 for i < 4 and key
+// 4q+i-4 of tile 1 otherwise; the V operand is gathered in the same slot
+// order).  P is split into bf16 hi and lo parts, two MFMAs per output tile,
+// so the probabilities keep about 16 significant bits.  The four waves'
+// (o, m, l) are combined through LDS in wave order.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
+                                                   int layer, const SeqDesc *seqs,
+                                                   const RowDesc *rows, float *part,
+                                                   int max_chunks) {
+  constexpr int KS = DH / 32;                 // k-steps of the score product
+  constexpr int DT = DH / 16;                 // 16-dim output tiles of P.V
+  constexpr int KW = 32;                      // keys per wave
+  constexpr int OST = DH + 4;                 // LDS row stride of the wave outputs
+  __shared__ float ow[4][16 * OST];
+  __shared__ float mw[4][16], lw[4][16];
+  __shared__ int kends[16];
+  const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const SeqDesc sd = seqs[b];
+  const int key0 = c * kCK;
+  if (key0 >= sd.kmax) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+  const int d = g.n_heads * DH;
+  const int64_t plane = (int64_t)g.max_ctx * DH;
+  const uint16_t *Kp =
+      (const uint16_t *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
+  const uint16_t *Vt = Kp + (int64_t)g.n_heads * plane;
+  const int kw0 = key0 + w * KW;
+  const int klast = sd.kmax - 1;              // every cache row below kmax holds data
+
+  // q of the first row group, then K (A operand: key kw0+16kt+lr, dims
+  // 32ks+8lq..+8) and V (B operand: dim 16dt+lr, keys kw0+4lq..+4 and
+  // kw0+16+4lq..+4); key indices are clamped into the written cache rows
+  int nr = min(16, sd.nrows);
+  float4 qf[KS][2];
+  {
+    const float *qr = q + (int64_t)(sd.row0 + min(lr, nr - 1)) * d + h * DH + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks][0] = *(const float4 *)(qr + 32 * ks);
+      qf[ks][1] = *(const float4 *)(qr + 32 * ks + 4);
+    }
+  }
+  int my_kend = rows[sd.row0 + min(lr, nr - 1)].kend;
+  bf16x8_t ka[2][KS];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const uint16_t *kr = Kp + (int64_t)min(kw0 + 16 * kt + lr, klast) * DH + 8 * lq;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *(const bf16x8_t *)(kr + 32 * ks);
+  }
+  const int ka0 = kw0 + 4 * lq, ka1 = kw0 + 16 + 4 * lq;   // first keys of the two V groups
+  const int va0 = min(ka0, klast & ~3), va1 = min(ka1, klast & ~3);
+  uint2 vg[DT][2];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint16_t *vr = Vt + (int64_t)(16 * dt + lr) * g.max_ctx;
+    vg[dt][0] = *(const uint2 *)(vr + va0);
+    vg[dt][1] = *(const uint2 *)(vr + va1);
+  }
+  // V operand in slot order; keys at or past kmax (never written) become 0
+  bf16x8_t vb[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    const uint32_t raw[4] = {vg[dt][0].x, vg[dt][0].y, vg[dt][1].x, vg[dt][1].y};
+    uint32_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = (i < 2 ? ka0 : ka1) + 2 * (i & 1);
+      const uint32_t lo = k < sd.kmax ? (raw[i] & 0xffffu) : 0u;
+      const uint32_t hi = k + 1 < sd.kmax ? (raw[i] & 0xffff0000u) : 0u;
+      o[i] = lo | hi;
+    }
+    vb[dt] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+  const float scale = 1.f / sqrtf((float)DH);
+
+  for (int rg = 0;;) {
+    if (t < 16) kends[t] = rows[sd.row0 + rg + min(t, nr - 1)].kend;
+    bf16x8_t qb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8_t v;
+      v[0] = (__bf16)qf[ks][0].x; v[1] = (__bf16)qf[ks][0].y;
+      v[2] = (__bf16)qf[ks][0].z; v[3] = (__bf16)qf[ks][0].w;
+      v[4] = (__bf16)qf[ks][1].x; v[5] = (__bf16)qf[ks][1].y;
+      v[6] = (__bf16)qf[ks][1].z; v[7] = (__bf16)qf[ks][1].w;
+      qb[ks] = v;
+    }
+    // S^T tiles: acc[kt][v] = score of key kw0+16kt+4lq+v for row lr
+    f32x4_t acc[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt][ks], qb[ks], acc[kt], 0, 0, 0);
+    }
+    float sv[8];
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int key = (kt ? ka1 : ka0) + v;
+        const float x = key < my_kend ? acc[kt][v] * scale : -INFINITY;
+        sv[kt * 4 + v] = x;
+        m = fmaxf(m, x);
+      }
+    // the four lane groups holding row lr
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f;
+    float ph[8], pl[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float p = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m);
+      l += p;
+      ph[i] = p;
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    bf16x8_t pa_hi, pa_lo;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const __bf16 hb = (__bf16)ph[i];
+      pa_hi[i] = hb;
+      pl[i] = ph[i] - (float)hb;
+      pa_lo[i] = (__bf16)pl[i];
+    }
+    f32x4_t o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[dt], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[dt], o[dt], 0, 0, 0);
+    }
+    // o[dt][v] = output of row 4lq+v, dim 16dt+lr
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) ow[w][(4 * lq + v) * OST + 16 * dt + lr] = o[dt][v];
+    if (lq == 0) {
+      mw[w][lr] = m;
+      lw[w][lr] = l;
+    }
+    __syncthreads();
+    for (int i = t; i < nr * DH; i += 256) {
+      const int r = i / DH, e = i - r * DH;
+      if (kends[r] <= key0) continue;
+      const float m0 = mw[0][r], m1 = mw[1][r], m2 = mw[2][r], m3 = mw[3][r];
+      const float M = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
+      const float f0 = m0 == -INFINITY ? 0.f : expf(m0 - M);
+      const float f1 = m1 == -INFINITY ? 0.f : expf(m1 - M);
+      const float f2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
+      const float f3 = m3 == -INFINITY ? 0.f : expf(m3 - M);
+      const float O = ((f0 * ow[0][r * OST + e] + f1 * ow[1][r * OST + e]) + f2 * ow[2][r * OST + e]) +
+                      f3 * ow[3][r * OST + e];
+      float *dst = part + (((int64_t)(sd.row0 + rg + r) * g.n_heads + h) * max_chunks + c) * (DH + 2);
+      dst[e] = O;
+      if (e == 0) {
+        dst[DH] = M;
+        dst[DH + 1] = ((f0 * lw[0][r] + f1 * lw[1][r]) + f2 * lw[2][r]) + f3 * lw[3][r];
+      }
+    }
+    rg += 16;
+    if (rg >= sd.nrows) break;
+    nr = min(16, sd.nrows - rg);
+    {
+      const float *qr = q + (int64_t)(sd.row0 + rg + min(lr, nr - 1)) * d + h * DH + 8 * lq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        qf[ks][0] = *(const float4 *)(qr + 32 * ks);
+        qf[ks][1] = *(const float4 *)(qr + 32 * ks + 4);
+      }
+    }
+    my_kend = rows[sd.row0 + rg + min(lr, nr - 1)].kend;
+    __syncthreads();                          // LDS of this row group fully read
+  }
+}
+
+// float32: keys staged in LDS, two threads per key for the scores (one DPP
+// exchange), softmax statistics by 16-lane groups, P.V by (dim, key
+// partition) threads with the thread's V column (a row of the transposed V)
+// in registers.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kvp, KVGeom g,
+                                                  int layer, const SeqDesc *seqs,
+                                                  const RowDesc *rows, float *part,
+                                                  int max_chunks) {
   constexpr int RG = 16;                              // rows per row group
-  constexpr int ROWB = DH * (int)sizeof(T);           // bytes of one key row
+  constexpr int ROWB = DH * 4;                        // bytes of one key row
   constexpr int LDB = ROWB + 16;                      // padded LDS row stride (bytes)
   constexpr int CPR = ROWB / 16;                      // 16-byte chunks per key row
   constexpr int HCH = CPR / 2;                        // chunks per half row
   constexpr int NP = 256 / DH, KPP = kCK / NP;        // P.V key partitions
-  constexpr int PER = kCK * CPR / 256;                // K (and V) chunks per thread
+  constexpr int PER = kCK * CPR / 256;                // K chunks per thread
   constexpr int QPT = RG * DH / 256;                  // q elements per thread
   __shared__ __align__(16) char ks[kCK * LDB];        // K rows, then P.V partials
-  __shared__ __align__(16) char vsm[kCK * LDB];       // V rows
-  __shared__ __align__(16) T qs[RG][DH];
+  __shared__ __align__(16) float qs[RG][DH];
   __shared__ __align__(16) float ps[RG][kCK];         // scores, then probabilities
-  __shared__ float redm[RG][4], reds[RG][4];
+  __shared__ float redm[RG], reds[RG];
   __shared__ int kends[RG];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
   const int key0 = c * kCK;
-  const int n_chunks = (sd.kmax + kCK - 1) / kCK;
-  if (c >= n_chunks) return;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  if (key0 >= sd.kmax) return;
+  const int t = threadIdx.x;
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
-  const char *Kb = (const char *)((const T *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane) + (int64_t)key0 * ROWB;
-  const char *Vb = Kb + (int64_t)g.n_heads * plane * (int64_t)sizeof(T);
+  const float *Kp = (const float *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
+  const float *Vt = Kp + (int64_t)g.n_heads * plane;
+  const char *Kb = (const char *)(Kp + (int64_t)key0 * DH);
   const int nkeys = min(kCK, sd.kmax - key0);
 
-  // small loads first (q and kend of the first row group), then the chunk's
-  // K and V rows with fully coalesced 16-byte loads; indices are clamped so
-  // the loads are unconditional
   int nr = min(RG, sd.nrows);
   float qv[QPT];
 #pragma unroll
@@ -516,51 +814,57 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, K
     qv[k] = q[(int64_t)(sd.row0 + min(r, nr - 1)) * d + h * DH + ee];
   }
   const int my_kend = rows[sd.row0 + min(t & (RG - 1), nr - 1)].kend;
-  uint4 kr[PER], vr[PER];
+  uint4 kr[PER];
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
-    const int64_t off = (int64_t)min(key, nkeys - 1) * ROWB + cc * 16;
-    kr[u] = *(const uint4 *)(Kb + off);
-    vr[u] = *(const uint4 *)(Vb + off);
+    kr[u] = *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
   }
+  const int kk = t >> 1, hf = t & 1;                  // score phase: key kk, half hf
+  const int e = t % DH, kp = t / DH;                  // P.V phase: dim e, partition kp
+  // this thread's V column over its key partition: a contiguous run of V^T
+  float vcol[KPP];
+#pragma unroll
+  for (int j = 0; j < KPP; ++j)
+    vcol[j] = Vt[(int64_t)e * g.max_ctx + key0 + min(kp * KPP + j, nkeys - 1)];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;
-    qs[r][ee] = from_f<T>(qv[k]);
+    qs[r][ee] = qv[k];
   }
   if (t < RG) kends[t] = my_kend;
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
     *(uint4 *)(ks + key * LDB + cc * 16) = kr[u];
-    *(uint4 *)(vsm + key * LDB + cc * 16) = vr[u];
   }
   const float scale = 1.f / sqrtf((float)DH);
-  const int kk = t >> 1, hf = t & 1;                  // score phase: key kk, half hf
-  const int e = t % DH, kp = t / DH;                  // P.V phase: dim e, partition kp
   __syncthreads();
-  // this thread's V column over its key partition stays in registers
-  float vcol[KPP];
-#pragma unroll
-  for (int j = 0; j < KPP; ++j) vcol[j] = to_f(*(const T *)(vsm + (kp * KPP + j) * LDB + e * (int)sizeof(T)));
 
   for (int rg = 0;;) {
     uint4 kh[HCH];
 #pragma unroll
     for (int u = 0; u < HCH; ++u) kh[u] = *(const uint4 *)(ks + kk * LDB + (hf * HCH + u) * 16);
-    // scores of every row: two threads per key, one xor-shuffle
-    for (int r = 0; r < nr; ++r) {
-      float acc = 0.f;
+    for (int r0 = 0; r0 < nr; r0 += 4) {
+      float acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] = 0.f;
 #pragma unroll
       for (int u = 0; u < HCH; ++u)
-        acc = dot_chunk<BF>(kh[u], *(const uint4 *)((const char *)&qs[r][0] + (hf * HCH + u) * 16), acc);
-      acc += __shfl_xor(acc, 1, 64);
-      if (hf == 0) ps[r][kk] = (key0 + kk < kends[r]) ? acc * scale : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[j] = dot_chunk<false>(kh[u], *(const uint4 *)((const char *)&qs[min(r0 + j, nr - 1)][0] +
+                                                            (hf * HCH + u) * 16), acc[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = group_sum<2>(acc[j]);
+        const int r = r0 + j;
+        if (hf == 0 && r < nr) ps[r][kk] = (key0 + kk < kends[r]) ? acc[j] * scale : -INFINITY;
+      }
     }
     __syncthreads();
     {
-      // softmax statistics: 16 threads per row, 8 keys each, 16-lane xor trees
+      // softmax statistics: 16 threads per row, 8 keys each
       const int r = t >> 4, sl = t & 15;
       float sv[kCK / 16];
       float m = -INFINITY;
@@ -569,8 +873,7 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, K
         sv[j] = ps[r][sl * (kCK / 16) + j];
         m = fmaxf(m, sv[j]);
       }
-#pragma unroll
-      for (int x = 1; x < 16; x <<= 1) m = fmaxf(m, __shfl_xor(m, x, 64));
+      m = group_max<16>(m);
       float l = 0.f;
 #pragma unroll
       for (int j = 0; j < kCK / 16; ++j) {
@@ -578,26 +881,31 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, K
         l += p;
         if (r < nr) ps[r][sl * (kCK / 16) + j] = p;
       }
-#pragma unroll
-      for (int x = 1; x < 16; x <<= 1) l += __shfl_xor(l, x, 64);
+      l = group_sum<16>(l);
       if (sl == 0) {
-        redm[r][0] = m;
-        reds[r][0] = l;
+        redm[r] = m;
+        reds[r] = l;
       }
     }
     __syncthreads();                                  // K rows are free: reuse for partials
     float *op = (float *)ks;                          // [NP][RG][DH]
-    for (int r = 0; r < nr; ++r) {
-      float o = 0.f;
+    for (int r0 = 0; r0 < nr; r0 += 4) {
+      float o[4];
 #pragma unroll
-      for (int j = 0; j < KPP; j += 4) {
-        const float4 p4 = *(const float4 *)&ps[r][kp * KPP + j];
-        o = fmaf(p4.x, vcol[j], o);
-        o = fmaf(p4.y, vcol[j + 1], o);
-        o = fmaf(p4.z, vcol[j + 2], o);
-        o = fmaf(p4.w, vcol[j + 3], o);
-      }
-      op[(kp * RG + r) * DH + e] = o;
+      for (int i = 0; i < 4; ++i) o[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < KPP; j += 4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float4 p4 = *(const float4 *)&ps[min(r0 + i, RG - 1)][kp * KPP + j];
+          o[i] = fmaf(p4.x, vcol[j], o[i]);
+          o[i] = fmaf(p4.y, vcol[j + 1], o[i]);
+          o[i] = fmaf(p4.z, vcol[j + 2], o[i]);
+          o[i] = fmaf(p4.w, vcol[j + 3], o[i]);
+        }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (r0 + i < nr) op[(kp * RG + r0 + i) * DH + e] = o[i];
     }
     __syncthreads();
     for (int i = t; i < nr * DH; i += 256) {
@@ -610,34 +918,29 @@ __global__ __launch_bounds__(256) void k_attn(const float *q, const void *kvp, K
       float *dst = part + (((int64_t)row * g.n_heads + h) * max_chunks + c) * (DH + 2);
       dst[ee] = acc;
       if (ee == 0) {
-        dst[DH] = redm[r][0];
-        dst[DH + 1] = reds[r][0];
+        dst[DH] = redm[r];
+        dst[DH + 1] = reds[r];
       }
     }
     rg += RG;
     if (rg >= sd.nrows) break;
-    // next row group: its q rows and kends; the K rows come back from registers
+    // next row group: its q rows and kends; the K rows come back from global
     __syncthreads();
     nr = min(RG, sd.nrows - rg);
 #pragma unroll
     for (int k = 0; k < QPT; ++k) {
       const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;
-      qs[r][ee] = from_f<T>(q[(int64_t)(sd.row0 + rg + min(r, nr - 1)) * d + h * DH + ee]);
+      qs[r][ee] = q[(int64_t)(sd.row0 + rg + min(r, nr - 1)) * d + h * DH + ee];
     }
     if (t < RG) kends[t] = rows[sd.row0 + rg + min(t, nr - 1)].kend;
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
-      *(uint4 *)(ks + key * LDB + cc * 16) =
-          *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
+      *(uint4 *)(ks + key * LDB + cc * 16) = *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
     }
     __syncthreads();
   }
-
 }
-
-
-
 
 // Merge of the chunk partials of (row, head) in chunk order, 32 chunks at a
 // time with a running max; the partial of chunk c sits at [row][h][e][c], so
@@ -694,11 +997,27 @@ __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDes
     const float v = z[j];
     if (v > best) { best = v; bi = j; }
   }
+  // (max, lowest index) over each 16-lane row by DPP, then over the rows
+#define BLT_ARGMAX_STEP(ctrl)                                            \
+  {                                                                     \
+    const float ob = dpp_f<ctrl>(best);                                 \
+    const int oi = dpp_i<ctrl>(bi);                                     \
+    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }   \
+  }
+  BLT_ARGMAX_STEP(kDppXor1) BLT_ARGMAX_STEP(kDppXor2)
+  BLT_ARGMAX_STEP(kDppHalfMirror) BLT_ARGMAX_STEP(kDppMirror)
+#undef BLT_ARGMAX_STEP
+  {
+    float bv = lane_f(best, 0);
+    int bx = __builtin_amdgcn_readlane(bi, 0);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const float ob = __shfl_xor(best, m, 64);
-    const int oi = __shfl_xor(bi, m, 64);
-    if (ob > best || (ob == best && oi < bi)) { best = ob; bi = oi; }
+    for (int q = 16; q < 64; q += 16) {
+      const float ob = lane_f(best, q);
+      const int oi = __builtin_amdgcn_readlane(bi, q);
+      if (ob > bv || (ob == bv && oi < bx)) { bv = ob; bx = oi; }
+    }
+    best = bv;
+    bi = bx;
   }
   float s = 0.f;
 #pragma unroll
@@ -789,13 +1108,18 @@ template <bool BF> int gemv_lanes(const GemmArgs &a) {
 
 template <bool BF, int G, int NC>
 hipError_t gemv_rows(const GemmArgs &a, hipStream_t s) {
-  // rows per block: 4 for up to 4 rows, else blocks of 8
+  // rows per block: 4, 8 or 16, the smallest that holds the pass (more rows
+  // loop over blocks of 16); narrow-K matrices only, so the 16-row staging
+  // fits the register budget
+  constexpr bool wide16 = NC <= 8;
   if (a.pro == PRO_NORM) {
     if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_NORM>(a, s);
-    return gemv_launch<BF, G, NC, 8, PRO_NORM>(a, s);
+    if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_NORM>(a, s);
+    return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_NORM>(a, s);
   }
   if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_PLAIN>(a, s);
-  return gemv_launch<BF, G, NC, 8, PRO_PLAIN>(a, s);
+  if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_PLAIN>(a, s);
+  return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_PLAIN>(a, s);
 }
 
 template <bool BF>
@@ -870,13 +1194,22 @@ template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
                         int n_seq, int grid_chunks, int max_chunks, const RowDesc *rows, int R,
                         float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
-  if (ev0) {
-    // events stamped by the dispatch itself at the kernel's start and end
-    hipExtLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s,
-                          ev0, ev1, 0, q, kv, g, layer, seqs, rows, part, max_chunks);
+  const dim3 grid(grid_chunks, g.n_heads, n_seq);
+  // with events: stamped by the dispatch itself at the kernel's start and end
+  if constexpr (BF) {
+    if (ev0)
+      hipExtLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
+                            seqs, rows, part, max_chunks);
+    else
+      hipLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
+                         part, max_chunks);
   } else {
-    hipLaunchKernelGGL((k_attn<BF, DH>), dim3(grid_chunks, g.n_heads, n_seq), dim3(256), 0, s, q,
-                       kv, g, layer, seqs, rows, part, max_chunks);
+    if (ev0)
+      hipExtLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
+                            seqs, rows, part, max_chunks);
+    else
+      hipLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
+                         part, max_chunks);
   }
   hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
                      g.n_heads, max_chunks, a_out);

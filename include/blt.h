@@ -102,8 +102,10 @@ typedef struct {
 } blt_weights;
 
 /* Caller-owned decode state (device), sized by blt_state_size:
- *   kv    : keys (after RoPE) and values of cached rows,
- *           [max_batch][n_layers][2][n_heads][max_ctx][d_model/n_heads], dtype;
+ *   kv    : keys (after RoPE) and values of cached rows, per
+ *           [max_batch][n_layers] a K plane [n_heads][ctx][d_model/n_heads]
+ *           and a transposed V plane [n_heads][d_model/n_heads][ctx], dtype,
+ *           with ctx = max_ctx rounded up to a multiple of 128;
  *   cross : per-latent cross-attention contributions W_o^c W_v^c W_lat o_m,
  *           [max_batch][max_latents][n_layers][d_model], float32.
  * Rows beyond a sequence's committed length hold scratch (the current
@@ -196,6 +198,19 @@ typedef enum { BLT_PROF_OFF = 0, BLT_PROF_ATTENTION = 1 } blt_prof_family;
 blt_status blt_profile_enable(blt_ctx *ctx, int32_t family);
 blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, double *bytes,
                             int32_t reset);
+
+/* Replay of decoder passes from HIP graphs (off by default: where the host
+ * waits for each pass's result before enqueueing the next, the graph launch
+ * latency at the head of a pass outweighs the launch gaps it removes).  The kernel
+ * sequence of a pass depends only on its shape (rows, sequences, the
+ * attention chunk grid in buckets of 4 chunks) and on its scalar and
+ * pointer arguments; the per-pass row and sequence descriptors are staged in
+ * device buffers before it.  The first pass of a shape is launched directly,
+ * the second is captured into a graph on a library-owned stream and every
+ * later one replays that graph on the context's stream; results are the same
+ * either way.  Passes while a profiling family is enabled are never replayed.
+ * enable = 0 launches every pass directly and frees the cached graphs. */
+blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
 
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
  * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),

@@ -98,22 +98,57 @@ def test_mini_bf16_blt_dv_teacher_forced():
 
 
 # ---------------------------------------------------------------- sessions
-def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_rows=64):
+def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_rows=64,
+             graphs=True, repeats=1, between=None):
+    """Run a native decode session; with repeats > 1 the generation is rerun
+    from the same prefill (calling `between` in between) and every run's
+    results are returned."""
     import torch
     import block_diffusion_byte_amd as blt
     dec = decoder_for(wl.replace(block=block), w, max_batch=len(inps), max_rows=max_rows)
+    blt.blt_graphs_enable(dec.ctx, graphs)
     table = torch.from_numpy(np.stack([i["latents"] for i in inps])).to("cuda:0", dec.torch_dtype)
     sess = blt.blt_session_create(dec.ctx, dec.state, [i["prompt"] for i in inps],
                                   [i["prompt_patches"] for i in inps], [i["salt"] for i in inps],
                                   table, wl.n_latents)
+    runs = []
     try:
         blt.blt_session_prefill(dec.ctx, sess)
-        blt.blt_session_generate(dec.ctx, sess, policy, block, alpha, n_gen, unmask, mask)
-        res = [blt.blt_session_result(sess, b, n_gen) for b in range(len(inps))]
+        for k in range(repeats):
+            if k and between:
+                between()
+            blt.blt_session_generate(dec.ctx, sess, policy, block, alpha, n_gen, unmask, mask)
+            runs.append([blt.blt_session_result(sess, b, n_gen) for b in range(len(inps))])
     finally:
         blt.blt_session_destroy(sess)
         dec.close()
-    return res
+    return runs if repeats > 1 else runs[0]
+
+
+@pytest.mark.parametrize("block", [4, 16])
+def test_graph_replays_match_direct_launches(block):
+    """Passes replayed from cached HIP graphs (GEMV path at block 4, MFMA path
+    at block 16) give the same bytes and counts as direct launches, on every
+    rerun, with unrelated eager GPU work and synchronisations in between."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = MINI_BF16.replace(head_scale=12.0)
+    w = bltgen.make_weights(wl)
+    inps = [bltgen.make_sequence_inputs(wl, b) for b in range(2)]
+
+    def eager_work():
+        x = torch.randn(512, 512, device="cuda:0")
+        (x @ x).sum().item()
+        torch.cuda.synchronize()
+
+    ref = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, block, 0.5, graphs=False)
+    runs = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, block, 0.5, graphs=True, repeats=4,
+                    between=eager_work)
+    for k, got in enumerate(runs):
+        for b in range(len(inps)):
+            assert got[b]["out"] == ref[b]["out"], f"run {k} seq {b}: bytes differ"
+            assert (got[b]["n_dec"], got[b]["n_eg"]) == (ref[b]["n_dec"], ref[b]["n_eg"])
+    say(f"block {block}: 4 graph runs identical to direct launches, n_dec {[r['n_dec'] for r in ref]}")
 
 
 @pytest.mark.parametrize("policy", ["greedy", "blt_d", "blt_s", "blt_dv"])
