@@ -19,6 +19,8 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <type_traits>
+
 #include "blt_internal.h"
 
 namespace blt {
@@ -28,6 +30,7 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
@@ -436,61 +439,122 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
 
 // ---------------------------------------------------------------------------
 // MFMA GEMM (bf16 x bf16 -> f32) for passes of >= 16 rows: Y[R][N] = X[R][K] W[N][K]^T.
-// 64x64 output tile per workgroup, K step 64 through LDS; each wave owns a
-// 32x32 quarter as 2x2 tiles of v_mfma_f32_16x16x32_bf16.
-constexpr int kBM = 64, kBN = 64, kBK = 64, kLdsK = kBK + 8;
+//
+// BM x BN output tile per workgroup: 4 waves as 2x2, each a (BM/2) x (BN/2)
+// block of 16x16 v_mfma_f32_16x16x32_bf16 tiles; K in steps of 64.  The
+// global loads of step k+2 are issued while step k computes (two register
+// slots) and each step's tile is stored to one of two LDS buffers, so the
+// load latency overlaps the MFMAs of the steps before.  An LDS tile row holds
+// its eight 16-byte chunks XOR-swizzled by the row index, so the 16 lanes
+// that read one chunk column of 16 rows hit distinct banks.  Workgroups are
+// dispatched round-robin over the 8 XCDs; tiles are ordered so that the
+// workgroups of one XCD take all row tiles of consecutive column tiles and
+// share those W tiles in the XCD's L2.
+constexpr int kGemmBK = 64;
 
+// f(integral_constant<int, I>) for I = 0..N-1: indices stay compile-time
+// constants, so register arrays indexed by them are never spilled.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+template <int BM, int BN, int P>
 __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
-  __shared__ uint16_t xs[kBM * kLdsK];
-  __shared__ uint16_t ws[kBN * kLdsK];
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-  const int n0 = blockIdx.x * kBN, m0 = blockIdx.y * kBM;
-  const int wr = (w >> 1) * 32, wc = (w & 1) * 32;
-  f32x4_t acc[2][2];
+  constexpr int CH = kGemmBK / 8;                   // 16-byte chunks per tile row
+  constexpr int LA = BM * CH / 256, LB = BN * CH / 256;  // chunks per thread per step
+  constexpr int TM = BM / 32, TN = BN / 32;         // 16x16 tiles per wave
+  static_assert(P % 2 == 0, "prefetch slots in pairs (two LDS buffers)");
+  __shared__ __align__(16) u32x4_t sa[2][BM * CH];
+  __shared__ __align__(16) u32x4_t sb[2][BN * CH];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int mt = (a.R + BM - 1) / BM, nt = (a.N + BN - 1) / BN, ntiles = mt * nt;
+  const int tile = (ntiles & 7) ? (int)blockIdx.x
+                                : (int)(blockIdx.x & 7) * (ntiles >> 3) + (int)(blockIdx.x >> 3);
+  const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
+  const uint16_t *X = (const uint16_t *)a.X, *W = (const uint16_t *)a.W;
+  // this thread's chunks of each step: tile chunk q = t + 256 i (row q / CH,
+  // column q % CH); rows past the matrix edge re-read its last row
+  const uint16_t *ga[LA], *gb[LB];
+  int sla[LA], slb[LB];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const uint16_t *X = (const uint16_t *)a.X;
-  const uint16_t *W = (const uint16_t *)a.W;
-  for (int k0 = 0; k0 < a.K; k0 += kBK) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int idx = tid + u * 256, row = idx >> 3, kc = idx & 7;
-      const int rr = m0 + row, nn = n0 + row;
-      uint4 xv = make_uint4(0, 0, 0, 0), wv = make_uint4(0, 0, 0, 0);
-      if (rr < a.R) {
-        const uint16_t *xr = X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx);
-        xv = *(const uint4 *)(xr + k0 + kc * 8);
-      }
-      if (nn < a.N) wv = *(const uint4 *)(W + (int64_t)nn * a.K + k0 + kc * 8);
-      *(uint4 *)&xs[row * kLdsK + kc * 8] = xv;
-      *(uint4 *)&ws[row * kLdsK + kc * 8] = wv;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int ks = 0; ks < kBK; ks += 32) {
-      bf16x8_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        uint4 v = *(const uint4 *)&xs[(wr + i * 16 + (l & 15)) * kLdsK + ks + 8 * (l >> 4)];
-        af[i] = __builtin_bit_cast(bf16x8_t, v);
-        uint4 u = *(const uint4 *)&ws[(wc + i * 16 + (l & 15)) * kLdsK + ks + 8 * (l >> 4)];
-        bfr[i] = __builtin_bit_cast(bf16x8_t, u);
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int i = 0; i < LA; ++i) {
+    const int q = t + 256 * i, r = q / CH, c = q % CH, rr = min(m0 + r, a.R - 1);
+    ga[i] = X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx) + c * 8;
+    sla[i] = r * CH + (c ^ (r & 7));
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < LB; ++i) {
+    const int q = t + 256 * i, r = q / CH, c = q % CH, nn = min(n0 + r, a.N - 1);
+    gb[i] = W + (int64_t)nn * a.K + c * 8;
+    slb[i] = r * CH + (c ^ (r & 7));
+  }
+  f32x4_t acc[TM][TN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int wr = (w >> 1) * (BM / 2), wc = (w & 1) * (BN / 2);
+  const int nk = a.K / kGemmBK;              // a multiple of P (K % 256 == 0)
+  u32x4_t xa[P][LA], xb[P][LB];              // register slots: step s waits in slot s % P
+
+  auto load = [&](u32x4_t (&ra)[LA], u32x4_t (&rb)[LB], int kt) {
+    kt = min(kt, nk - 1);                    // past the end: harmless re-reads
+    static_for<0, LA>([&](auto i) { ra[i] = *(const u32x4_t *)(ga[i] + kt * kGemmBK); });
+    static_for<0, LB>([&](auto i) { rb[i] = *(const u32x4_t *)(gb[i] + kt * kGemmBK); });
+  };
+  auto store = [&](u32x4_t *s_a, u32x4_t *s_b, const u32x4_t (&ra)[LA], const u32x4_t (&rb)[LB]) {
+    static_for<0, LA>([&](auto i) { s_a[sla[i]] = ra[i]; });
+    static_for<0, LB>([&](auto i) { s_b[slb[i]] = rb[i]; });
+  };
+  auto compute = [&](const u32x4_t *s_a, const u32x4_t *s_b) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int c = ks * 4 + (l >> 4);
+      bf16x8_t af[TM], bw[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = wr + i * 16 + (l & 15);
+        af[i] = __builtin_bit_cast(bf16x8_t, s_a[r * CH + (c ^ (r & 7))]);
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int r = wc + j * 16 + (l & 15);
+        bw[j] = __builtin_bit_cast(bf16x8_t, s_b[r * CH + (c ^ (r & 7))]);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bw[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // steps 0..P-1 in flight, step 0 staged in LDS buffer 0 and slot 0 refilled
+  static_for<0, P>([&](auto j) { load(xa[j], xb[j], j); });
+  store(sa[0], sb[0], xa[0], xb[0]);
+  load(xa[0], xb[0], P);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += P) {
+    // step kt+j computes from buffer j&1 while steps kt+j+1 .. kt+j+P load;
+    // step kt+j+1 moves from its slot to the other buffer, and the slot
+    // takes step kt+j+1+P
+    static_for<0, P>([&](auto j) {
+      constexpr int jn = (decltype(j)::value + 1) % P;
+      compute(sa[decltype(j)::value & 1], sb[decltype(j)::value & 1]);
+      store(sa[(decltype(j)::value + 1) & 1], sb[(decltype(j)::value + 1) & 1], xa[jn], xb[jn]);
+      load(xa[jn], xb[jn], kt + decltype(j)::value + 1 + P);
+      __syncthreads();
+    });
+  }
+  // acc[i][j][v]: row wr+16i+4(l/16)+v, column wc+16j+l%16 of the tile
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wr + i * 16 + 4 * (l >> 4) + v;
@@ -1161,8 +1225,14 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, float * /*rinv_ws*/, void *
     b.ldx = a.K;
     b.x_row_off = nullptr;
   }
-  hipLaunchKernelGGL(k_gemm_mfma, dim3((a.N + kBN - 1) / kBN, (a.R + kBM - 1) / kBM), dim3(256), 0,
-                     s, b);
+  if (b.K % (4 * kGemmBK)) return hipErrorInvalidValue;  // the pipeline takes K steps in fours
+  // 128x128 tiles when they alone give the chip enough workgroups
+  const int big = ((a.R + 127) / 128) * ((a.N + 127) / 128);
+  if (big >= 128)
+    hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2>), dim3(big), dim3(256), 0, s, b);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<64, 64, 4>), dim3(((a.R + 63) / 64) * ((a.N + 63) / 64)),
+                       dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
