@@ -3,6 +3,7 @@
   * byte_choice: the greedy byte and its confidence from one row's logits;
   * unmask_commit: confidence-threshold unmasking with the forced fallback,
     or one-step filling;
+  * entropy / unmask_commit_entropy: entropy-bounded (EB) unmasking;
   * verify_accept: the greedy exact-match verification of a draft.
 """
 from __future__ import annotations
@@ -52,6 +53,48 @@ def unmask_commit(block, choice, conf, alpha, one_step=False):
         if not chosen:
             best = max(conf[i] for i in masked)
             chosen = [min(i for i in masked if conf[i] == best)]
+    for i in chosen:
+        block[i] = int(choice[i])
+    return block, chosen
+
+
+def entropy(z):
+    """Entropy in nats of the byte distribution of one row of 257 logits.
+
+    The distribution is the softmax over bytes 0..255 ([MASK] takes no part,
+    as for the greedy byte): H = -sum_b p_b log p_b.
+    """
+    z = np.asarray(z, dtype=np.float64)[:256]
+    p = np.exp(z - z.max())
+    p = p / p.sum()
+    nz = p[p > 0]
+    return float(-(nz * np.log(nz)).sum())
+
+
+def unmask_commit_entropy(block, choice, ent, gamma):
+    """Entropy-bounded unmasking after one decoder pass.
+
+    pytorch.kr summary, "block unmasking strategies" (EB sampling): the
+    masked positions are ranked by the entropy of their prediction, lowest
+    first, and the largest set of them whose summed entropy does not exceed
+    gamma is decoded at once.  Readings: equal entropies rank by position;
+    the entropies are summed in rank order; at least the lowest-entropy
+    position is committed, so decoding always advances (as the forced commit
+    of the threshold rule).  Committed positions take their greedy byte and
+    stay committed.  Returns (new block, committed positions in order).
+    """
+    block = list(block)
+    masked = [i for i, t in enumerate(block) if t == MASK]
+    if not masked:
+        return block, []
+    order = sorted(masked, key=lambda i: (ent[i], i))
+    total, n = 0.0, 0
+    for i in order:
+        total += ent[i]
+        if total > gamma:
+            break
+        n += 1
+    chosen = sorted(order[:max(n, 1)])
     for i in chosen:
         block[i] = int(choice[i])
     return block, chosen

@@ -288,6 +288,66 @@ def test_unmask_rules():
     assert blk == [1, 4, 3]
 
 
+def test_entropy_closed_forms_and_library():
+    """Entropy of the byte distribution: scipy's entropy of the softmax over
+    bytes 0..255; uniform -> ln 256, two tied bytes -> ln 2, one-hot -> 0;
+    the [MASK] logit never counts."""
+    from scipy.stats import entropy as sp_entropy
+    rng = np.random.default_rng(7)
+    for _ in range(5):
+        z = rng.normal(0, 3, 257)
+        p = np.exp(z[:256] - z[:256].max())
+        assert decide.entropy(z) == pytest.approx(sp_entropy(p / p.sum()), rel=1e-12, abs=1e-12)
+        z2 = z.copy()
+        z2[256] = 1e3
+        assert decide.entropy(z2) == decide.entropy(z)
+    assert decide.entropy(np.zeros(257)) == pytest.approx(np.log(256), rel=1e-14)
+    two = np.full(257, -1e9)
+    two[[3, 200]] = 5.0
+    assert decide.entropy(two) == pytest.approx(np.log(2), rel=1e-14)
+    one = np.zeros(257)
+    one[17] = 1e4
+    assert decide.entropy(one) == 0.0
+
+
+def test_entropy_bounded_unmask_rules():
+    M = decide.MASK
+    # ranked 1 (0.1), 2 (0.3), 0 (0.5): cumulative 0.1, 0.4, 0.9
+    blk, ch = decide.unmask_commit_entropy([M, M, M], [7, 8, 9], [0.5, 0.1, 0.3], 0.45)
+    assert blk == [M, 8, 9] and ch == [1, 2]
+    blk, ch = decide.unmask_commit_entropy([M, M, M], [7, 8, 9], [0.5, 0.1, 0.3], 0.05)
+    assert blk == [M, 8, M] and ch == [1]                 # at least one commit
+    blk, ch = decide.unmask_commit_entropy([M, 4, M], [7, 8, 9], [0.2, 0.0, 0.2], 0.3)
+    assert blk == [7, 4, M] and ch == [0]                 # equal entropies: lower position first
+    blk, ch = decide.unmask_commit_entropy([M, 4, M], [7, 8, 9], [0.2, 0.0, 0.2], np.inf)
+    assert blk == [7, 4, 9]
+
+
+def test_entropy_bounded_unmask_is_the_largest_subset_within_gamma():
+    """Brute force over every subset of the masked positions (B <= 6): the
+    number committed is the largest size of a subset whose entropies sum to
+    at most gamma (at least 1), and the committed positions are the lowest-
+    entropy ones."""
+    M = decide.MASK
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        B = int(rng.integers(1, 7))
+        block = [M if rng.random() < 0.8 else 5 for _ in range(B)]
+        masked = [i for i in range(B) if block[i] == M]
+        ent = list(np.round(rng.exponential(0.7, B), 2))   # rounded: ties happen
+        gamma = float(rng.choice([0.0, rng.uniform(0, 3), np.inf]))
+        out, ch = decide.unmask_commit_entropy(block, list(range(10, 10 + B)), ent, gamma)
+        if not masked:
+            assert ch == [] and out == block
+            continue
+        best = max((len(S) for r in range(len(masked) + 1) for S in itertools.combinations(masked, r)
+                    if sum(ent[i] for i in S) <= gamma), default=0)
+        assert len(ch) == max(best, 1)
+        worst_in = max(ent[i] for i in ch)
+        assert all(ent[i] >= worst_in for i in masked if i not in ch)
+        assert all(out[i] == 10 + i for i in ch) and all(out[i] == block[i] for i in range(B) if i not in ch)
+
+
 def test_verify_exhaustive_against_greedy_continuation():
     """r <= 3, 2-symbol alphabet: the committed bytes are exactly the first
     a + 1 bytes of the greedy continuation, and a is the longest draft prefix
@@ -373,6 +433,23 @@ def test_blt_d_alpha_extremes(tiny):
     lo = loops.blt_d(W, wl, inp, 32, 4, 1.0 / 512)
     one = loops.blt_d(W, wl, inp, 32, 4, 0.7, one_step=True)
     assert lo.out == one.out and lo.n_dec == 8 == one.n_dec
+
+
+def test_blt_d_entropy_bound_extremes(tiny):
+    """Entropy-bounded unmasking: an unbounded gamma fills the block in one
+    pass (= one-step); gamma = 0 commits one position per pass; with B = 1
+    every rule is the masked-row greedy decoder."""
+    wl, W, inp = tiny
+    inf = loops.blt_d(W, wl, inp, 32, 4, np.inf, unmask="entropy")
+    one = loops.blt_d(W, wl, inp, 32, 4, 0.7, one_step=True)
+    assert inf.out == one.out and inf.n_dec == one.n_dec == 8
+    zero = loops.blt_d(W, wl, inp, 32, 4, 0.0, unmask="entropy", trace=True)
+    assert zero.n_dec == 32 and all(len(p["chosen"]) == 1 for p in zero.passes)
+    for p in zero.passes:               # the committed position has the lowest entropy
+        masked = [j for j, t in enumerate(p["block_before"]) if t == decide.MASK]
+        assert p["entropy"][p["chosen"][0]] == min(p["entropy"][j] for j in masked)
+    ref = loops.masked_row_greedy(W, wl, inp, 12)
+    assert loops.blt_d(W, wl, inp, 12, 1, 0.5, unmask="entropy").out == ref
 
 
 def test_blt_d_peaked_head_commits_several_per_pass():
