@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libblt.so")
 
 BLT_OK, BLT_EINVAL, BLT_ECAPACITY, BLT_EDTYPE, BLT_EHIP = 0, -1, -2, -3, -4
 BLT_F32, BLT_BF16 = 0, 1
-BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP = 0, 1
+BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP, BLT_UNMASK_ENTROPY = 0, 1, 2
 BLT_BLOCK_BIDIR, BLT_BLOCK_CAUSAL = 0, 1
 BLT_POLICY_GREEDY, BLT_POLICY_BLT_D, BLT_POLICY_BLT_S, BLT_POLICY_BLT_DV = 0, 1, 2, 3
 BLT_PROF_OFF, BLT_PROF_ATTENTION = 0, 1

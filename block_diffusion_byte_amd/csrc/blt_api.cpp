@@ -145,7 +145,7 @@ struct PassLaunch {
   const int32_t *block_tok, *tokens_dev;
   bool unmask;
   float alpha;
-  int one_step;
+  int mode;                          // a blt_unmask value
   int32_t *masked_left, *argmax_out;
   float *conf_out, *logits_out;
   const std::vector<SeqDesc> *seqs;  // for the profiling byte counts
@@ -215,11 +215,12 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
   a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
   HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
-  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, p.argmax_out,
+  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, c->ent_ws,
+                           p.unmask && p.mode == BLT_UNMASK_ENTROPY, p.argmax_out,
                            p.conf_out, p.logits_out, s));
   if (p.unmask)
-    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, (int32_t *)p.block_tok,
-                             p.alpha, p.one_step, p.masked_left, s));
+    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, c->ent_ws,
+                             (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
   return BLT_OK;
 }
 
@@ -235,7 +236,7 @@ void drop_graphs(blt_ctx *c) {
 // capture stream, launched on its stream).
 blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
                     const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
-                    const int32_t *tokens_dev, bool unmask, float alpha, int one_step,
+                    const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
                     float *logits_out) {
   blt_status bs = stage_pass(c, rows, seqs, nullptr);
@@ -243,7 +244,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
   int kmax = 0;
   for (const SeqDesc &sd : seqs) kmax = std::max(kmax, sd.kmax);
   PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk, st,
-               block_tok, tokens_dev, unmask, alpha, one_step, masked_left, argmax_out, conf_out,
+               block_tok, tokens_dev, unmask, alpha, mode, masked_left, argmax_out, conf_out,
                logits_out, &seqs};
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
@@ -252,7 +253,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> 
   PassKey key;
   memset(&key, 0, sizeof(key));
   key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.unmask = unmask;
-  key.one_step = one_step;
+  key.mode = mode;
   memcpy(&key.alpha_bits, &alpha, sizeof(float));
   key.kv = st->kv; key.cross = st->cross; key.block_tok = block_tok; key.tokens_dev = tokens_dev;
   key.masked_left = masked_left; key.argmax_out = argmax_out; key.conf_out = conf_out;
@@ -335,6 +336,7 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(dalloc(&c->logits, (size_t)R * kVocab));
   chk(dalloc(&c->rinv, (size_t)R));
   chk(dalloc(&c->conf_ws, (size_t)R));
+  chk(dalloc(&c->ent_ws, (size_t)R));
   chk(dalloc(&c->argmax_ws, (size_t)R));
   chk(hipMalloc(&c->xa, std::max<size_t>(1, (size_t)R * wide * e)));
   chk(hipMalloc(&c->xb, std::max<size_t>(1, (size_t)R * std::max(d, cfg->d_global) * e)));
@@ -376,7 +378,7 @@ blt_status blt_destroy(blt_ctx *c) {
   (void)hipStreamSynchronize(c->stream);
   drop_graphs(c);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->argmax_ws,
+  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->ent_ws, c->argmax_ws,
                   c->xa, c->xb, c->desc_d, c->rope_tab};
   for (void *p : bufs)
     if (p) (void)hipFree(p);
@@ -508,9 +510,11 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
   if (!start_pos || !block_tok || !block_lat || !masked_left)
     return fail(c, BLT_EINVAL, "blt_decode_block_step: NULL argument");
   if (B < 1 || B > g.max_block) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: B outside 1..max_block");
-  if (mode != BLT_UNMASK_THRESHOLD && mode != BLT_UNMASK_ONE_STEP) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad unmask mode");
+  if (mode != BLT_UNMASK_THRESHOLD && mode != BLT_UNMASK_ONE_STEP && mode != BLT_UNMASK_ENTROPY)
+    return fail(c, BLT_EINVAL, "blt_decode_block_step: bad unmask mode");
   if (mask != BLT_BLOCK_BIDIR && mask != BLT_BLOCK_CAUSAL) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad block mask");
-  if (!isfinite(alpha)) return fail(c, BLT_EINVAL, "blt_decode_block_step: alpha must be finite");
+  if (mode == BLT_UNMASK_ENTROPY ? !(alpha >= 0.f) : !isfinite(alpha))
+    return fail(c, BLT_EINVAL, "blt_decode_block_step: alpha must be finite (an entropy bound: >= 0, may be +inf)");
   if (n_append_max < 0 || (n_append_max > 0 && (!n_append || !append_bytes || !append_lat)))
     return fail(c, BLT_EINVAL, "blt_decode_block_step: bad append arguments");
   std::vector<RowDesc> rows;
@@ -538,7 +542,7 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
     }
     seqs.push_back(sd);
   }
-  return run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, mode == BLT_UNMASK_ONE_STEP,
+  return run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, (int)mode,
                   masked_left, argmax_out, conf_out, logits_out);
 }
 

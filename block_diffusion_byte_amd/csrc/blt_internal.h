@@ -108,12 +108,14 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
                             hipEvent_t ev1, hipStream_t s);
 bool gemv_supported(bool bf16, int K);
+// report_entropy: conf_out receives each row's entropy instead of its confidence.
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
-                         float *conf_ws, int32_t *argmax_out, float *conf_out,
-                         float *logits_out, hipStream_t s);
+                         float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
+                         float *conf_out, float *logits_out, hipStream_t s);
+// mode: a blt_unmask value; alpha: the confidence threshold or the entropy bound.
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
-                         const float *conf_ws, int32_t *block_tok, float alpha, int one_step,
-                         int32_t *masked_left, hipStream_t s);
+                         const float *conf_ws, const float *ent_ws, int32_t *block_tok,
+                         float alpha, int mode, int32_t *masked_left, hipStream_t s);
 hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,
                          int ld_draft, const int32_t *pred, int ld_pred, int32_t *accept_len,
                          int32_t *next_byte, hipStream_t s);

@@ -1048,9 +1048,9 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
 // Greedy byte and confidence of each row: max over logits 0..255 (the [MASK]
 // logit takes no part), lowest id on ties, conf = 1 / sum exp(z - max).
 __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDesc *rows,
-                                               int32_t *argmax_ws, float *conf_ws,
-                                               int32_t *argmax_out, float *conf_out,
-                                               float *logits_out) {
+                                               int32_t *argmax_ws, float *conf_ws, float *ent_ws,
+                                               int report_entropy, int32_t *argmax_out,
+                                               float *conf_out, float *logits_out) {
   const int r = blockIdx.x, l = threadIdx.x;
   const float *z = logits + (int64_t)r * kVocab;
   float best = -INFINITY;
@@ -1083,45 +1083,76 @@ __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDes
     best = bv;
     bi = bx;
   }
-  float s = 0.f;
+  // S = sum_b e_b and T = sum_b e_b (z_b - max) with e_b = exp(z_b - max):
+  // conf = 1 / S, entropy = ln S - T / S (nats)
+  float s = 0.f, tz = 0.f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) s += expf(z[l + 64 * i] - best);
+  for (int i = 0; i < 4; ++i) {
+    const float x = z[l + 64 * i] - best;
+    const float e = expf(x);
+    s += e;
+    tz = fmaf(e, x, tz);
+  }
   s = wave_sum(s);
+  tz = wave_sum(tz);
+  const float ent = logf(s) - tz / s;
   const int oidx = rows[r].oidx;
   if (l == 0) {
     argmax_ws[r] = bi;
     conf_ws[r] = 1.f / s;
+    ent_ws[r] = ent;
     if (oidx >= 0) {
       if (argmax_out) argmax_out[oidx] = bi;
-      if (conf_out) conf_out[oidx] = 1.f / s;
+      if (conf_out) conf_out[oidx] = report_entropy ? ent : 1.f / s;
     }
   }
   if (oidx >= 0 && logits_out)
     for (int j = l; j < kVocab; j += 64) logits_out[(int64_t)oidx * kVocab + j] = z[j];
 }
 
-// Confidence-threshold unmasking with the forced single commit, or one-step
-// filling; one wave per sequence, lane j = block position j.
+// Unmasking after a pass; one wave per sequence, lane j = block position j.
+// THRESHOLD: masked positions with conf > alpha, or if none the most
+// confident one (lowest position on ties); ONE_STEP: every masked position;
+// ENTROPY: masked positions ranked by entropy (ties by position), committed
+// in rank order while the running entropy sum stays <= alpha (the bound
+// gamma), at least the first.
 __global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_t *argmax_ws,
-                                               const float *conf_ws, int32_t *block_tok,
-                                               float alpha, int one_step, int32_t *masked_left) {
+                                               const float *conf_ws, const float *ent_ws,
+                                               int32_t *block_tok, float alpha, int mode,
+                                               int32_t *masked_left) {
   const SeqDesc sd = seqs[blockIdx.x];
   if (sd.nblk <= 0) return;
   const int j = threadIdx.x;
   const bool active = j < sd.nblk;
   const int tok = active ? block_tok[sd.blk0 + j] : 0;
   const bool masked = active && tok == kMask;
-  const float c = masked ? conf_ws[sd.blk_row0 + j] : -1.f;
-  bool commit = masked && (one_step || c > alpha);
   const unsigned long long mm = __ballot(masked);
-  unsigned long long cm = __ballot(commit);
-  if (cm == 0ull && mm != 0ull) {
-    const float best = wave_max(c);
-    const unsigned long long cand = __ballot(masked && c == best);
-    commit = (j == __ffsll((long long)cand) - 1);
-    cm = __ballot(commit);
+  unsigned long long cm = 0ull;
+  if (mode == BLT_UNMASK_ENTROPY) {
+    const float e = masked ? ent_ws[sd.blk_row0 + j] : INFINITY;
+    int rank = 0;                                   // masked positions ahead of this one
+    for (int i = 0; i < 64; ++i) {
+      const float ei = lane_f(e, i);
+      rank += ((mm >> i) & 1ull) && (ei < e || (ei == e && i < j));
+    }
+    float sum = 0.f;
+    const int nm = __popcll(mm);
+    for (int k = 0; k < nm; ++k) {                  // uniform walk in rank order
+      const int who = __ffsll((long long)__ballot(masked && rank == k)) - 1;
+      sum += lane_f(e, who);
+      if (k > 0 && !(sum <= alpha)) break;
+      cm |= 1ull << who;
+    }
+  } else {
+    const float c = masked ? conf_ws[sd.blk_row0 + j] : -1.f;
+    cm = __ballot(masked && (mode == BLT_UNMASK_ONE_STEP || c > alpha));
+    if (cm == 0ull && mm != 0ull) {
+      const float best = wave_max(c);
+      const unsigned long long cand = __ballot(masked && c == best);
+      cm = 1ull << (__ffsll((long long)cand) - 1);
+    }
   }
-  if (commit) block_tok[sd.blk0 + j] = argmax_ws[sd.blk_row0 + j];
+  if ((cm >> j) & 1ull) block_tok[sd.blk0 + j] = argmax_ws[sd.blk_row0 + j];
   if (j == 0) masked_left[sd.out_b] = __popcll(mm) - __popcll(cm);
 }
 
@@ -1305,18 +1336,18 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
 }
 
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
-                         float *conf_ws, int32_t *argmax_out, float *conf_out, float *logits_out,
-                         hipStream_t s) {
-  hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws,
-                     argmax_out, conf_out, logits_out);
+                         float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
+                         float *conf_out, float *logits_out, hipStream_t s) {
+  hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
+                     report_entropy, argmax_out, conf_out, logits_out);
   return hipGetLastError();
 }
 
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
-                         const float *conf_ws, int32_t *block_tok, float alpha, int one_step,
-                         int32_t *masked_left, hipStream_t s) {
-  hipLaunchKernelGGL(k_unmask, dim3(n_seq), dim3(64), 0, s, seqs, argmax_ws, conf_ws, block_tok,
-                     alpha, one_step, masked_left);
+                         const float *conf_ws, const float *ent_ws, int32_t *block_tok, float alpha,
+                         int mode, int32_t *masked_left, hipStream_t s) {
+  hipLaunchKernelGGL(k_unmask, dim3(n_seq), dim3(64), 0, s, seqs, argmax_ws, conf_ws, ent_ws,
+                     block_tok, alpha, mode, masked_left);
   return hipGetLastError();
 }
 

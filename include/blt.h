@@ -53,12 +53,20 @@ typedef enum {
 
 typedef enum { BLT_F32 = 0, BLT_BF16 = 1 } blt_dtype;
 
-/* How a decode step commits masked block positions (block unmasking
- * strategies): THRESHOLD commits every masked position whose confidence
- * (largest byte probability) is > alpha, and the single most confident one
- * (lowest position on ties) when none is; ONE_STEP commits every masked
- * position in one pass (the one-step diffusion draft of BLT-DV). */
-typedef enum { BLT_UNMASK_THRESHOLD = 0, BLT_UNMASK_ONE_STEP = 1 } blt_unmask;
+/* How a decode step commits masked block positions (pytorch.kr summary,
+ * "block unmasking strategies"): THRESHOLD commits every masked position
+ * whose confidence (largest byte probability) is > alpha, and the single most
+ * confident one (lowest position on ties) when none is; ONE_STEP commits
+ * every masked position in one pass (the one-step diffusion draft of BLT-DV);
+ * ENTROPY (entropy-bounded, EB) ranks the masked positions by the entropy in
+ * nats of their byte distribution (ties by position) and commits them in rank
+ * order while the running sum of their entropies is <= alpha (the bound
+ * gamma), at least the first one.  Committed positions take their greedy byte. */
+typedef enum {
+  BLT_UNMASK_THRESHOLD = 0,
+  BLT_UNMASK_ONE_STEP = 1,
+  BLT_UNMASK_ENTROPY = 2
+} blt_unmask;
 
 /* Self-attention inside the block: bidirectional (diffusion mode) or causal
  * (the same weights run autoregressively). */
@@ -163,9 +171,11 @@ blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const
  * cached row and every block row (BIDIR) or the block rows up to themselves
  * (CAUSAL).  Block rows are not kept as clean rows (their cache rows are
  * scratch).  Then every still-masked block position is decided by `mode` /
- * `alpha` and block_tok is updated in place; masked_left[slot[b]] (device)
- * receives the number of [MASK]s left.  Optional device outputs for block
- * rows: argmax_out/conf_out [slot[b]*B+j], logits_out [(slot[b]*B+j)*257+v]. */
+ * `alpha` (a finite threshold; for ENTROPY a bound >= 0, +inf allowed) and
+ * block_tok is updated in place; masked_left[slot[b]] (device) receives the
+ * number of [MASK]s left.  Optional device outputs for block rows:
+ * argmax_out/conf_out [slot[b]*B+j] (conf_out: the row's confidence, or its
+ * entropy in nats under ENTROPY), logits_out [(slot[b]*B+j)*257+v]. */
 blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batch,
                                  const int32_t *slot, const int32_t *start_pos,
                                  const int32_t *n_append, int32_t n_append_max,
@@ -243,7 +253,7 @@ typedef enum {
 typedef struct {
   blt_policy policy;
   int32_t block;            /* B (BLT-D, BLT-DV) or draft window k (BLT-S) */
-  float alpha;              /* confidence threshold */
+  float alpha;              /* confidence threshold, or the entropy bound for ENTROPY */
   blt_unmask unmask;
   blt_block_mask block_mask;
   int32_t n_gen;            /* bytes to generate per sequence */

@@ -36,7 +36,7 @@ def _replay(wl, policy, n_gen, gains="random", **kw):
     W, inp, inp64 = oracle_inputs(wl, w)
     if policy == "blt_d":
         run = loops.blt_d(W, wl, inp64, n_gen, kw["B"], kw["alpha"], kw.get("one_step", False),
-                          kw.get("causal", False), trace=True)
+                          kw.get("causal", False), trace=True, unmask=kw.get("unmask"))
     elif policy == "blt_s":
         run = loops.blt_s(W, wl, inp64, n_gen, kw["k"], trace=True)
     elif policy == "blt_dv":
@@ -48,7 +48,8 @@ def _replay(wl, policy, n_gen, gains="random", **kw):
     dec = decoder_for(wl2, w, max_batch=1, max_rows=64)
     try:
         worst, comp, skip = replay_and_compare(dec, wl2, inp, run, kw.get("alpha", 0.0),
-                                               kw.get("one_step", policy == "blt_dv"), wl.dtype)
+                                               kw.get("unmask") or kw.get("one_step", policy == "blt_dv"),
+                                               wl.dtype)
     finally:
         dec.close()
     say(f"{wl.name} {policy}: {len(run.passes)} passes, worst logit err {worst:.3g}, "
@@ -95,6 +96,19 @@ def test_mini_bf16_blt_s_teacher_forced():
 def test_mini_bf16_blt_dv_teacher_forced():
     wl = MINI_BF16.replace(block=8)
     _replay(wl, "blt_dv", 24, B=8, alpha=0.7, one_step=True)
+
+
+def test_tiny_fp32_entropy_bounded_teacher_forced():
+    """Entropy-bounded unmasking (gamma 4 nats, B 8, peaked head: passes
+    commit 1 to 5 positions), float32 GEMV path."""
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    _replay(wl, "blt_d", 32, B=8, alpha=4.0, unmask="entropy")
+
+
+def test_mini_bf16_entropy_bounded_block16_teacher_forced():
+    """Entropy-bounded unmasking, B 16 on the bf16 MFMA path."""
+    wl = MINI_BF16.replace(head_scale=12.0, block=16)
+    _replay(wl, "blt_d", 32, B=16, alpha=4.0, unmask="entropy")
 
 
 # ---------------------------------------------------------------- sessions
@@ -180,6 +194,25 @@ def test_tiny_fp32_sessions_match_oracle_exactly(policy):
         if r.accept:
             assert g["rounds"] == len(r.accept) and g["accepted"] == sum(r.accept)
     say(f"{policy}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
+
+
+def test_tiny_fp32_entropy_bounded_session_exact():
+    """The native BLT-D driver with entropy-bounded unmasking reproduces the
+    oracle's bytes and pass counts exactly (3 sequences, gamma 4 nats)."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    w = bltgen.make_weights(wl, gains="random")
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        refs.append(loops.blt_d(W, wl, inp64, 40, 8, 4.0, unmask="entropy"))
+    got = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 8, 4.0, blt.BLT_UNMASK_ENTROPY)
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
+    assert min(r.n_dec for r in refs) < 40
+    say(f"EB sessions: n_dec {[g['n_dec'] for g in got]} for 40 bytes")
 
 
 def test_tiny_fp32_peaked_session_multi_commit_exact():
