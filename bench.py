@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-PROFILE_MD = os.path.join(ROOT, "profiles", "k_attn_bltd4_bf16_b1_ctx4096.md")
+PROFILE_MD = os.path.join(ROOT, "profiles", "k_attn_mfma_bltd4_bf16_b1_ctx4096.md")
 KERNELS_SRC = os.path.join(ROOT, "block_diffusion_byte_amd", "csrc", "kernels.hip")
 
 
@@ -206,7 +206,7 @@ def main():
                    "bytes_generated": wl.n_gen},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic(args.workload),
-                     "kernel": "k_attn (split-K attention partials)",
+                     "kernel": "k_attn_mfma (split-K attention partials, MFMA)",
                      "launches": launches, "avg_us": avg_us, "bytes_per_launch": bytes_per_launch,
                      "ms_per_step_with_events": 1e3 * elapsed_prof / args.steps},
         "counters": {"decoder_passes_per_seq": n_dec / wl.batch,
