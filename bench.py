@@ -23,6 +23,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak (published)
 PROFILE_MD = os.path.join(ROOT, "profiles", "k_attn_mfma_bltd4_bf16_b1_ctx4096.md")
 KERNELS_SRC = os.path.join(ROOT, "block_diffusion_byte_amd", "csrc", "kernels.hip")
 
@@ -103,6 +104,20 @@ def cpu_baseline(wl, w, n_bytes, ctx):
                       f"{t_dec:.1f} s (prefill {t_pre:.1f} s, untimed)"}
 
 
+def prefill_report(rows, seconds, max_rows, launches, ms, flops):
+    """Prompt prefill: rows per second, and the causal attention kernel's
+    achieved bf16 MFMA rate (algorithmic flops / event-timed duration)."""
+    avg_us = 1e3 * ms / max(launches, 1)
+    fpl = flops / max(launches, 1)
+    tflops = fpl / (avg_us * 1e-6) / 1e12 if launches else 0.0
+    return {"rows": rows, "seconds": seconds, "rows_per_s": rows / seconds,
+            "rows_per_pass": max_rows,
+            "roofline": {"bound": "mfma", "kernel": "k_attn_flash (causal attention, MFMA bf16)",
+                         "achieved": tflops, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tflops / MFMA_BF16_PEAK_TFLOPS, "launches": launches,
+                         "avg_us": avg_us, "flops_per_launch": fpl}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -132,7 +147,9 @@ def main():
     dev = "cuda:0"
     w = bltgen.make_weights(wl)
     inps = [bltgen.make_sequence_inputs(wl, b) for b in range(wl.batch)]
-    max_rows = max(1024, wl.batch * (2 * wl.block + 2))
+    # one prefill pass per prompt (the causal kernel wants long passes), and
+    # room for the largest decode pass
+    max_rows = max(1024, wl.batch * (2 * wl.block + 2), wl.prompt_len)
     dec = blt.Decoder(w, n_layers=wl.n_layers, d_model=wl.d_model, n_heads=wl.n_heads,
                       d_ffn=wl.d_ffn, d_global=wl.d_global, dtype=wl.dtype, max_batch=wl.batch,
                       max_ctx=wl.max_ctx, max_latents=wl.n_latents, max_rows=max_rows,
@@ -145,10 +162,21 @@ def main():
     sess = blt.blt_session_create(dec.ctx, dec.state, [i["prompt"] for i in inps],
                                   [i["prompt_patches"] for i in inps], [i["salt"] for i in inps],
                                   table, wl.n_latents)
+    # Prefill (the prompts' clean rows through blt_kv_append): once to warm
+    # up, once timed, once with the causal attention kernel's launches
+    # stamped by HIP events (its average duration and algorithmic flops).
+    blt.blt_session_prefill(dec.ctx, sess)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     blt.blt_session_prefill(dec.ctx, sess)
     torch.cuda.synchronize()
     t_prefill = time.perf_counter() - t0
+    blt.blt_profile_enable(dec.ctx, blt.BLT_PROF_ATTENTION_CAUSAL)
+    blt.blt_profile_read(dec.ctx, reset=True)
+    blt.blt_session_prefill(dec.ctx, sess)
+    pf_launches, pf_ms, pf_flops = blt.blt_profile_read(dec.ctx, reset=True)
+    blt.blt_profile_enable(dec.ctx, blt.BLT_PROF_OFF)
+    prefill_rows = sum(len(i["prompt"]) - 1 for i in inps)
     unmask = blt.BLT_UNMASK_ONE_STEP if wl.unmask == "one_step" else blt.BLT_UNMASK_THRESHOLD
     pid = policy_id(blt, wl)
 
@@ -214,6 +242,7 @@ def main():
                      "proxy_gb_per_seq_counted_params": gb_counted,
                      "proxy_gb_per_seq_pages_params": gb_pages,
                      "prefill_s": t_prefill},
+        "prefill": prefill_report(prefill_rows, t_prefill, max_rows, pf_launches, pf_ms, pf_flops),
     }
     if not args.no_cpu:
         n_cpu = args.cpu_bytes or {0: 64, 1: 128, 2: 128, 3: 128, 4: 48}[args.workload]

@@ -25,7 +25,7 @@ BLT_F32, BLT_BF16 = 0, 1
 BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP, BLT_UNMASK_ENTROPY = 0, 1, 2
 BLT_BLOCK_BIDIR, BLT_BLOCK_CAUSAL = 0, 1
 BLT_POLICY_GREEDY, BLT_POLICY_BLT_D, BLT_POLICY_BLT_S, BLT_POLICY_BLT_DV = 0, 1, 2, 3
-BLT_PROF_OFF, BLT_PROF_ATTENTION = 0, 1
+BLT_PROF_OFF, BLT_PROF_ATTENTION, BLT_PROF_ATTENTION_CAUSAL = 0, 1, 2
 MASK = 256
 VOCAB = 257
 

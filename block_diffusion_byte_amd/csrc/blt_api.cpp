@@ -140,7 +140,7 @@ GemmArgs base_args(const blt_ctx *c) {
 
 // Arguments of the kernel sequence of one pass besides the staged descriptors.
 struct PassLaunch {
-  int R, S, grid_chunks;
+  int R, S, grid_chunks, flash_tiles;
   const blt_state *st;
   const int32_t *block_tok, *tokens_dev;
   bool unmask;
@@ -148,7 +148,8 @@ struct PassLaunch {
   int mode;                          // a blt_unmask value
   int32_t *masked_left, *argmax_out;
   float *conf_out, *logits_out;
-  const std::vector<SeqDesc> *seqs;  // for the profiling byte counts
+  double split_bytes;                // per layer: K and V rows the split-K kernel's sequences read
+  double flash_flops;                // per layer: the causal kernel's QK^T and PV flops
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
@@ -180,15 +181,14 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
       HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
     }
     hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (c->prof_family == BLT_PROF_ATTENTION) {
-      // algorithmic bytes: the K and V rows the pass's rows must read
-      double kvb = 0;
-      for (const SeqDesc &sd : *p.seqs) kvb += (double)sd.kmax * 2.0 * d * (bf ? 2 : 4);
-      blt_status pb = prof_next(c, kvb, &e0, &e1);
+    const bool ev_flash = c->prof_family == BLT_PROF_ATTENTION_CAUSAL;
+    if ((c->prof_family == BLT_PROF_ATTENTION && p.grid_chunks > 0) ||
+        (ev_flash && p.flash_tiles > 0)) {
+      blt_status pb = prof_next(c, ev_flash ? p.flash_flops : p.split_bytes, &e0, &e1);
       if (pb != BLT_OK) return pb;
     }
     HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, c->max_chunks,
-                                c->rows_d, R, c->part, c->xa, e0, e1, s));
+                                p.flash_tiles, c->rows_d, R, c->part, c->xa, e0, e1, ev_flash, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.wo; a.N = d; a.K = d;
@@ -234,25 +234,46 @@ void drop_graphs(blt_ctx *c) {
 // staged, then the kernel sequence is launched directly or, for a pass shape
 // seen before, replayed from a cached graph (captured on the context's own
 // capture stream, launched on its stream).
-blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
-                    const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
+blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
+                    std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
                     float *logits_out) {
+  // Attention path per sequence, from its own rows only: a bf16 sequence
+  // whose rows in the pass are all clean (no block) and number at least
+  // kFlashMinRows takes the causal kernel; every other one the split-K kernel.
+  // Profiling figures per layer: the split-K kernel must read the K and V
+  // rows below each of its sequences' kmax; the causal kernel does 4 d flops
+  // per (row, key) pair (two multiply-adds per head dimension, QK^T and PV).
+  const int d = c->cfg.d_model;
+  int kmax = 0, flash_tiles = 0;
+  double split_bytes = 0, flash_flops = 0;
+  for (SeqDesc &sd : seqs) {
+    sd.attn_flash = c->bf16 && sd.blk0 < 0 && sd.nrows >= kFlashMinRows;
+    for (int r = sd.row0; r < sd.row0 + sd.nrows; ++r) {
+      rows[r].attn_flash = sd.attn_flash;
+      if (sd.attn_flash) flash_flops += 4.0 * d * rows[r].kend;
+    }
+    if (sd.attn_flash) {
+      flash_tiles = std::max(flash_tiles, (sd.nrows + kFlashRows - 1) / kFlashRows);
+    } else {
+      kmax = std::max(kmax, sd.kmax);
+      split_bytes += (double)sd.kmax * 2.0 * d * (c->bf16 ? 2 : 4);
+    }
+  }
   blt_status bs = stage_pass(c, rows, seqs, nullptr);
   if (bs != BLT_OK) return bs;
-  int kmax = 0;
-  for (const SeqDesc &sd : seqs) kmax = std::max(kmax, sd.kmax);
-  PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk, st,
-               block_tok, tokens_dev, unmask, alpha, mode, masked_left, argmax_out, conf_out,
-               logits_out, &seqs};
+  PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk,
+               flash_tiles, st, block_tok, tokens_dev, unmask, alpha, mode, masked_left,
+               argmax_out, conf_out, logits_out, split_bytes, flash_flops};
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
   p.grid_chunks = std::min((p.grid_chunks + 3) / 4 * 4, c->max_chunks);
   PassKey key;
   memset(&key, 0, sizeof(key));
-  key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.unmask = unmask;
+  key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.flash_tiles = p.flash_tiles;
+  key.unmask = unmask;
   key.mode = mode;
   memcpy(&key.alpha_bits, &alpha, sizeof(float));
   key.kv = st->kv; key.cross = st->cross; key.block_tok = block_tok; key.tokens_dev = tokens_dev;
@@ -569,7 +590,7 @@ blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int
 
 blt_status blt_profile_enable(blt_ctx *c, int32_t family) {
   if (!c) return BLT_EINVAL;
-  if (family != BLT_PROF_OFF && family != BLT_PROF_ATTENTION)
+  if (family != BLT_PROF_OFF && family != BLT_PROF_ATTENTION && family != BLT_PROF_ATTENTION_CAUSAL)
     return fail(c, BLT_EINVAL, "blt_profile_enable: unknown kernel family");
   if (family != BLT_PROF_OFF && c->prof_pool.empty()) {
     c->prof_pool.resize(4096);

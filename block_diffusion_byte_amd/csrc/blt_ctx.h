@@ -28,7 +28,7 @@ struct StageSlot {
 // Everything the kernel sequence of a decoder pass depends on besides the
 // staged descriptors: passes with equal keys replay one HIP graph.
 struct PassKey {
-  int R, S, grid_chunks, unmask, mode;
+  int R, S, grid_chunks, flash_tiles, unmask, mode;
   uint32_t alpha_bits;
   const void *kv, *cross, *block_tok, *tokens_dev, *masked_left, *argmax_out, *conf_out,
       *logits_out;
@@ -94,7 +94,7 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
                       const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs);
 blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1);
 blt_status prof_collect(blt_ctx *c);
-blt_status run_pass(blt_ctx *c, const blt_state *st, const std::vector<RowDesc> &rows,
+blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                     const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,

@@ -18,6 +18,8 @@ constexpr int kAttnChunk = 128;     // keys per split-K attention chunk (aligned
 constexpr int kMaxChunks = 128;     // chunks per sequence the fused merge handles (max_ctx <= 16384)
 constexpr int kMaxBlock = 64;       // block rows per sequence handled by one wave in unmask
 constexpr int kGemvRows = 16;       // rows per GEMV row block; passes with R >= 16 use MFMA (bf16)
+constexpr int kFlashRows = 128;     // rows per workgroup of the causal (flash) attention kernel
+constexpr int kFlashMinRows = 64;   // a bf16 sequence with this many clean rows in a pass takes it
 
 // Token source codes in RowDesc::tok (values >= 0 are literal token ids).
 constexpr int kTokFromBlock = -1;   // block_tok[blk]
@@ -32,7 +34,7 @@ struct RowDesc {
   int32_t lat;    // latent index read by the cross-attention
   int32_t kend;   // the row attends cache rows [0, kend)
   int32_t oidx;   // index into the caller's per-row outputs, -1 for none
-  int32_t pad;
+  int32_t attn_flash;  // 1: its sequence takes the causal kernel (no partials to merge)
 };
 
 // One sequence of a decoder pass.
@@ -44,6 +46,7 @@ struct SeqDesc {
   int32_t blk_row0;      // pass row of its first block row
   int32_t nblk;          // block rows
   int32_t out_b;         // index of the sequence in the caller's batch
+  int32_t attn_flash;    // 1: self-attention by the causal kernel (clean rows only, >= kFlashMinRows)
 };
 
 enum Epilogue { EP_STORE_F32 = 0, EP_RESID = 1, EP_SILU_ACT = 2, EP_STORE_ACT = 3, EP_ROWOFF_F32 = 4 };
@@ -102,11 +105,14 @@ hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const 
 hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
                           hipStream_t s);
-// ev0/ev1 (nullable) are recorded right before and after the partials kernel.
+// ev0/ev1 (nullable) are stamped by the dispatch of the split-K partials
+// kernel, or of the causal kernel when ev_flash is set.  grid_chunks = 0
+// skips the split-K kernel and its merge (every sequence on the causal
+// kernel); flash_tiles = 0 skips the causal kernel.
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
-                            hipEvent_t ev1, hipStream_t s);
+                            int flash_tiles, const RowDesc *rows, int R, float *part, void *a_out,
+                            hipEvent_t ev0, hipEvent_t ev1, bool ev_flash, hipStream_t s);
 bool gemv_supported(bool bf16, int K);
 // report_entropy: conf_out receives each row's entropy instead of its confidence.
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,

@@ -676,7 +676,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
   const int key0 = c * kCK;
-  if (key0 >= sd.kmax) return;
+  if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
@@ -833,6 +833,269 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
     }
     my_kend = rows[sd.row0 + rg + min(lr, nr - 1)].kend;
     __syncthreads();                          // LDS of this row group fully read
+  }
+}
+
+// Causal attention for long runs of clean rows (prompt prefill, KV rebuild):
+// the keys of every row are a prefix [0, kend) of its sequence's cache, so
+// one pass over the keys serves a whole tile of rows with an online softmax
+// (running max and sum per row, the accumulator rescaled when the max grows)
+// and the normalised output is written straight to the activations, with no
+// partials and no merge.
+//
+// Row tiles hold kFlashRows = 128 consecutive rows of a sequence in the pass,
+// 32 per wave in two groups of 16.  Under the causal mask tile i reads about
+// i + 1 key tiles, so workgroup (p, head h, sequence b) takes the pair of row
+// tiles n-1-p and p, which balances the work of the workgroups.  For each row
+// tile it walks the keys below the tile's largest kend in tiles of KT keys
+// staged through LDS (double-buffered: the next tile's loads are in flight
+// during the current tile's products).  Same MFMA formulation as the split-K
+// kernel: S^T = K Q^T leaves each lane with scores of one row, which are
+// already the B operand of O^T += V^T P^T (P split into bf16 hi and lo
+// parts), and the lane's O^T entries belong to that same row, so the softmax
+// bookkeeping is lane-local apart from the row max over the four lane groups
+// (two permlane swaps).  Each K and V operand read from LDS serves both row
+// groups.  Scores are taken in base-2 units (times log2(e) / sqrt(d_h)), so
+// each probability is one fma and one exp2.  A row's result depends only on
+// its own query and kend: keys past kend get probability exactly 0 and leave
+// the row's statistics unchanged, whatever the other rows of the tile read.
+// Cache rows at or past the sequence's kmax are never written and are staged
+// as zeros.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  // max over lanes l, l^16, l^32, l^48 (the four lane groups of a 16-lane row)
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
+                                                    int layer, const SeqDesc *seqs,
+                                                    const RowDesc *rows, void *a_out) {
+  constexpr int KS = DH / 32;                 // k-steps of the score product
+  constexpr int DT = DH / 16;                 // 16-dim output tiles
+  constexpr int KT = DH <= 64 ? 64 : 32;      // keys per LDS tile
+  constexpr int N16 = KT / 16;                // 16-key score tiles per LDS tile
+  constexpr int NJ = KT / 32;                 // 32-key slot groups of the P.V product
+  constexpr int KST = DH + 8;                 // LDS row strides (elements), +16 bytes
+  constexpr int VST = KT + 8;
+  constexpr int NK = KT * DH / 8 / 256;       // 16-byte pieces per thread per tile, K and V each
+  static_assert(NK >= 1 && KT * DH / 8 == NK * 256, "tile must split evenly over 256 threads");
+  static_assert(kFlashRows == 128, "4 waves x 2 groups x 16 rows");
+  __shared__ __align__(16) uint16_t kt_s[2][KT * KST];
+  __shared__ __align__(16) uint16_t vt_s[2][DH * VST];
+  __shared__ int kend_s[kFlashRows];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const SeqDesc sd = seqs[b];
+  if (!sd.attn_flash) return;
+  const int ntile = (sd.nrows + kFlashRows - 1) / kFlashRows;
+  const int pr = (int)blockIdx.x;
+  if (pr >= (ntile + 1) / 2) return;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+  const int d = g.n_heads * DH;
+  const int64_t plane = (int64_t)g.max_ctx * DH;
+  const uint16_t *Kp =
+      (const uint16_t *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
+  const uint16_t *Vt = Kp + (int64_t)g.n_heads * plane;
+  const int kmax = sd.kmax;
+  const float c2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
+
+  // staging: thread t moves NK 16-byte pieces of K ([key][dim]) and of V^T
+  // ([dim][key]) per tile; pieces past kmax become zeros
+  u32x4_t kr[NK], vr[NK];
+  auto load = [&](int tk) {
+    const int key0 = tk * KT;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int i = t + 256 * j;
+      const int kk = i / (DH / 8), kp = i % (DH / 8);
+      kr[j] = *(const u32x4_t *)(Kp + (int64_t)(key0 + kk) * DH + 8 * kp);
+      const int dd = i / (KT / 8), vp = i % (KT / 8);
+      vr[j] = *(const u32x4_t *)(Vt + (int64_t)dd * g.max_ctx + key0 + 8 * vp);
+    }
+  };
+  auto store = [&](int tk, int buf) {
+    const int key0 = tk * KT;
+#pragma unroll
+    for (int j = 0; j < NK; ++j) {
+      const int i = t + 256 * j;
+      const int kk = i / (DH / 8), kp = i % (DH / 8);
+      u32x4_t kv = kr[j];
+      if (key0 + kk >= kmax) kv = u32x4_t{0u, 0u, 0u, 0u};
+      *(u32x4_t *)(&kt_s[buf][kk * KST + 8 * kp]) = kv;
+      const int dd = i / (KT / 8), vp = i % (KT / 8);
+      u32x4_t vv = vr[j];
+      const int k0 = key0 + 8 * vp;
+      if (k0 + 8 > kmax) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t lo = k0 + 2 * e < kmax ? (vv[e] & 0xffffu) : 0u;
+          const uint32_t hi = k0 + 2 * e + 1 < kmax ? (vv[e] & 0xffff0000u) : 0u;
+          vv[e] = lo | hi;
+        }
+      }
+      *(u32x4_t *)(&vt_s[buf][dd * VST + 8 * vp]) = vv;
+    }
+  };
+
+  for (int half = 0; half < 2; ++half) {
+    const int tile = half ? pr : ntile - 1 - pr;
+    if (half && tile >= ntile - 1 - pr) break;   // odd tile count: the middle tile runs alone
+    const int r0 = tile * kFlashRows;
+    const int nr = min(kFlashRows, sd.nrows - r0);
+    if (half) __syncthreads();                   // LDS of the first row tile fully read
+    if (t < kFlashRows) kend_s[t] = rows[sd.row0 + r0 + min(t, nr - 1)].kend;
+    // the lane's rows: 32 w + 16 g + lr of the tile (clamped into the tile's rows)
+    bf16x8_t qb[2][KS];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int row = sd.row0 + r0 + min(32 * w + 16 * gi + lr, nr - 1);
+      const float *qr = q + (int64_t)row * d + h * DH + 8 * lq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const float4 a = *(const float4 *)(qr + 32 * ks), c = *(const float4 *)(qr + 32 * ks + 4);
+        bf16x8_t v;
+        v[0] = (__bf16)a.x; v[1] = (__bf16)a.y; v[2] = (__bf16)a.z; v[3] = (__bf16)a.w;
+        v[4] = (__bf16)c.x; v[5] = (__bf16)c.y; v[6] = (__bf16)c.z; v[7] = (__bf16)c.w;
+        qb[gi][ks] = v;
+      }
+    }
+    __syncthreads();
+    int my_kend[2];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) my_kend[gi] = kend_s[min(32 * w + 16 * gi + lr, nr - 1)];
+    // largest kend of the tile, largest and smallest of the wave's rows
+    int kend_wg = 0, kend_hi = 0, kend_lo = 0x7fffffff;
+    for (int i = 0; i < nr; ++i) {
+      const int k = kend_s[i];
+      kend_wg = max(kend_wg, k);
+      if ((i >> 5) == w) {
+        kend_hi = max(kend_hi, k);
+        kend_lo = min(kend_lo, k);
+      }
+    }
+    const int ntk = (kend_wg + KT - 1) / KT;
+
+    f32x4_t o[2][DT];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) o[gi][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    if (ntk > 0) {
+      load(0);
+      store(0, 0);
+    }
+    __syncthreads();
+    for (int tk = 0; tk < ntk; ++tk) {
+      const int buf = tk & 1;
+      const int key0 = tk * KT;
+      if (tk + 1 < ntk) load(tk + 1);
+      if (key0 < kend_hi) {                   // wave-uniform: some row of the wave reads these keys
+        // S^T for both row groups; every K operand read once
+        f32x4_t acc[2][N16];
+#pragma unroll
+        for (int k16 = 0; k16 < N16; ++k16) {
+          bf16x8_t ka[KS];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            ka[ks] = *(const bf16x8_t *)(&kt_s[buf][(16 * k16 + lr) * KST + 32 * ks + 8 * lq]);
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi) {
+            acc[gi][k16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+              acc[gi][k16] =
+                  __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[ks], qb[gi][ks], acc[gi][k16], 0, 0, 0);
+          }
+        }
+        // acc[g][k16][v]: raw score of key key0 + 16 k16 + 4 lq + v for the
+        // lane's row of group g; masking only where the tile reaches past the
+        // smallest kend of the wave's rows
+        if (key0 + KT > kend_lo) {
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int k16 = 0; k16 < N16; ++k16)
+#pragma unroll
+              for (int v = 0; v < 4; ++v)
+                if (key0 + 16 * k16 + 4 * lq + v >= my_kend[gi]) acc[gi][k16][v] = -INFINITY;
+        }
+        u32x4_t ph[2][NJ], pl[2][NJ];
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          float mt = -INFINITY;
+#pragma unroll
+          for (int k16 = 0; k16 < N16; ++k16)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mt = fmaxf(mt, acc[gi][k16][v]);
+          // key 0 lies in the first tile and every row has kend >= 1, so the
+          // running max is finite from the first tile on; exp2(-inf) = 0
+          const float m_new = fmaxf(m_run[gi], max_lane_groups(mt) * c2);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[gi] - m_new);
+          m_run[gi] = m_new;
+          float ps = 0.f;
+#pragma unroll
+          for (int i = 0; i < KT / 4; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4], c2, -m_new));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4 + 1], c2, -m_new));
+            ps += p0 + p1;
+            const uint32_t hb = f2bf2(p0, p1);
+            ph[gi][i / 8][(i % 8) / 2] = hb;
+            pl[gi][i / 8][(i % 8) / 2] =
+                f2bf2(p0 - __uint_as_float(hb << 16), p1 - __uint_as_float(hb & 0xffff0000u));
+          }
+          l_run[gi] = l_run[gi] * alpha + ps;
+          if (__ballot(alpha != 1.f)) {       // the running max moved for some row of the wave
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt) o[gi][dt] = o[gi][dt] * alpha;
+          }
+        }
+        // O^T += V^T P^T: slot group j holds k-slots 8 lq + i <-> keys
+        // 32 j + 4 lq + i (i < 4) and 32 j + 16 + 4 lq + i - 4; every V operand read once
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            const uint16_t *vrow = &vt_s[buf][(16 * dt + lr) * VST + 32 * j];
+            const uint2 v0 = *(const uint2 *)(vrow + 4 * lq), v1 = *(const uint2 *)(vrow + 16 + 4 * lq);
+            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+#pragma unroll
+            for (int gi = 0; gi < 2; ++gi) {
+              o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  va, __builtin_bit_cast(bf16x8_t, ph[gi][j]), o[gi][dt], 0, 0, 0);
+              o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  va, __builtin_bit_cast(bf16x8_t, pl[gi][j]), o[gi][dt], 0, 0, 0);
+            }
+          }
+      }
+      if (tk + 1 < ntk) store(tk + 1, buf ^ 1);
+      __syncthreads();
+    }
+    // o[g][dt][v]: unnormalised output of the lane's row of group g, dim 16 dt + 4 lq + v
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const float L = sum_lane_groups(l_run[gi]);
+      const int wr = 32 * w + 16 * gi + lr;
+      if (wr < nr) {
+        uint16_t *dst = (uint16_t *)a_out + (int64_t)(sd.row0 + r0 + wr) * d + h * DH + 4 * lq;
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          uint2 pk;
+          pk.x = f2bf2(o[gi][dt][0] / L, o[gi][dt][1] / L);
+          pk.y = f2bf2(o[gi][dt][2] / L, o[gi][dt][3] / L);
+          *(uint2 *)(dst + 16 * dt) = pk;
+        }
+      }
+    }
   }
 }
 
@@ -1015,7 +1278,9 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   using T = typename Act<BF>::T;
   __shared__ float fw[kMaxChunks];
   const int row = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
-  const int nc = (rows[row].kend + kCK - 1) / kCK;
+  const RowDesc rd = rows[row];
+  if (rd.attn_flash) return;                  // written by the causal kernel
+  const int nc = (rd.kend + kCK - 1) / kCK;
   const float *pb = part + ((int64_t)row * n_heads + h) * max_chunks * (DH + 2);
   // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
   const int c0 = min(l, nc - 1), c1 = min(l + 64, nc - 1);
@@ -1293,8 +1558,22 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
-                        int n_seq, int grid_chunks, int max_chunks, const RowDesc *rows, int R,
-                        float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, hipStream_t s) {
+                        int n_seq, int grid_chunks, int max_chunks, int flash_tiles,
+                        const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
+                        hipEvent_t ev1, bool ev_flash, hipStream_t s) {
+  if constexpr (BF) {
+    if (flash_tiles > 0) {
+      const dim3 fg((flash_tiles + 1) / 2, g.n_heads, n_seq);   // pairs of row tiles
+      if (ev0 && ev_flash)
+        hipExtLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
+                              seqs, rows, a_out);
+      else
+        hipLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
+                           a_out);
+    }
+  }
+  if (ev_flash) ev0 = ev1 = nullptr;
+  if (grid_chunks <= 0) return;
   const dim3 grid(grid_chunks, g.n_heads, n_seq);
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
@@ -1318,13 +1597,14 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
-                            hipEvent_t ev1, hipStream_t s) {
+                            int flash_tiles, const RowDesc *rows, int R, float *part, void *a_out,
+                            hipEvent_t ev0, hipEvent_t ev1, bool ev_flash, hipStream_t s) {
+  if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
-  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,  \
-                                  part, a_out, ev0, ev1, s);                                      \
-  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, rows, R,      \
-                              part, a_out, ev0, ev1, s);
+  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks,          \
+                                  flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);      \
+  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, flash_tiles, \
+                              rows, R, part, a_out, ev0, ev1, ev_flash, s);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;

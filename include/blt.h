@@ -156,7 +156,12 @@ blt_status blt_latents_put(blt_ctx *ctx, const blt_state *st, int32_t n, const i
  * Outputs (device, nullable): argmax_out[slot[b]*n_max+j] (greedy byte of the
  * row: lowest id among the largest of logits 0..255), conf_out (its
  * probability), logits_out[(slot[b]*n_max+j)*257 + v] (float32).  At most
- * max_rows rows in total; a sequence with n_rows[b] = 0 is skipped. */
+ * max_rows rows in total; a sequence with n_rows[b] = 0 is skipped.
+ * Self-attention of a bfloat16 sequence with at least 64 rows in the call
+ * runs as one causal (flash) pass over its keys, tiles of 128 rows at a
+ * time; shorter ones take the split-K decode kernel.  Either way a row's
+ * result depends only on its own inputs and on which of the two kernels its
+ * sequence took (the two agree to rounding). */
 blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const int32_t *slot,
                          const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
                          const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
@@ -197,14 +202,20 @@ blt_status blt_verify_accept(blt_ctx *ctx, int32_t batch, const int32_t *slot, i
                              int32_t ld_pred, int32_t *accept_len, int32_t *next_byte);
 
 /* Kernel timing with HIP events on the context's stream (profiling aid).
- * While a family is enabled, every launch of it is bracketed by an event
- * pair.  blt_profile_read synchronises the stream and returns the launches
- * timed so far, their summed duration and the algorithmic bytes they must
- * move: for BLT_PROF_ATTENTION, the key and value rows of the cache that the
- * pass's rows read (sum over sequences of kmax * 2 * d_model * element size;
- * kmax = the largest key count of the sequence's rows).  reset != 0 clears
- * the totals.  Enabling or disabling collects pending events first. */
-typedef enum { BLT_PROF_OFF = 0, BLT_PROF_ATTENTION = 1 } blt_prof_family;
+ * While a family is enabled, every launch of it is stamped by its own
+ * dispatch (start and end events).  blt_profile_read synchronises the stream
+ * and returns the launches timed so far, their summed duration and the
+ * algorithmic work they must do, in `bytes`:
+ *  - BLT_PROF_ATTENTION, the split-K self-attention kernel of decode passes:
+ *    bytes of the key and value rows of the cache its sequences read (sum over
+ *    sequences of kmax * 2 * d_model * element size; kmax = the largest key
+ *    count of the sequence's rows);
+ *  - BLT_PROF_ATTENTION_CAUSAL, the causal (flash) self-attention kernel of
+ *    long clean-row passes (prefill): floating-point operations, sum over its
+ *    rows of 4 * d_model * kend (the multiply-adds of QK^T and PV).
+ * reset != 0 clears the totals.  Enabling or disabling collects pending
+ * events first. */
+typedef enum { BLT_PROF_OFF = 0, BLT_PROF_ATTENTION = 1, BLT_PROF_ATTENTION_CAUSAL = 2 } blt_prof_family;
 blt_status blt_profile_enable(blt_ctx *ctx, int32_t family);
 blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, double *bytes,
                             int32_t reset);

@@ -1,0 +1,138 @@
+"""GPU parity of long clean-row passes (prompt prefill, KV rebuild) against the
+CPU oracle.
+
+A bf16 sequence with at least 64 clean rows in a pass takes the causal
+(flash) attention kernel; shorter ones and block passes take the split-K
+kernel.  These tests append ragged runs of rows (tiles of 64 with a partial
+last tile, a cached prefix before the run, two sequences of different lengths
+in one pass, and a pass that mixes both kernels) and compare every row's
+logits with the float64 oracle's cached decoder (bf16 tolerance: 2e-2
+absolute), and every greedy byte whose oracle top-2 gap is outside the
+rounding band.
+"""
+import numpy as np
+import pytest
+
+import bltgen
+from oracle import cache, patcher
+from tests.gpu_util import BF16_ABS, decoder_for, logits_ok, oracle_inputs, say
+
+pytestmark = pytest.mark.gpu
+
+MINI = bltgen.WORKLOADS[1].replace(name="mini_prefill_bf16", n_layers=2, d_model=256, n_heads=4,
+                                   d_ffn=1024, d_global=512, prompt_len=600, prompt_patches=150,
+                                   n_gen=8, block=4, batch=2)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import block_diffusion_byte_amd as blt
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    blt.lib()
+    yield
+
+
+class _Seq:
+    """One sequence: its oracle cached decoder, bytes and causal targets."""
+
+    def __init__(self, wl, w, s):
+        W, inp, inp64 = oracle_inputs(wl, w, seq=s)
+        self.inp = inp
+        self.x = [int(b) for b in inp["prompt"]]
+        patch, ends = patcher.segment(self.x, inp["prompt_patches"], inp["salt"])
+        self.tau = [patcher.causal_target(patch, ends, i) for i in range(len(self.x) - 1)]
+        self.oracle = cache.CachedDecoder(W, wl, inp64["latents"], len(self.x) + 8)
+
+    def expect(self, start, n):
+        return self.oracle.run(self.x[start:start + n], start, self.tau[start:start + n], n)
+
+
+def _check(got, ref, tag):
+    ok, err, tol = logits_ok(got, ref, "bf16")
+    # greedy bytes wherever the oracle's top-2 gap clears twice the tolerance
+    top2 = np.sort(ref[:, :256], axis=1)[:, -2:]
+    sure = (top2[:, 1] - top2[:, 0]) > 2 * BF16_ABS
+    am_ref = np.argmax(ref[:, :256], axis=1)
+    am_got = np.argmax(got[:, :256], axis=1)
+    say(f"{tag}: {len(ref)} rows, worst logit err {err:.3g} (tol {tol:.3g}), "
+        f"{int(sure.sum())} greedy bytes compared")
+    assert ok, f"{tag}: logits err {err} > {tol}"
+    assert np.array_equal(am_ref[sure], am_got[sure]), tag
+
+
+def _append(blt, torch, dec, seqs, plan, z):
+    """One kv_append pass: plan = [(slot, start, n)]; returns per-slot logits."""
+    n_max = max(n for _, _, n in plan)
+    slots = [s for s, _, _ in plan]
+    lat = np.zeros((len(plan), n_max), dtype=np.int64)
+    byt = np.zeros((len(plan), n_max), dtype=np.int64)
+    for i, (s, st, n) in enumerate(plan):
+        lat[i, :n] = seqs[s].tau[st:st + n]
+        byt[i, :n] = seqs[s].x[st:st + n]
+    blt.blt_kv_append(dec.ctx, dec.state, slots, [st for _, st, _ in plan], [n for _, _, n in plan],
+                      n_max, lat, bytes_=byt, logits_out=z)
+    torch.cuda.synchronize()
+    out = {}
+    for s, st, n in plan:
+        base = s * n_max
+        out[s] = z[base * 257:(base + n) * 257].view(n, 257).cpu().numpy().astype(np.float64)
+    return out
+
+
+def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes():
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = MINI
+    w = bltgen.make_weights(wl, gains="random")
+    seqs = [_Seq(wl, w, s) for s in range(2)]
+    dec = decoder_for(wl, w, max_batch=2, max_rows=512)
+    try:
+        for s in range(2):
+            table = torch.from_numpy(seqs[s].inp["latents"]).to("cuda:0", dec.torch_dtype)
+            blt.blt_latents_put(dec.ctx, dec.state, [s] * wl.n_latents, list(range(wl.n_latents)),
+                                table, 0)
+        z = torch.zeros(2 * 512 * 257, device="cuda:0")
+        # pass 1: both sequences on the causal kernel, 150 rows (two full
+        # tiles and a partial one) and 70 rows (one full tile and 6 rows)
+        got = _append(blt, torch, dec, seqs, [(0, 0, 150), (1, 0, 70)], z)
+        _check(got[0], seqs[0].expect(0, 150), "seq 0 rows 0..149 (causal kernel)")
+        _check(got[1], seqs[1].expect(0, 70), "seq 1 rows 0..69 (causal kernel)")
+        # pass 2: 229 rows after a 150-row prefix (causal kernel) beside
+        # 10 rows of the other sequence (split-K kernel) in the same pass
+        got = _append(blt, torch, dec, seqs, [(0, 150, 229), (1, 70, 10)], z)
+        _check(got[0], seqs[0].expect(150, 229), "seq 0 rows 150..378 after a prefix (causal kernel)")
+        _check(got[1], seqs[1].expect(70, 10), "seq 1 rows 70..79 (split-K kernel, mixed pass)")
+        # pass 3: exactly one tile; then a rollback that rewrites the tail
+        got = _append(blt, torch, dec, seqs, [(1, 80, 64)], z)
+        _check(got[1], seqs[1].expect(80, 64), "seq 1 rows 80..143 (one full tile)")
+        seqs[0].oracle.truncate(300)
+        got = _append(blt, torch, dec, seqs, [(0, 300, 299)], z)
+        _check(got[0], seqs[0].expect(300, 299), "seq 0 rows 300..598 after truncation to 300")
+    finally:
+        dec.close()
+
+
+def test_causal_kernel_matches_split_k_pass_by_pass():
+    """The same rows through both kernels (one 200-row pass vs passes of 50
+    rows): the logits agree within the bf16 tolerance."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = MINI
+    w = bltgen.make_weights(wl, gains="random")
+    seqs = [_Seq(wl, w, 0)]
+    res = []
+    for chunk in (200, 50):
+        dec = decoder_for(wl, w, max_batch=2, max_rows=256)
+        try:
+            table = torch.from_numpy(seqs[0].inp["latents"]).to("cuda:0", dec.torch_dtype)
+            blt.blt_latents_put(dec.ctx, dec.state, [0] * wl.n_latents, list(range(wl.n_latents)),
+                                table, 0)
+            z = torch.zeros(2 * 256 * 257, device="cuda:0")
+            parts = [_append(blt, torch, dec, seqs, [(0, c0, chunk)], z)[0] for c0 in range(0, 200, chunk)]
+            res.append(np.concatenate(parts))
+        finally:
+            dec.close()
+    err = np.abs(res[0] - res[1]).max()
+    say(f"causal kernel vs split-K over 200 rows: max logit difference {err:.3g}")
+    assert err <= BF16_ABS
