@@ -4,11 +4,15 @@
   * unmask_commit: confidence-threshold unmasking with the forced fallback,
     or one-step filling;
   * entropy / unmask_commit_entropy: entropy-bounded (EB) unmasking;
-  * verify_accept: the greedy exact-match verification of a draft.
+  * verify_accept: the greedy exact-match verification of a draft;
+  * uniform / sample_top_p: temperature and top-p (nucleus) sampling of a
+    position's byte, the stochastic variant the pages pair with EB sampling.
 """
 from __future__ import annotations
 
 import numpy as np
+
+from . import patcher
 
 MASK = 256
 
@@ -119,3 +123,60 @@ def verify_accept(draft, pred):
     while a < r and int(draft[a]) == int(pred[a]):
         a += 1
     return a, int(pred[a])
+
+
+def uniform(seed, counter):
+    """A uniform number in [0, 1) with 24 random bits for draw ``counter``
+    (>= 0) of the stream ``seed``: the top 24 bits of output counter + 1 of
+    SplitMix64 started from state ``seed`` (Steele, Lea and Flood, 2014),
+    divided by 2^24 (exact in float32 and float64)."""
+    return (patcher.splitmix64_nth(seed, counter + 1) >> 40) / float(1 << 24)
+
+
+def sample_top_p(z, temperature, top_p, u):
+    """Temperature and top-p (nucleus) sampling of one masked position.
+
+    pytorch.kr summary, "block unmasking strategies": EB sampling can be
+    combined with top-p sampling to control the diversity of the output; the
+    pages give no further detail, so the plainest reading of nucleus
+    sampling is taken:
+      p_b = softmax(z_b / temperature) over bytes 0..255 ([MASK] excluded);
+      bytes ranked by p descending, equal probabilities by byte id;
+      the nucleus is the shortest prefix of that ranking whose mass reaches
+      top_p (a byte belongs to it iff the mass ranked before it is below
+      top_p; bytes of probability 0 never do);
+      with c = u * (mass of the nucleus), the chosen byte is the last byte
+      of the nucleus, in rank order, whose preceding mass is <= c (the byte
+      whose interval [before, before + p) of the nucleus holds c).
+    Temperature and top-p shape only the draw: the position's confidence is
+    the model's probability of the drawn byte and its entropy that of the
+    model's distribution (temperature 1, as in greedy decoding), so the
+    unmask rules judge positions the same way and the limits top_p -> 0 or
+    temperature -> 0 are greedy decoding.
+    Returns (byte, model probability of the byte, model entropy in nats,
+    margin): margin is the smallest distance, in probability, between a
+    quantity that decides the draw and its threshold (c to the chosen
+    interval's ends, and the preceding mass of the nucleus' last byte and of
+    the first byte left out to top_p); a computation whose probabilities are
+    off by less than the margin draws the same byte.
+    """
+    z = np.asarray(z, dtype=np.float64)[:256]
+    q = np.exp(z - z.max())
+    q = q / q.sum()
+    nz = q[q > 0]
+    ent = float(-(nz * np.log(nz)).sum())
+    y = z / float(temperature)
+    e = np.exp(y - y.max())
+    p = e / e.sum()
+    order = sorted(range(256), key=lambda b: (-p[b], b))
+    before = np.concatenate([[0.0], np.cumsum([p[b] for b in order])[:-1]])
+    inside = [i for i in range(256) if before[i] < top_p and p[order[i]] > 0]
+    n = len(inside)                     # the nucleus is order[:n]
+    mass = float(sum(p[order[i]] for i in range(n)))
+    c = u * mass
+    k = max(i for i in range(n) if before[i] <= c)
+    b = order[k]
+    margin = min(c - before[k], before[k] + p[b] - c, top_p - before[n - 1])
+    if n < 256:
+        margin = min(margin, before[n] - top_p)
+    return b, float(q[b]), ent, float(margin)

@@ -377,6 +377,88 @@ def test_splitmix64_reference_vector():
     assert [patcher.splitmix64_nth(g["seed"], i + 1) for i in range(3)] == [int(v, 16) for v in g["outputs"]]
 
 
+def test_uniform_draws_are_published_splitmix64_outputs():
+    """decide.uniform(seed, k) is the top 24 bits of SplitMix64 output k + 1,
+    over 2^24: pinned to the published outputs from state 0."""
+    with open(os.path.join(GOLDEN, "splitmix64.json")) as f:
+        g = json.load(f)
+    for k, v in enumerate(g["outputs"]):
+        assert decide.uniform(g["seed"], k) == (int(v, 16) >> 40) / 2.0 ** 24
+    u = [decide.uniform(7, k) for k in range(4096)]
+    assert min(u) >= 0.0 and max(u) < 1.0 and abs(np.mean(u) - 0.5) < 0.02
+
+
+def _logits_of(p):
+    z = np.full(257, -1e4)
+    for b, q in p.items():
+        z[b] = np.log(q)
+    return z
+
+
+def test_top_p_worked_distributions():
+    """Dyadic probabilities make every interval boundary exact: with p =
+    (1/2, 1/4, 1/8, 1/8) on bytes 0..3, u in [0, 1/2) picks 0, [1/2, 3/4)
+    picks 1, and so on; top_p = 0.7 keeps bytes 0 and 1 (the mass before
+    byte 2 is 3/4 >= 0.7), whose mass 3/4 scales u.  Equal probabilities
+    rank by byte id.  [MASK] never takes part."""
+    z = _logits_of({0: 0.5, 1: 0.25, 2: 0.125, 3: 0.125})
+    for u, full, cut in [(0.0, 0, 0), (0.4999, 0, 0), (0.5, 1, 0), (0.6666, 1, 0), (0.6667, 1, 1),
+                         (0.7499, 1, 1), (0.75, 2, 1), (0.8749, 2, 1), (0.875, 3, 1), (0.9999, 3, 1)]:
+        assert decide.sample_top_p(z, 1.0, 1.0, u)[0] == full, u
+        assert decide.sample_top_p(z, 1.0, 0.7, u)[0] == cut, u
+    b, pb, ent, _ = decide.sample_top_p(z, 1.0, 1.0, 0.8)
+    assert b == 2 and abs(pb - 0.125) < 1e-12 and abs(ent - 1.75 * np.log(2)) < 1e-9
+    # temperature 1/2 squares and renormalises the probabilities for the draw
+    # (0.5^2, 0.25^2, 2 x 0.125^2 over 11/32: 8/11, 2/11, 1/22, 1/22) but the
+    # confidence and entropy stay the model's
+    for u, want in [(0.72, 0), (0.73, 1), (0.9, 1), (0.91, 2), (0.954, 2), (0.955, 3)]:
+        b, pb, ent, _ = decide.sample_top_p(z, 0.5, 1.0, u)
+        assert b == want, u
+        assert abs(pb - [0.5, 0.25, 0.125, 0.125][b]) < 1e-12 and abs(ent - 1.75 * np.log(2)) < 1e-9
+    tie = _logits_of({200: 0.25, 3: 0.25, 9: 0.25, 7: 0.25})
+    tie[256] = 50.0                                   # a huge [MASK] logit changes nothing
+    assert [decide.sample_top_p(tie, 1.0, 1.0, u)[0] for u in (0.1, 0.3, 0.6, 0.9)] == [3, 7, 9, 200]
+    assert [decide.sample_top_p(tie, 1.0, 0.5, u)[0] for u in (0.1, 0.6)] == [3, 7]
+
+
+def test_top_p_limits_are_greedy():
+    """A vanishing top_p keeps only the most probable byte (lowest id on
+    ties), and a vanishing temperature puts all mass on it: both give the
+    greedy byte for every u."""
+    rng = np.random.default_rng(5)
+    for _ in range(20):
+        z = rng.normal(0, 2, 257)
+        g = decide.byte_choice(z)[0]
+        for u in (0.0, 0.37, 0.999):
+            assert decide.sample_top_p(z, 1.0, 1e-9, u)[0] == g
+            assert decide.sample_top_p(z, 1e-3, 1.0, u)[0] == g
+    z = np.zeros(257)
+    assert [decide.sample_top_p(z, 1.0, 1e-9, u)[0] for u in (0.0, 0.99)] == [0, 0]
+
+
+@pytest.mark.parametrize("top_p", [1.0, 0.9, 0.5])
+def test_top_p_nucleus_and_frequencies(top_p):
+    """On a grid of u the sampler only visits the nucleus -- the smallest set
+    of most probable bytes whose mass reaches top_p, found here by a sort of
+    (-p, byte id) -- and each nucleus byte with frequency p_b / mass(nucleus)
+    to within the grid step."""
+    rng = np.random.default_rng(11)
+    z = rng.normal(0, 1.5, 257)
+    y = z[:256] / 0.8
+    p = np.exp(y - y.max())
+    p /= p.sum()
+    rank = np.lexsort((np.arange(256), -p))
+    k = int(np.searchsorted(np.cumsum(p[rank]), top_p - 1e-15)) + 1
+    nucleus = rank[:min(k, 256)]
+    mass = p[nucleus].sum()
+    n = 8192
+    hits = np.zeros(256)
+    for i in range(n):
+        hits[decide.sample_top_p(z, 0.8, top_p, (i + 0.5) / n)[0]] += 1
+    assert set(np.flatnonzero(hits)) <= set(nucleus.tolist())
+    assert np.abs(hits[nucleus] / n - p[nucleus] / mass).max() <= 1.0 / n + 1e-12
+
+
 def test_targets_worked_example():
     with open(os.path.join(GOLDEN, "targets_example.json")) as f:
         g = json.load(f)
@@ -450,6 +532,24 @@ def test_blt_d_entropy_bound_extremes(tiny):
         assert p["entropy"][p["chosen"][0]] == min(p["entropy"][j] for j in masked)
     ref = loops.masked_row_greedy(W, wl, inp, 12)
     assert loops.blt_d(W, wl, inp, 12, 1, 0.5, unmask="entropy").out == ref
+
+
+def test_sampled_blt_d_limits_and_determinism(tiny):
+    """Sampled BLT-D: a vanishing top_p or temperature is greedy BLT-D (same
+    bytes, same passes) under every unmask rule; a fixed seed reproduces the
+    run; the draws follow the counter layout (pass d, position j -> d*64+j)."""
+    wl, W, inp = tiny
+    for mode, alpha in (("threshold", 0.7), ("entropy", 2.0), ("one_step", 0.0)):
+        g = loops.blt_d(W, wl, inp, 24, 4, alpha, unmask=mode)
+        for smp in ((1.0, 1e-9, 3), (1e-4, 1.0, 4)):
+            r = loops.blt_d(W, wl, inp, 24, 4, alpha, unmask=mode, sampling=smp)
+            assert r.out == g.out and r.n_dec == g.n_dec, (mode, smp)
+    a = loops.blt_d(W, wl, inp, 24, 4, 2.0, unmask="entropy", sampling=(1.0, 0.9, 99), trace=True)
+    b = loops.blt_d(W, wl, inp, 24, 4, 2.0, unmask="entropy", sampling=(1.0, 0.9, 99))
+    g = loops.blt_d(W, wl, inp, 24, 4, 2.0, unmask="entropy")
+    assert a.out == b.out and a.out != g.out
+    for d, rec in enumerate(a.passes):
+        assert rec["u"] == [decide.uniform(99, d * loops.MAX_BLOCK + j) for j in range(4)]
 
 
 def test_blt_d_peaked_head_commits_several_per_pass():
