@@ -62,6 +62,8 @@ def parse():
                     help="only run a plain device-to-device copy of MIB MiB ten times (the "
                          "reference kernel for scaling HBM traffic counters) and exit")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--max-rows", type=int, default=0,
+                    help="rows per decoder pass (default: the whole prompt, so prefill is one pass)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every decoder pass directly instead of replaying HIP graphs")
     return ap.parse_args()
@@ -149,7 +151,7 @@ def main():
     inps = [bltgen.make_sequence_inputs(wl, b) for b in range(wl.batch)]
     # one prefill pass per prompt (the causal kernel wants long passes), and
     # room for the largest decode pass
-    max_rows = max(1024, wl.batch * (2 * wl.block + 2), wl.prompt_len)
+    max_rows = args.max_rows or max(1024, wl.batch * (2 * wl.block + 2), wl.prompt_len)
     dec = blt.Decoder(w, n_layers=wl.n_layers, d_model=wl.d_model, n_heads=wl.n_heads,
                       d_ffn=wl.d_ffn, d_global=wl.d_global, dtype=wl.dtype, max_batch=wl.batch,
                       max_ctx=wl.max_ctx, max_latents=wl.n_latents, max_rows=max_rows,

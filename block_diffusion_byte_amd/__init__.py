@@ -20,7 +20,7 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libblt.so")
 
-BLT_OK, BLT_EINVAL, BLT_ECAPACITY, BLT_EDTYPE, BLT_EHIP = 0, -1, -2, -3, -4
+BLT_OK, BLT_EINVAL, BLT_ECAPACITY, BLT_EDTYPE, BLT_EHIP, BLT_ENOTIMPL = 0, -1, -2, -3, -4, -5
 BLT_F32, BLT_BF16 = 0, 1
 BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP, BLT_UNMASK_ENTROPY = 0, 1, 2
 BLT_BLOCK_BIDIR, BLT_BLOCK_CAUSAL = 0, 1
@@ -76,7 +76,12 @@ class blt_params(C.Structure):
 
 class blt_policy_args(C.Structure):
     _fields_ = [("policy", C.c_int32), ("block", C.c_int32), ("alpha", C.c_float),
-                ("unmask", C.c_int32), ("block_mask", C.c_int32), ("n_gen", C.c_int32)]
+                ("unmask", C.c_int32), ("block_mask", C.c_int32), ("n_gen", C.c_int32),
+                ("temperature", C.c_float), ("top_p", C.c_float), ("seed", C.c_uint64)]
+
+
+class blt_sampling(C.Structure):
+    _fields_ = [("temperature", C.c_float), ("top_p", C.c_float), ("seed", C.c_uint64)]
 
 
 _lib = None
@@ -98,7 +103,7 @@ def lib():
             "blt_latents_put": [P, P, I32, P, P, P, I64],
             "blt_kv_append": [P, P, I32, P, P, P, I32, P, P, P, P, P, P],
             "blt_decode_block_step": [P, P, I32, P, P, P, I32, P, P, P, I32, P, F, I32, I32,
-                                      P, P, P, P],
+                                      P, P, P, P, P, P],
             "blt_verify_accept": [P, I32, P, I32, P, I32, P, I32, P, P],
             "blt_bw_model": [P, P, P, P],
             "blt_session_create": [P, P, I32, P, P, P, P, P, P, I32, P],
@@ -185,8 +190,17 @@ def blt_kv_append(ctx, state, slot, start_pos, n_rows, n_max, lat_idx, bytes_=No
 def blt_decode_block_step(ctx, state, slot, start_pos, block_tok, B, block_lat, alpha,
                           mode=BLT_UNMASK_THRESHOLD, mask=BLT_BLOCK_BIDIR, n_append=None,
                           n_append_max=0, append_bytes=None, append_lat=None, argmax_out=None,
-                          conf_out=None, logits_out=None, masked_left=None):
+                          conf_out=None, logits_out=None, masked_left=None, sampling=None,
+                          draw=None):
+    """sampling: None (greedy) or (temperature, top_p, seed); draw: one draw
+    index per sequence (required with sampling)."""
     s, sp = _i32(slot)
+    smp = smpp = dr = drp = None
+    if sampling is not None:
+        smp = blt_sampling(C.c_float(sampling[0]), C.c_float(sampling[1]), int(sampling[2]))
+        smpp = C.byref(smp)
+    if draw is not None:
+        dr, drp = _i32(draw)
     st, stp = _i32(start_pos)
     bl, blp = _i32(block_lat)
     keep = []
@@ -199,7 +213,7 @@ def blt_decode_block_step(ctx, state, slot, start_pos, block_tok, B, block_lat, 
     _check("blt_decode_block_step", lib().blt_decode_block_step(
         ctx, C.byref(state), len(s), sp, stp, nap, n_append_max, abp, alp, _ptr(block_tok), B,
         blp, C.c_float(alpha), mode, mask, _ptr(argmax_out), _ptr(conf_out), _ptr(logits_out),
-        _ptr(masked_left)), ctx)
+        _ptr(masked_left), smpp, drp), ctx)
 
 
 def blt_verify_accept(ctx, r, draft, ld_draft, pred, ld_pred, accept_len, next_byte, slot=None,
@@ -257,8 +271,8 @@ def blt_session_prefill(ctx, sess):
 
 
 def blt_session_generate(ctx, sess, policy, block, alpha, n_gen, unmask=BLT_UNMASK_THRESHOLD,
-                         block_mask=BLT_BLOCK_BIDIR):
-    a = blt_policy_args(policy, block, alpha, unmask, block_mask, n_gen)
+                         block_mask=BLT_BLOCK_BIDIR, temperature=0.0, top_p=1.0, seed=0):
+    a = blt_policy_args(policy, block, alpha, unmask, block_mask, n_gen, temperature, top_p, seed)
     _check("blt_session_generate", lib().blt_session_generate(sess, C.byref(a)), ctx)
 
 

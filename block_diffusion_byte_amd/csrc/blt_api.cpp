@@ -150,6 +150,8 @@ struct PassLaunch {
   float *conf_out, *logits_out;
   double split_bytes;                // per layer: K and V rows the split-K kernel's sequences read
   double flash_flops;                // per layer: the causal kernel's QK^T and PV flops
+  bool sample;                       // block rows draw their bytes (smp)
+  SampleArgs smp;
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
@@ -217,7 +219,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
   HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
   HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, c->ent_ws,
                            p.unmask && p.mode == BLT_UNMASK_ENTROPY, p.argmax_out,
-                           p.conf_out, p.logits_out, s));
+                           p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s));
   if (p.unmask)
     HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, c->ent_ws,
                              (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
@@ -238,7 +240,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                     std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
-                    float *logits_out) {
+                    float *logits_out, const blt_sampling *smp) {
   // Attention path per sequence, from its own rows only: a bf16 sequence
   // whose rows in the pass are all clean (no block) and number at least
   // kFlashMinRows takes the causal kernel; every other one the split-K kernel.
@@ -265,7 +267,9 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   if (bs != BLT_OK) return bs;
   PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk,
                flash_tiles, st, block_tok, tokens_dev, unmask, alpha, mode, masked_left,
-               argmax_out, conf_out, logits_out, split_bytes, flash_flops};
+               argmax_out, conf_out, logits_out, split_bytes, flash_flops, smp != nullptr,
+               SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
+                          smp ? smp->seed : 0}};
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
@@ -276,6 +280,10 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   key.unmask = unmask;
   key.mode = mode;
   memcpy(&key.alpha_bits, &alpha, sizeof(float));
+  key.sample = p.sample;
+  memcpy(&key.temp_bits, &p.smp.temperature, sizeof(float));
+  memcpy(&key.top_p_bits, &p.smp.top_p, sizeof(float));
+  key.seed = p.smp.seed;
   key.kv = st->kv; key.cross = st->cross; key.block_tok = block_tok; key.tokens_dev = tokens_dev;
   key.masked_left = masked_left; key.argmax_out = argmax_out; key.conf_out = conf_out;
   key.logits_out = logits_out;
@@ -504,14 +512,14 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
       if (li < 0 || li >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_kv_append: latent index beyond max_latents");
       const int dj = slot[b] * n_max + j;  // device arrays are indexed by slot
       RowDesc rd{slot[b], s0 + j, bytes ? (int)bytes[(size_t)b * n_max + j] : kTokFromDev, dj, li,
-                 s0 + j + 1, dj, 0};
+                 s0 + j + 1, dj, 0, -1};
       rows.push_back(rd);
     }
     seqs.push_back(sd);
   }
   if (rows.empty()) return BLT_OK;
   return run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
-                  conf_out, logits_out);
+                  conf_out, logits_out, nullptr);
 }
 
 blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
@@ -521,7 +529,8 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
                                  int32_t *block_tok, int32_t B, const int32_t *block_lat,
                                  float alpha, blt_unmask mode, blt_block_mask mask,
                                  int32_t *argmax_out, float *conf_out, float *logits_out,
-                                 int32_t *masked_left) {
+                                 int32_t *masked_left, const blt_sampling *sampling,
+                                 const int32_t *draw) {
   if (!c) return BLT_EINVAL;
   const blt_config &g = c->cfg;
   static const char *fn = "blt_decode_block_step";
@@ -538,6 +547,14 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
     return fail(c, BLT_EINVAL, "blt_decode_block_step: alpha must be finite (an entropy bound: >= 0, may be +inf)");
   if (n_append_max < 0 || (n_append_max > 0 && (!n_append || !append_bytes || !append_lat)))
     return fail(c, BLT_EINVAL, "blt_decode_block_step: bad append arguments");
+  if (sampling) {
+    if (!(sampling->temperature > 0.f) || !isfinite(sampling->temperature) ||
+        !(sampling->top_p > 0.f && sampling->top_p <= 1.f) || !draw)
+      return fail(c, BLT_EINVAL, "blt_decode_block_step: sampling needs temperature > 0, 0 < top_p <= 1 and draw");
+    for (int b = 0; b < batch; ++b)
+      if (draw[b] < 0 || (int64_t)draw[b] * kMaxBlock + kMaxBlock > INT32_MAX)
+        return fail(c, BLT_EINVAL, "blt_decode_block_step: draw out of range");
+  }
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
   for (int b = 0; b < batch; ++b) {
@@ -554,17 +571,18 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
       const int li = append_lat[(size_t)b * n_append_max + j];
       if (li < 0 || li >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: latent index beyond max_latents");
       rows.push_back(RowDesc{slot[b], s0 + j, (int)append_bytes[(size_t)b * n_append_max + j], 0, li,
-                             s0 + j + 1, -1, 0});
+                             s0 + j + 1, -1, 0, -1});
     }
     for (int j = 0; j < B; ++j) {
       const int pos = s0 + na + j;
       rows.push_back(RowDesc{slot[b], pos, kTokFromBlock, slot[b] * B + j, bl,
-                             mask == BLT_BLOCK_CAUSAL ? pos + 1 : (int)end, slot[b] * B + j, 0});
+                             mask == BLT_BLOCK_CAUSAL ? pos + 1 : (int)end, slot[b] * B + j, 0,
+                             sampling ? draw[b] * kMaxBlock + j : -1});
     }
     seqs.push_back(sd);
   }
   return run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, (int)mode,
-                  masked_left, argmax_out, conf_out, logits_out);
+                  masked_left, argmax_out, conf_out, logits_out, sampling);
 }
 
 blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int32_t r,

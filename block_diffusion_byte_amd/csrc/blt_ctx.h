@@ -28,8 +28,9 @@ struct StageSlot {
 // Everything the kernel sequence of a decoder pass depends on besides the
 // staged descriptors: passes with equal keys replay one HIP graph.
 struct PassKey {
-  int R, S, grid_chunks, flash_tiles, unmask, mode;
-  uint32_t alpha_bits;
+  int R, S, grid_chunks, flash_tiles, unmask, mode, sample;
+  uint32_t alpha_bits, temp_bits, top_p_bits;
+  uint64_t seed;
   const void *kv, *cross, *block_tok, *tokens_dev, *masked_left, *argmax_out, *conf_out,
       *logits_out;
   bool operator==(const PassKey &o) const { return memcmp(this, &o, sizeof(PassKey)) == 0; }
@@ -95,8 +96,8 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
 blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1);
 blt_status prof_collect(blt_ctx *c);
 blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
-                    const std::vector<SeqDesc> &seqs, const int32_t *block_tok,
+                    std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
-                    float *logits_out);
+                    float *logits_out, const blt_sampling *smp);
 }  // namespace blt

@@ -35,6 +35,13 @@ struct RowDesc {
   int32_t kend;   // the row attends cache rows [0, kend)
   int32_t oidx;   // index into the caller's per-row outputs, -1 for none
   int32_t attn_flash;  // 1: its sequence takes the causal kernel (no partials to merge)
+  int32_t ctr;    // sampled passes: the row's draw number (block rows), -1: no draw
+};
+
+// Temperature / top-p sampling of a pass's block rows (temperature > 0).
+struct SampleArgs {
+  float temperature, top_p;
+  uint64_t seed;    // stream of the row's sequence: seed + slot
 };
 
 // One sequence of a decoder pass.
@@ -115,9 +122,11 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             hipEvent_t ev0, hipEvent_t ev1, bool ev_flash, hipStream_t s);
 bool gemv_supported(bool bf16, int K);
 // report_entropy: conf_out receives each row's entropy instead of its confidence.
+// smp (nullable): rows with ctr >= 0 draw their byte by temperature / top-p
+// sampling; confidence and entropy stay those of the model's distribution.
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
-                         float *conf_out, float *logits_out, hipStream_t s);
+                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s);
 // mode: a blt_unmask value; alpha: the confidence threshold or the entropy bound.
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok,

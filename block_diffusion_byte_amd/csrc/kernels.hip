@@ -1375,6 +1375,98 @@ __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDes
     for (int j = l; j < kVocab; j += 64) logits_out[(int64_t)oidx * kVocab + j] = z[j];
 }
 
+// Sampled decisions (temperature / top-p, the stochastic variant paired
+// with EB sampling): one workgroup per row, thread j = byte j.  The greedy
+// byte, confidence and entropy are those of k_decide (model distribution);
+// a row with a draw number ctr >= 0 then takes instead the byte drawn from
+// the nucleus of softmax(z / T): with e_j = exp((z_j - max) / T), the mass
+// ranked before byte j (larger e, or equal e and lower id) is summed in
+// byte order, the nucleus is the bytes with e_j > 0 whose preceding mass is
+// below top_p * sum(e), and the draw is the nucleus byte of largest rank
+// whose preceding mass is <= u * (nucleus mass).  u is the top 24 bits of
+// SplitMix64 output ctr + 1 from state seed + slot (Steele, Lea and Flood,
+// 2014), over 2^24.  Its confidence is the model probability of the drawn
+// byte.
+__device__ __forceinline__ uint64_t splitmix64_nth(uint64_t seed, uint64_t n) {
+  uint64_t x = seed + 0x9E3779B97F4A7C15ull * n;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
+
+// Sum and max over the 256 threads: each wave, then the four waves in order.
+__device__ __forceinline__ float block_sum256(float v, float *red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return (red[0] + red[1]) + (red[2] + red[3]);
+}
+__device__ __forceinline__ float block_max256(float v, float *red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__global__ __launch_bounds__(256) void k_decide_sample(const float *logits, const RowDesc *rows,
+                                                      int32_t *argmax_ws, float *conf_ws,
+                                                      float *ent_ws, int report_entropy,
+                                                      int32_t *argmax_out, float *conf_out,
+                                                      float *logits_out, SampleArgs smp) {
+  __shared__ float ew[256];
+  __shared__ float red[4];
+  __shared__ float pick_e;
+  const int r = blockIdx.x, t = threadIdx.x;
+  const RowDesc rd = rows[r];
+  const float *zr = logits + (int64_t)r * kVocab;
+  const float z = zr[t];
+  // greedy byte: the largest logit, lowest id on ties
+  const float best = block_max256(z, red);
+  const float bi = block_max256(z == best ? -(float)t : -INFINITY, red);
+  int choice = (int)-bi;
+  const float x = z - best, e = expf(x);
+  const float s = block_sum256(e, red);
+  const float tz = block_sum256(e * x, red);
+  const float ent = logf(s) - tz / s;
+  float conf = 1.f / s;
+  if (rd.ctr >= 0) {
+    const float eT = expf(x / smp.temperature);
+    ew[t] = eT;
+    const float sT = block_sum256(eT, red);   // its barriers also publish ew
+    float before = 0.f;
+    int rank = 0;
+    for (int k = 0; k < 256; ++k) {
+      const float ek = ew[k];
+      const bool prior = ek > eT || (ek == eT && k < t);
+      before += prior ? ek : 0.f;
+      rank += prior;
+    }
+    const bool in = before < smp.top_p * sT && eT > 0.f;
+    const float mass = block_sum256(in ? eT : 0.f, red);
+    const uint64_t bits = splitmix64_nth(smp.seed + (uint64_t)rd.slot, (uint64_t)rd.ctr + 1) >> 40;
+    const float c = (float)bits * (1.f / 16777216.f) * mass;
+    const bool cand = in && before <= c;
+    const float top = block_max256(cand ? (float)rank : -1.f, red);
+    choice = (int)block_max256(cand && (float)rank == top ? (float)t : -1.f, red);
+    if (t == choice) pick_e = e;
+    __syncthreads();
+    conf = pick_e / s;
+  }
+  if (t == 0) {
+    argmax_ws[r] = choice;
+    conf_ws[r] = conf;
+    ent_ws[r] = ent;
+    if (rd.oidx >= 0) {
+      if (argmax_out) argmax_out[rd.oidx] = choice;
+      if (conf_out) conf_out[rd.oidx] = report_entropy ? ent : conf;
+    }
+  }
+  if (rd.oidx >= 0 && logits_out)
+    for (int j = t; j < kVocab; j += 256) logits_out[(int64_t)rd.oidx * kVocab + j] = zr[j];
+}
+
 // Unmasking after a pass; one wave per sequence, lane j = block position j.
 // THRESHOLD: masked positions with conf > alpha, or if none the most
 // confident one (lowest position on ties); ONE_STEP: every masked position;
@@ -1522,9 +1614,10 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, float * /*rinv_ws*/, void *
     b.x_row_off = nullptr;
   }
   if (b.K % (4 * kGemmBK)) return hipErrorInvalidValue;  // the pipeline takes K steps in fours
-  // 128x128 tiles when they alone give the chip enough workgroups
+  // 128x128 tiles only when they give every CU a workgroup (measured at the
+  // decode and prefill shapes: below that the 64x64 tiles are faster)
   const int big = ((a.R + 127) / 128) * ((a.N + 127) / 128);
-  if (big >= 128)
+  if (big >= 256)
     hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2>), dim3(big), dim3(256), 0, s, b);
   else
     hipLaunchKernelGGL((k_gemm_mfma<64, 64, 4>), dim3(((a.R + 63) / 64) * ((a.N + 63) / 64)),
@@ -1617,9 +1710,13 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
 
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
-                         float *conf_out, float *logits_out, hipStream_t s) {
-  hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
-                     report_entropy, argmax_out, conf_out, logits_out);
+                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s) {
+  if (smp)
+    hipLaunchKernelGGL(k_decide_sample, dim3(R), dim3(256), 0, s, logits, rows, argmax_ws, conf_ws,
+                       ent_ws, report_entropy, argmax_out, conf_out, logits_out, *smp);
+  else
+    hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
+                       report_entropy, argmax_out, conf_out, logits_out);
   return hipGetLastError();
 }
 

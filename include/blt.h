@@ -48,7 +48,8 @@ typedef enum {
   BLT_EINVAL = -1,     /* bad argument: NULL, out of range, inconsistent sizes */
   BLT_ECAPACITY = -2,  /* a size exceeds a capacity fixed in blt_config */
   BLT_EDTYPE = -3,     /* unsupported dtype */
-  BLT_EHIP = -4        /* a HIP runtime call failed (message in blt_last_error) */
+  BLT_EHIP = -4,       /* a HIP runtime call failed (message in blt_last_error) */
+  BLT_ENOTIMPL = -5    /* a combination of options this library does not implement */
 } blt_status;
 
 typedef enum { BLT_F32 = 0, BLT_BF16 = 1 } blt_dtype;
@@ -180,7 +181,27 @@ blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const
  * block_tok is updated in place; masked_left[slot[b]] (device) receives the
  * number of [MASK]s left.  Optional device outputs for block rows:
  * argmax_out/conf_out [slot[b]*B+j] (conf_out: the row's confidence, or its
- * entropy in nats under ENTROPY), logits_out [(slot[b]*B+j)*257+v]. */
+ * entropy in nats under ENTROPY), logits_out [(slot[b]*B+j)*257+v].
+ *
+ * Sampling (pytorch.kr summary, "block unmasking strategies": EB sampling
+ * combined with top-p sampling).  sampling == NULL: each position takes its
+ * greedy byte.  Otherwise each block position draws its byte from the
+ * nucleus of softmax(z / temperature) over bytes 0..255 (bytes ranked by
+ * probability, ties by byte id; the nucleus is the shortest prefix of that
+ * ranking whose mass reaches top_p; with c = u * its mass, the byte whose
+ * interval of the nucleus holds c), where u in [0, 1) is the top 24 bits of
+ * output n + 1 of SplitMix64 started from state seed + slot[b], over 2^24,
+ * and n = draw[b] * 64 + j for block position j (draw: host, >= 0, one
+ * value per sequence, e.g. its count of sampling passes so far).  The
+ * position's confidence and entropy stay those of the model's distribution
+ * (temperature 1): the probability of the drawn byte, and the entropy of
+ * softmax(z).  Requires a bfloat16 or float32 context alike; temperature
+ * > 0 and finite, 0 < top_p <= 1, draw[b] * 64 + 63 < 2^31. */
+typedef struct {
+  float temperature;
+  float top_p;
+  uint64_t seed;
+} blt_sampling;
 blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batch,
                                  const int32_t *slot, const int32_t *start_pos,
                                  const int32_t *n_append, int32_t n_append_max,
@@ -188,7 +209,8 @@ blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batc
                                  int32_t *block_tok, int32_t B, const int32_t *block_lat,
                                  float alpha, blt_unmask mode, blt_block_mask mask,
                                  int32_t *argmax_out, float *conf_out, float *logits_out,
-                                 int32_t *masked_left);
+                                 int32_t *masked_left, const blt_sampling *sampling,
+                                 const int32_t *draw);
 
 /* Greedy exact-match verification (pytorch.kr summary, "BLT-S and BLT-DV").
  * For sequence slot s = slot[b] (slot NULL: s = b): draft[s*ld_draft+j]
@@ -268,6 +290,14 @@ typedef struct {
   blt_unmask unmask;
   blt_block_mask block_mask;
   int32_t n_gen;            /* bytes to generate per sequence */
+  /* Sampled BLT-D (temperature > 0): the bytes of sequence b are drawn as in
+   * blt_decode_block_step with seed `seed` (stream seed + b) and draw[b] =
+   * the sequence's decoder passes so far in this call.  temperature = 0:
+   * greedy.  Other policies with temperature > 0 return BLT_ENOTIMPL (their
+   * verification would need rejection sampling). */
+  float temperature;
+  float top_p;
+  uint64_t seed;
 } blt_policy_args;
 
 typedef struct blt_session blt_session;

@@ -103,10 +103,10 @@ class Replayer:
         z = self.logits[base * 257:(base + n) * 257].view(n, 257).cpu().numpy()
         return z, self.argmax[base:base + n].cpu().numpy()
 
-    def block(self, rec, alpha, unmask):
+    def block(self, rec, alpha, unmask, sampling=None, draw=None):
         """Run a BLT-D pass from the oracle's block state; return logits of
-        the block rows, argmax, conf (entropy under "entropy") and the block
-        after the commit."""
+        the block rows, argmax (the drawn bytes when sampling), conf (entropy
+        under "entropy") and the block after the commit."""
         B, na = len(rec["block_before"]), rec["n_append"]
         s = self.slot
         self.block_tok[s * B:(s + 1) * B] = self.torch.tensor(rec["block_before"], dtype=self.torch.int32)
@@ -119,7 +119,8 @@ class Replayer:
             mask=self.blt.BLT_BLOCK_CAUSAL if rec["block_causal"] else self.blt.BLT_BLOCK_BIDIR,
             n_append=[na], n_append_max=na, append_bytes=rec["tokens"][:na] if na else None,
             append_lat=rec["targets"][:na] if na else None, argmax_out=self.argmax,
-            conf_out=self.conf, logits_out=self.logits, masked_left=self.masked)
+            conf_out=self.conf, logits_out=self.logits, masked_left=self.masked,
+            sampling=sampling, draw=None if draw is None else [draw])
         self.torch.cuda.synchronize()
         z = self.logits[s * B * 257:(s + 1) * B * 257].view(B, 257).cpu().numpy()
         return (z, self.argmax[s * B:(s + 1) * B].cpu().numpy(),

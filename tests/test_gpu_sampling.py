@@ -1,0 +1,172 @@
+"""GPU parity of sampled BLT-D (temperature and top-p sampling combined with
+the unmask rules) against the CPU oracle.
+
+Teacher-forced replays run each pass of an oracle trace on the GPU from the
+oracle's own block state and check, per block position:
+  * the logits, within the path's tolerance;
+  * the drawn byte against the oracle's sampler applied to the GPU's own
+    logits (the sampling logic, to float32 rounding: compared where that
+    draw's margin exceeds 1e-5), and against the oracle's draw wherever the
+    oracle's margin exceeds the probability error the logit tolerance allows;
+  * the confidence (the model probability of the drawn byte) or entropy;
+  * the commit: the oracle's unmask rule applied to the GPU's draws and
+    confidences must give the GPU's block, unless a confidence lies within
+    1e-5 of the threshold (or an entropy prefix sum within 1e-4 of gamma).
+Native sessions are checked for determinism per seed and for the greedy
+limit; options the library does not implement fail with BLT_ENOTIMPL.
+"""
+import numpy as np
+import pytest
+
+import bltgen
+from oracle import decide, loops
+from tests.gpu_util import (BF16_ABS, FP32_REL, Replayer, decoder_for, logits_ok, oracle_inputs,
+                            say)
+
+pytestmark = pytest.mark.gpu
+
+MINI_BF16 = bltgen.WORKLOADS[1].replace(n_layers=2, d_model=256, n_heads=4, d_ffn=1024,
+                                        d_global=512, prompt_len=300, prompt_patches=80,
+                                        n_gen=40, block=4)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    import torch
+    import block_diffusion_byte_amd as blt
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    blt.lib()
+    yield
+
+
+def _rule(block, choice, conf, ent, alpha, unmask):
+    if unmask == "entropy":
+        return decide.unmask_commit_entropy(block, choice, ent, alpha)[0]
+    return decide.unmask_commit(block, choice, conf, alpha, unmask == "one_step")[0]
+
+
+def _near_threshold(block, conf, ent, alpha, unmask):
+    masked = [j for j, t in enumerate(block) if t == decide.MASK]
+    if unmask == "threshold":
+        return any(abs(conf[j] - alpha) < 1e-5 for j in masked)
+    if unmask == "entropy":
+        srt = sorted(ent[j] for j in masked)
+        return any(abs(c - alpha) < 1e-4 for c in np.cumsum(srt))
+    return False
+
+
+def _replay_sampled(wl, unmask, alpha, sampling, n_gen=32, B=4):
+    import torch
+    w = bltgen.make_weights(wl, gains="random")
+    W, inp, inp64 = oracle_inputs(wl, w)
+    run = loops.blt_d(W, wl, inp64, n_gen, B, alpha, unmask=unmask, sampling=sampling, trace=True)
+    temp, top_p, seed = sampling
+    dec = decoder_for(wl.replace(block=B), w, max_batch=1, max_rows=256)
+    scale = wl.head_scale
+    stats = dict(drawn=0, vs_oracle=0, commits=0, worst=0.0)
+    try:
+        rp = Replayer(dec, wl, inp)
+        rp.prefill(inp)
+        for d, rec in enumerate(run.passes):
+            z, am, cf, after, left = rp.block(rec, alpha, unmask, sampling=sampling, draw=d)
+            na = rec["n_append"]
+            ref = np.asarray(rec["logits"])[na:]
+            ok, err, tol = logits_ok(z, ref, wl.dtype, scale)
+            assert ok, f"pass {d}: logits err {err} > {tol}"
+            stats["worst"] = max(stats["worst"], err)
+            conf, ent = [0.0] * B, [0.0] * B
+            for j in range(B):
+                # logit error bound eps of the path -> probability error <= 2 eps / T
+                eps = FP32_REL * np.abs(ref[j][:256]).max() if wl.dtype == "fp32" else BF16_ABS * scale
+                prob_tol = 2.5 * eps / temp
+                u = decide.uniform(seed, d * loops.MAX_BLOCK + j)
+                assert u == rec["u"][j]
+                b, _, e, margin = decide.sample_top_p(z[j], temp, top_p, u)
+                zj = np.asarray(z[j][:256], dtype=np.float64)
+                q = np.exp(zj - zj.max())
+                conf[j], ent[j] = float(q[am[j]] / q.sum()), e
+                if margin > 1e-5:
+                    assert am[j] == b, f"pass {d} pos {j}: drew {am[j]}, sampler on its logits {b}"
+                    stats["drawn"] += 1
+                if rec["gap"][j] > prob_tol:
+                    assert am[j] == rec["choice"][j], f"pass {d} pos {j}: drew {am[j]}, oracle {rec['choice'][j]}"
+                    stats["vs_oracle"] += 1
+                want = ent[j] if unmask == "entropy" else conf[j]
+                assert abs(cf[j] - want) <= 1e-4 * max(1.0, abs(want)), (d, j, cf[j], want)
+            if not _near_threshold(rec["block_before"], conf, ent, alpha, unmask):
+                exp_after = _rule(rec["block_before"], list(am), conf, ent, alpha, unmask)
+                assert list(after) == exp_after, f"pass {d}: block {list(after)} vs rule {exp_after}"
+                stats["commits"] += 1
+            assert left == sum(1 for t in after if t == decide.MASK)
+    finally:
+        dec.close()
+    say(f"{wl.name} sampled BLT-D ({unmask}, T={temp}, top_p={top_p}): {len(run.passes)} passes, "
+        f"worst logit err {stats['worst']:.3g}, {stats['drawn']} draws vs the sampler on GPU logits, "
+        f"{stats['vs_oracle']} vs the oracle's draws, {stats['commits']} commits checked")
+    assert stats["drawn"] > 0 and stats["commits"] > 0
+    return stats
+
+
+@pytest.mark.parametrize("unmask,alpha", [("threshold", 0.3), ("entropy", 3.0), ("one_step", 0.0)])
+def test_tiny_fp32_sampled_blt_d_teacher_forced(unmask, alpha):
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    st = _replay_sampled(wl, unmask, alpha, (0.8, 0.9, 1234))
+    assert st["vs_oracle"] > 0
+
+
+def test_mini_bf16_sampled_blt_d_entropy_teacher_forced():
+    wl = MINI_BF16.replace(head_scale=12.0)
+    _replay_sampled(wl, "entropy", 3.0, (1.0, 0.8, 77), n_gen=24)
+
+
+def _session(wl, w, inps, n_gen, block, alpha, unmask, temp, top_p, seed, policy=None):
+    import torch
+    import block_diffusion_byte_amd as blt
+    dec = decoder_for(wl.replace(block=block), w, max_batch=len(inps), max_rows=64)
+    table = torch.from_numpy(np.stack([i["latents"] for i in inps])).to("cuda:0", dec.torch_dtype)
+    sess = blt.blt_session_create(dec.ctx, dec.state, [i["prompt"] for i in inps],
+                                  [i["prompt_patches"] for i in inps], [i["salt"] for i in inps],
+                                  table, wl.n_latents)
+    try:
+        blt.blt_session_prefill(dec.ctx, sess)
+        blt.blt_session_generate(dec.ctx, sess, blt.BLT_POLICY_BLT_D if policy is None else policy,
+                                 block, alpha, n_gen, unmask, temperature=temp, top_p=top_p, seed=seed)
+        return [blt.blt_session_result(sess, b, n_gen) for b in range(len(inps))]
+    finally:
+        blt.blt_session_destroy(sess)
+        dec.close()
+
+
+def test_sampled_sessions_are_seeded_and_reach_the_greedy_limit():
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    w = bltgen.make_weights(wl, gains="random")
+    inps = [bltgen.make_sequence_inputs(wl, b) for b in range(3)]
+    E = blt.BLT_UNMASK_ENTROPY
+    a = _session(wl, w, inps, 40, 4, 3.0, E, 0.8, 0.9, 5)
+    b = _session(wl, w, inps, 40, 4, 3.0, E, 0.8, 0.9, 5)
+    c = _session(wl, w, inps, 40, 4, 3.0, E, 0.8, 0.9, 6)
+    assert [r["out"] for r in a] == [r["out"] for r in b]
+    assert [r["out"] for r in a] != [r["out"] for r in c]
+    assert all(r["n"] == 40 for r in a)
+    g = _session(wl, w, inps, 40, 4, 3.0, E, 0.0, 1.0, 0)
+    lim = _session(wl, w, inps, 40, 4, 3.0, E, 1.0, 1e-7, 5)
+    assert [(r["out"], r["n_dec"]) for r in lim] == [(r["out"], r["n_dec"]) for r in g]
+    # the oracle's greedy EB run agrees with the greedy session
+    W, _, inp64 = oracle_inputs(wl, w, 0)
+    ref = loops.blt_d(W, wl, inp64, 40, 4, 3.0, unmask="entropy")
+    assert list(g[0]["out"]) == ref.out
+    say(f"sampled sessions: seeded, n_dec {[r['n_dec'] for r in a]}; top_p -> 0 equals greedy")
+
+
+def test_sampling_argument_errors():
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    w = bltgen.make_weights(wl)
+    inps = [bltgen.make_sequence_inputs(wl, 0)]
+    with pytest.raises(blt.BltError) as ei:
+        _session(wl, w, inps, 8, 8, 0.0, 0, 1.0, 0.9, 1, policy=blt.BLT_POLICY_BLT_S)
+    assert ei.value.status == blt.BLT_ENOTIMPL
+    with pytest.raises(blt.BltError) as ei:
+        _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.0, 1)
+    assert ei.value.status == blt.BLT_EINVAL
