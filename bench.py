@@ -28,11 +28,21 @@ PROFILE_MD = os.path.join(ROOT, "profiles", "k_attn_mfma_bltd4_bf16_b1_ctx4096.m
 KERNELS_SRC = os.path.join(ROOT, "block_diffusion_byte_amd", "csrc", "kernels.hip")
 
 
+def kernel_source_sha256(name):
+    """sha256 of one kernel's definition in kernels.hip: from its template
+    line to the closing brace at the start of a line."""
+    import hashlib
+    src = open(KERNELS_SRC).read()
+    i = src.index(f"void {name}(")
+    i = src.rindex("template", 0, i)
+    j = src.index("\n}\n", i) + 3
+    return hashlib.sha256(src[i:j].encode()).hexdigest()
+
+
 def measured_traffic(workload_index):
     """HBM bytes per attention launch from the committed rocprofv3 PMC summary
     (FETCH_SIZE + WRITE_SIZE scaled by a plain copy), or None when the summary
-    is for another workload or the kernel source changed since it was taken."""
-    import hashlib
+    is for another workload or the kernel's source changed since it was taken."""
     if workload_index != 1 or not os.path.exists(PROFILE_MD):
         return None
     fields = {}
@@ -40,8 +50,7 @@ def measured_traffic(workload_index):
         if ":" in line and not line.startswith(("#", "-", "|", "`")):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    src = hashlib.sha256(open(KERNELS_SRC, "rb").read()).hexdigest()
-    if fields.get("kernels_hip_sha256") != src:
+    if fields.get("k_attn_mfma_source_sha256") != kernel_source_sha256("k_attn_mfma"):
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
