@@ -373,7 +373,7 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
   c->row_off = ((size_t)cfg->max_batch * sizeof(SeqDesc) + 255) & ~(size_t)255;
   c->off_off = (c->row_off + (size_t)R * sizeof(RowDesc) + 255) & ~(size_t)255;
-  const size_t stage = c->off_off + (size_t)R * sizeof(int64_t);
+  const size_t stage = c->off_off + 2 * (size_t)R * sizeof(int64_t);
   chk(hipMalloc(&c->desc_d, stage));
   if (he == hipSuccess) {
     c->seqs_d = (SeqDesc *)c->desc_d;
@@ -394,6 +394,28 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
       }
     chk(hipMemcpy(c->rope_tab, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice));
   }
+  if (he == hipSuccess) {
+    // The cross-attention read of one latent is W_o^c_l W_v^c_l W_lat o for
+    // every layer l: the two per-layer matrices are multiplied once here,
+    // C_l = W_o^c_l (W_v^c_l^T)^T by the GEMM (rows of W_o^c_l against rows of
+    // the transposed W_v^c_l), stacked as [L*d][d] so that one product per
+    // latent fills all its cross vectors.
+    const int L = cfg->n_layers;
+    void *tmp = nullptr;
+    chk(hipMalloc(&c->cross_w, (size_t)L * d * d * e));
+    chk(hipMalloc(&tmp, (size_t)d * d * e));
+    for (int l = 0; l < L && he == hipSuccess; ++l) {
+      const blt_layer_weights &lw = c->layers[l];
+      chk(launch_transpose(c->bf16, lw.wv_c, tmp, d, c->stream));
+      GemmArgs a = base_args(c);
+      a.R = d; a.W = tmp; a.N = d; a.K = d;
+      a.pro = PRO_PLAIN; a.X = lw.wo_c; a.ldx = d;
+      a.ep = EP_STORE_ACT; a.out_act = (char *)c->cross_w + (size_t)l * d * d * e; a.ldo = d;
+      chk(launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+    }
+    chk(hipStreamSynchronize(c->stream));
+    if (tmp) (void)hipFree(tmp);
+  }
   if (he != hipSuccess) {
     blt_destroy(c);
     return BLT_EHIP;
@@ -408,7 +430,7 @@ blt_status blt_destroy(blt_ctx *c) {
   drop_graphs(c);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->ent_ws, c->argmax_ws,
-                  c->xa, c->xb, c->desc_d, c->rope_tab};
+                  c->xa, c->xb, c->desc_d, c->rope_tab, c->cross_w};
   for (void *p : bufs)
     if (p) (void)hipFree(p);
   for (int i = 0; i < kRing; ++i) {
@@ -436,16 +458,15 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
   const int d = g.d_model, L = g.n_layers;
   for (int i0 = 0; i0 < n; i0 += g.max_rows) {
     const int m = std::min(g.max_rows, n - i0);
+    // staged offsets: the source rows of the latents, then their cross rows
     std::vector<int64_t> offs(2 * (size_t)m);
     for (int i = 0; i < m; ++i) {
-      offs[i] = ((int64_t)slot[i0 + i] * seq_stride + idx[i0 + i]) * g.d_global;        // source row
-      offs[m + i] = (((int64_t)slot[i0 + i] * g.max_latents + idx[i0 + i]) * L) * d;     // cross row
+      offs[i] = ((int64_t)slot[i0 + i] * seq_stride + idx[i0 + i]) * g.d_global;
+      offs[m + i] = (((int64_t)slot[i0 + i] * g.max_latents + idx[i0 + i]) * L) * d;
     }
-    // source offsets for W_lat, then (restaged) destination offsets
-    std::vector<int64_t> src(offs.begin(), offs.begin() + m), dst(offs.begin() + m, offs.end());
     std::vector<RowDesc> no_rows;
     std::vector<SeqDesc> no_seqs;
-    blt_status bs = stage_pass(c, no_rows, no_seqs, &src);
+    blt_status bs = stage_pass(c, no_rows, no_seqs, &offs);
     if (bs != BLT_OK) return bs;
     // o~ = W_lat o  -> xb
     GemmArgs a = base_args(c);
@@ -453,23 +474,12 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
     a.pro = PRO_PLAIN; a.X = table; a.x_row_off = c->offs_d;
     a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
     HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
-    // The destination offsets replace the source offsets once W_lat has read them.
-    bs = stage_pass(c, no_rows, no_seqs, &dst);
-    if (bs != BLT_OK) return bs;
-    for (int l = 0; l < L; ++l) {
-      const blt_layer_weights &lw = c->layers[l];
-      a = base_args(c);
-      a.R = m; a.W = lw.wv_c; a.N = d; a.K = d;
-      a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
-      a.ep = EP_STORE_ACT; a.out_act = c->xa; a.ldo = d;
-      HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
-      a = base_args(c);
-      a.R = m; a.W = lw.wo_c; a.N = d; a.K = d;
-      a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
-      a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = c->offs_d;
-      a.off_add = (int64_t)l * d;
-      HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
-    }
+    // cross[slot][idx][l][:] = C_l o~ for every layer at once (N = L*d)
+    a = base_args(c);
+    a.R = m; a.W = c->cross_w; a.N = L * d; a.K = d;
+    a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
+    a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = c->offs_d + m;
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
   }
   return BLT_OK;
 }

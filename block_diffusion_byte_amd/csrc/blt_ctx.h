@@ -68,6 +68,7 @@ struct blt_ctx {
   int32_t *argmax_ws = nullptr;
   void *xa = nullptr;         // GEMM activations [R][max(d, F)]
   void *xb = nullptr;         // GEMM activations [R][max(d, d_global)]
+  void *cross_w = nullptr;    // [L*d][d]: W_o^c_l W_v^c_l of every layer, stacked (set-up)
   void *desc_d = nullptr;      // per-pass descriptors: sequences, rows, row offsets
   blt::SeqDesc *seqs_d = nullptr;
   blt::RowDesc *rows_d = nullptr;

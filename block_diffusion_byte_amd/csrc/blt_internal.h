@@ -131,6 +131,8 @@ hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok,
                          float alpha, int mode, int32_t *masked_left, hipStream_t s);
+// dst = src^T, n x n elements of the context's dtype (set-up only).
+hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStream_t s);
 hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,
                          int ld_draft, const int32_t *pred, int ld_pred, int32_t *accept_len,
                          int32_t *next_byte, hipStream_t s);

@@ -19,6 +19,7 @@
 #include <hip/hip_runtime.h>
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "blt_internal.h"
@@ -1467,6 +1468,16 @@ __global__ __launch_bounds__(256) void k_decide_sample(const float *logits, cons
     for (int j = t; j < kVocab; j += 256) logits_out[(int64_t)rd.oidx * kVocab + j] = zr[j];
 }
 
+// dst = src^T for an n x n matrix (set-up only: the cross-attention weights).
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose(const T *src, T *dst, int n) {
+  const int64_t total = (int64_t)n * n;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / n, c = i - r * n;
+    dst[c * n + r] = src[i];
+  }
+}
+
 // Unmasking after a pass; one wave per sequence, lane j = block position j.
 // THRESHOLD: masked positions with conf > alpha, or if none the most
 // confident one (lowest position on ties); ONE_STEP: every masked position;
@@ -1717,6 +1728,17 @@ hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_
   else
     hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
                        report_entropy, argmax_out, conf_out, logits_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStream_t s) {
+  const int blocks = (int)std::min<int64_t>(((int64_t)n * n + 255) / 256, 4096);
+  if (bf16)
+    hipLaunchKernelGGL(k_transpose<uint16_t>, dim3(blocks), dim3(256), 0, s, (const uint16_t *)src,
+                       (uint16_t *)dst, n);
+  else
+    hipLaunchKernelGGL(k_transpose<float>, dim3(blocks), dim3(256), 0, s, (const float *)src,
+                       (float *)dst, n);
   return hipGetLastError();
 }
 
