@@ -217,9 +217,15 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
   a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
   HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
-  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, c->ent_ws,
-                           p.unmask && p.mode == BLT_UNMASK_ENTROPY, p.argmax_out,
-                           p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s));
+  const int rep_ent = p.unmask && p.mode == BLT_UNMASK_ENTROPY;
+  if (p.unmask && !p.sample) {
+    HIP_TRY(c, launch_decide_unmask(c->logits, S, c->seqs_d, c->rows_d, c->argmax_ws, c->conf_ws,
+                                    c->ent_ws, rep_ent, p.argmax_out, p.conf_out, p.logits_out,
+                                    (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
+    return BLT_OK;
+  }
+  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, c->ent_ws, rep_ent,
+                           p.argmax_out, p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s));
   if (p.unmask)
     HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, c->ent_ws,
                              (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));

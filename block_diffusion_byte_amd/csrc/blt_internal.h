@@ -131,6 +131,13 @@ hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok,
                          float alpha, int mode, int32_t *masked_left, hipStream_t s);
+// Greedy decisions of every row and the unmasking of every sequence's block
+// in one launch (block passes without sampling): one workgroup per sequence.
+hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *seqs,
+                                const RowDesc *rows, int32_t *argmax_ws, float *conf_ws,
+                                float *ent_ws, int report_entropy, int32_t *argmax_out,
+                                float *conf_out, float *logits_out, int32_t *block_tok,
+                                float alpha, int mode, int32_t *masked_left, hipStream_t s);
 // dst = src^T, n x n elements of the context's dtype (set-up only).
 hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStream_t s);
 hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,

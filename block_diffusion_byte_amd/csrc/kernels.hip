@@ -1313,11 +1313,12 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
 // ---------------------------------------------------------------------------
 // Greedy byte and confidence of each row: max over logits 0..255 (the [MASK]
 // logit takes no part), lowest id on ties, conf = 1 / sum exp(z - max).
-__global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDesc *rows,
-                                               int32_t *argmax_ws, float *conf_ws, float *ent_ws,
-                                               int report_entropy, int32_t *argmax_out,
-                                               float *conf_out, float *logits_out) {
-  const int r = blockIdx.x, l = threadIdx.x;
+// One wave decides row r (lane l = threadIdx.x & 63).
+__device__ __forceinline__ void decide_row(int r, const float *logits, const RowDesc *rows,
+                                           int32_t *argmax_ws, float *conf_ws, float *ent_ws,
+                                           int report_entropy, int32_t *argmax_out,
+                                           float *conf_out, float *logits_out) {
+  const int l = threadIdx.x & 63;
   const float *z = logits + (int64_t)r * kVocab;
   float best = -INFINITY;
   int bi = 0x7fffffff;
@@ -1374,6 +1375,14 @@ __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDes
   }
   if (oidx >= 0 && logits_out)
     for (int j = l; j < kVocab; j += 64) logits_out[(int64_t)oidx * kVocab + j] = z[j];
+}
+
+__global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDesc *rows,
+                                               int32_t *argmax_ws, float *conf_ws, float *ent_ws,
+                                               int report_entropy, int32_t *argmax_out,
+                                               float *conf_out, float *logits_out) {
+  decide_row(blockIdx.x, logits, rows, argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out,
+             conf_out, logits_out);
 }
 
 // Sampled decisions (temperature / top-p, the stochastic variant paired
@@ -1484,13 +1493,13 @@ __global__ __launch_bounds__(256) void k_transpose(const T *src, T *dst, int n) 
 // ENTROPY: masked positions ranked by entropy (ties by position), committed
 // in rank order while the running entropy sum stays <= alpha (the bound
 // gamma), at least the first.
-__global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_t *argmax_ws,
-                                               const float *conf_ws, const float *ent_ws,
-                                               int32_t *block_tok, float alpha, int mode,
-                                               int32_t *masked_left) {
-  const SeqDesc sd = seqs[blockIdx.x];
+// One wave unmasks the block of sequence sd (lane j = block position j).
+__device__ __forceinline__ void unmask_seq(const SeqDesc &sd, const int32_t *argmax_ws,
+                                           const float *conf_ws, const float *ent_ws,
+                                           int32_t *block_tok, float alpha, int mode,
+                                           int32_t *masked_left) {
   if (sd.nblk <= 0) return;
-  const int j = threadIdx.x;
+  const int j = threadIdx.x & 63;
   const bool active = j < sd.nblk;
   const int tok = active ? block_tok[sd.blk0 + j] : 0;
   const bool masked = active && tok == kMask;
@@ -1522,6 +1531,32 @@ __global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_
   }
   if ((cm >> j) & 1ull) block_tok[sd.blk0 + j] = argmax_ws[sd.blk_row0 + j];
   if (j == 0) masked_left[sd.out_b] = __popcll(mm) - __popcll(cm);
+}
+
+__global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_t *argmax_ws,
+                                               const float *conf_ws, const float *ent_ws,
+                                               int32_t *block_tok, float alpha, int mode,
+                                               int32_t *masked_left) {
+  unmask_seq(seqs[blockIdx.x], argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left);
+}
+
+// Decisions and unmasking of a block pass in one launch: workgroup b takes
+// sequence b, its four waves decide the sequence's rows (row0 + w, + 4, ...)
+// exactly as k_decide does, then wave 0 unmasks its block.
+__global__ __launch_bounds__(256) void k_decide_unmask(const float *logits, const SeqDesc *seqs,
+                                                      const RowDesc *rows, int32_t *argmax_ws,
+                                                      float *conf_ws, float *ent_ws,
+                                                      int report_entropy, int32_t *argmax_out,
+                                                      float *conf_out, float *logits_out,
+                                                      int32_t *block_tok, float alpha, int mode,
+                                                      int32_t *masked_left) {
+  const SeqDesc sd = seqs[blockIdx.x];
+  const int w = threadIdx.x >> 6;
+  for (int r = sd.row0 + w; r < sd.row0 + sd.nrows; r += 4)
+    decide_row(r, logits, rows, argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out, conf_out,
+               logits_out);
+  __syncthreads();                            // the rows' decisions are visible to wave 0
+  if (w == 0) unmask_seq(sd, argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left);
 }
 
 // Greedy exact-match acceptance: leading draft bytes equal to the prediction
@@ -1728,6 +1763,17 @@ hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_
   else
     hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
                        report_entropy, argmax_out, conf_out, logits_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *seqs,
+                                const RowDesc *rows, int32_t *argmax_ws, float *conf_ws,
+                                float *ent_ws, int report_entropy, int32_t *argmax_out,
+                                float *conf_out, float *logits_out, int32_t *block_tok,
+                                float alpha, int mode, int32_t *masked_left, hipStream_t s) {
+  hipLaunchKernelGGL(k_decide_unmask, dim3(n_seq), dim3(256), 0, s, logits, seqs, rows, argmax_ws,
+                     conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, block_tok,
+                     alpha, mode, masked_left);
   return hipGetLastError();
 }
 
