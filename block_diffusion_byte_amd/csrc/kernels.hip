@@ -653,13 +653,30 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
 // only on its own query and keys (never on the other rows of the pass).
 constexpr int kCK = kAttnChunk;
 
+// Row reductions over the four 16-lane groups of a wave (lanes l, l^16, l^32,
+// l^48 hold the same row): two cross-lane swaps, no LDS.
+__device__ __forceinline__ float max_lane_groups(float x) {
+  // max over lanes l, l^16, l^32, l^48 (the four lane groups of a 16-lane row)
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
+}
+__device__ __forceinline__ float sum_lane_groups(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+
 // bfloat16: each wave takes 32 keys of the chunk and up to 16 rows at a time.
-// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16:
-// a lane then holds 4 keys of each of the two 16-key tiles for one row,
-// which is exactly the A-operand layout P[row][k-slot] of the P.V product
-// (k-slot 8q+i of lane group q is key 4q+i of tile 0 for i < 4 and key
-// 4q+i-4 of tile 1 otherwise; the V operand is gathered in the same slot
-// order).  P is split into bf16 hi and lo parts, two MFMAs per output tile,
+// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16;
+// the K rows are fed to the two 16-key score tiles permuted (row m of tile t
+// is key 8(m/4) + 4t + m%4) so that lane group q ends up holding keys
+// 8q..8q+7 of the wave's 32 for one row: exactly the A-operand layout
+// P[row][k-slot] of the P.V product with k-slot 8q+i = key 8q+i, and the V
+// operand of lane (dim, q) is one 16-byte piece of the transposed V row.  P is split into bf16 hi and lo parts, two MFMAs per output tile,
 // so the probabilities keep about 16 significant bits.  The four waves'
 // (o, m, l) are combined through LDS in wave order.
 template <int DH>
@@ -704,33 +721,28 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
   bf16x8_t ka[2][KS];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
-    const uint16_t *kr = Kp + (int64_t)min(kw0 + 16 * kt + lr, klast) * DH + 8 * lq;
+    const uint16_t *kr = Kp + (int64_t)min(kw0 + 8 * (lr >> 2) + 4 * kt + (lr & 3), klast) * DH + 8 * lq;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *(const bf16x8_t *)(kr + 32 * ks);
   }
-  const int ka0 = kw0 + 4 * lq, ka1 = kw0 + 16 + 4 * lq;   // first keys of the two V groups
-  const int va0 = min(ka0, klast & ~3), va1 = min(ka1, klast & ~3);
-  uint2 vg[DT][2];
+  const int kq = kw0 + 8 * lq;                // the lane group's first key
+  const int va = min(kq, klast & ~7);         // a group clamped here lies wholly past kmax
+  u32x4_t vg[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    const uint16_t *vr = Vt + (int64_t)(16 * dt + lr) * g.max_ctx;
-    vg[dt][0] = *(const uint2 *)(vr + va0);
-    vg[dt][1] = *(const uint2 *)(vr + va1);
-  }
-  // V operand in slot order; keys at or past kmax (never written) become 0
+  for (int dt = 0; dt < DT; ++dt)
+    vg[dt] = *(const u32x4_t *)(Vt + (int64_t)(16 * dt + lr) * g.max_ctx + va);
+  // V operand (k-slot 8q+i = key kq+i); keys at or past kmax (never written) become 0
   bf16x8_t vb[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    const uint32_t raw[4] = {vg[dt][0].x, vg[dt][0].y, vg[dt][1].x, vg[dt][1].y};
-    uint32_t o[4];
+    u32x4_t o = vg[dt];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int k = (i < 2 ? ka0 : ka1) + 2 * (i & 1);
-      const uint32_t lo = k < sd.kmax ? (raw[i] & 0xffffu) : 0u;
-      const uint32_t hi = k + 1 < sd.kmax ? (raw[i] & 0xffff0000u) : 0u;
+      const uint32_t lo = kq + 2 * i < sd.kmax ? (o[i] & 0xffffu) : 0u;
+      const uint32_t hi = kq + 2 * i + 1 < sd.kmax ? (o[i] & 0xffff0000u) : 0u;
       o[i] = lo | hi;
     }
-    vb[dt] = __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+    vb[dt] = __builtin_bit_cast(bf16x8_t, o);
   }
   const float scale = 1.f / sqrtf((float)DH);
 
@@ -746,7 +758,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       v[6] = (__bf16)qf[ks][1].z; v[7] = (__bf16)qf[ks][1].w;
       qb[ks] = v;
     }
-    // S^T tiles: acc[kt][v] = score of key kw0+16kt+4lq+v for row lr
+    // S^T tiles: acc[kt][v] = score of key kq+4kt+v for row lr
     f32x4_t acc[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -761,14 +773,12 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int key = (kt ? ka1 : ka0) + v;
+        const int key = kq + 4 * kt + v;
         const float x = key < my_kend ? acc[kt][v] * scale : -INFINITY;
         sv[kt * 4 + v] = x;
         m = fmaxf(m, x);
       }
-    // the four lane groups holding row lr
-    m = fmaxf(m, __shfl_xor(m, 16, 64));
-    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    m = max_lane_groups(m);                   // the four lane groups holding row lr
     float l = 0.f;
     float ph[8], pl[8];
 #pragma unroll
@@ -777,8 +787,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       l += p;
       ph[i] = p;
     }
-    l += __shfl_xor(l, 16, 64);
-    l += __shfl_xor(l, 32, 64);
+    l = sum_lane_groups(l);
     bf16x8_t pa_hi, pa_lo;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -862,20 +871,6 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
 // the row's statistics unchanged, whatever the other rows of the tile read.
 // Cache rows at or past the sequence's kmax are never written and are staged
 // as zeros.
-__device__ __forceinline__ float max_lane_groups(float x) {
-  // max over lanes l, l^16, l^32, l^48 (the four lane groups of a 16-lane row)
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(c[0]), __uint_as_float(c[1]));
-}
-__device__ __forceinline__ float sum_lane_groups(float x) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
-}
-
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
                                                     int layer, const SeqDesc *seqs,
@@ -1271,26 +1266,28 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 }
 
 // Merge of the chunk partials of (row, head) in chunk order, 32 chunks at a
-// time with a running max; the partial of chunk c sits at [row][h][e][c], so
-// one float4 load fetches four chunks.
+// time with a running max; chunk c's partial sits at [row][h][c][d_h + 2].
+// Every load is addressed by the pass's chunk count gc alone (chunks past the
+// row's own count are read but weighted by an exact 0), so the row
+// descriptor, the statistics and the partials are all in flight at once.
 template <bool BF, int DH>
 __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
-                                                   int n_heads, int max_chunks, void *a_out) {
+                                                   int n_heads, int max_chunks, int gc,
+                                                   void *a_out) {
   using T = typename Act<BF>::T;
   __shared__ float fw[kMaxChunks];
   const int row = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
-  const RowDesc rd = rows[row];
-  if (rd.attn_flash) return;                  // written by the causal kernel
-  const int nc = (rd.kend + kCK - 1) / kCK;
   const float *pb = part + ((int64_t)row * n_heads + h) * max_chunks * (DH + 2);
-  // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
-  const int c0 = min(l, nc - 1), c1 = min(l + 64, nc - 1);
+  const int c0 = min(l, gc - 1), c1 = min(l + 64, gc - 1);
   const float m0 = pb[c0 * (DH + 2) + DH], m1 = pb[c1 * (DH + 2) + DH];
   const float l0 = pb[c0 * (DH + 2) + DH + 1], l1 = pb[c1 * (DH + 2) + DH + 1];
+  const RowDesc rd = rows[row];
+  const int nc = (rd.kend + kCK - 1) / kCK;
+  // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
   const bool ok0 = l < nc, ok1 = l + 64 < nc;
   const float M = wave_max(fmaxf(ok0 ? m0 : -INFINITY, ok1 ? m1 : -INFINITY));
   const float f0 = ok0 ? expf(m0 - M) : 0.f, f1 = ok1 ? expf(m1 - M) : 0.f;
-  const float L = wave_sum(l0 * f0 + l1 * f1);
+  const float L = wave_sum((ok0 ? l0 : 0.f) * f0 + (ok1 ? l1 : 0.f) * f1);
   fw[l] = f0;
   fw[l + 64] = f1;
   __syncthreads();
@@ -1298,15 +1295,16 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   // contiguous row of the partials, 32 chunks in flight at a time
   for (int e = l; e < DH; e += 64) {
     float O = 0.f;
-    for (int cb = 0; cb < nc; cb += 32) {
+    for (int cb = 0; cb < gc; cb += 32) {
       float ov[32];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) ov[u] = pb[min(cb + u, nc - 1) * (DH + 2) + e];
+      for (int u = 0; u < 32; ++u) ov[u] = pb[min(cb + u, gc - 1) * (DH + 2) + e];
 #pragma unroll
       for (int u = 0; u < 32; ++u)
         O = fmaf(cb + u < nc ? ov[u] : 0.f, fw[min(cb + u, kMaxChunks - 1)], O);
     }
-    ((T *)a_out)[(int64_t)row * n_heads * DH + h * DH + e] = from_f<T>(O / L);
+    if (!rd.attn_flash)                       // else written by the causal kernel
+      ((T *)a_out)[(int64_t)row * n_heads * DH + h * DH + e] = from_f<T>(O / L);
   }
 }
 
@@ -1731,7 +1729,7 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                          part, max_chunks);
   }
   hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
-                     g.n_heads, max_chunks, a_out);
+                     g.n_heads, max_chunks, grid_chunks, a_out);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
