@@ -6,7 +6,9 @@
   * entropy / unmask_commit_entropy: entropy-bounded (EB) unmasking;
   * verify_accept: the greedy exact-match verification of a draft;
   * uniform / sample_top_p: temperature and top-p (nucleus) sampling of a
-    position's byte, the stochastic variant the pages pair with EB sampling.
+    position's byte, the stochastic variant the pages pair with EB sampling;
+  * sampling_dist / verify_sample: verification of sampled drafts by
+    rejection sampling (the extension to temperature > 0 the pages mention).
 """
 from __future__ import annotations
 
@@ -180,3 +182,66 @@ def sample_top_p(z, temperature, top_p, u):
     if n < 256:
         margin = min(margin, before[n] - top_p)
     return b, float(q[b]), ent, float(margin)
+
+
+def sampling_dist(z, temperature, top_p):
+    """The distribution sample_top_p draws from: softmax(z / temperature)
+    over bytes 0..255 restricted to the nucleus and renormalised (0 outside
+    it).  Returns a float64 vector of 256 probabilities."""
+    y = np.asarray(z, dtype=np.float64)[:256] / float(temperature)
+    e = np.exp(y - y.max())
+    p = e / e.sum()
+    order = sorted(range(256), key=lambda b: (-p[b], b))
+    before = 0.0
+    d = np.zeros(256)
+    for b in order:
+        if before < top_p and p[b] > 0:
+            d[b] = p[b]
+        before += p[b]
+    return d / d.sum()
+
+
+def verify_sample(draft, q, p, u_acc, u_next):
+    """Rejection-sampling verification of a sampled draft.
+
+    pytorch.kr summary, "BLT-S and BLT-DV": sampling at temperature > 0
+    extends the shared verification by rejection sampling (mentioned, not
+    evaluated, and not spelled out there).  The plainest reading is the
+    standard speculative-sampling rule.  draft: the r draft bytes
+    x'_{l+1..l+r}; q[j]: the distribution draft byte j was drawn from; p[j]
+    (j = 0..r): the target distribution of the byte after verify row l+j
+    (sampling_dist of that row's logits).  For j = 0, 1, ...: x = draft[j]
+    is accepted iff u_acc[j] * q[j][x] < p[j][x] (probability
+    min(1, p/q)); at the first rejection the appended byte is drawn from
+    max(0, p[j] - q[j]) renormalised, walking bytes in id order (the first
+    byte whose cumulative residual mass exceeds u_next times the total); if
+    every draft byte is accepted, the free byte is drawn from p[r] as
+    sample_top_p draws (bytes ranked by probability, ties by id, the first
+    whose cumulative mass exceeds u_next).  Returns (accepted count a,
+    appended byte, margin): margin is the smallest distance, in
+    probability, between a quantity that decided the outcome and its
+    threshold.
+    """
+    r = len(draft)
+    if len(q) != r or len(p) != r + 1:
+        raise ValueError("need r draft distributions and r + 1 target distributions")
+    margin = np.inf
+    for j in range(r):
+        x = int(draft[j])
+        qj, pj = np.asarray(q[j], dtype=np.float64), np.asarray(p[j], dtype=np.float64)
+        t = u_acc[j] * qj[x]
+        margin = min(margin, abs(pj[x] - t))
+        if t < pj[x]:
+            continue
+        res = np.maximum(pj - qj, 0.0)
+        cum = np.cumsum(res)
+        c = u_next * cum[-1]
+        b = int(np.flatnonzero(cum > c)[0])
+        lo = cum[b - 1] if b > 0 else 0.0
+        return j, b, float(min(margin, c - lo, cum[b] - c))
+    pr = np.asarray(p[r], dtype=np.float64)
+    order = sorted(range(256), key=lambda b: (-pr[b], b))
+    cum = np.cumsum([pr[b] for b in order])
+    k = int(np.flatnonzero(cum > u_next)[0])
+    lo = cum[k - 1] if k > 0 else 0.0
+    return r, order[k], float(min(margin, u_next - lo, cum[k] - u_next))

@@ -459,6 +459,79 @@ def test_top_p_nucleus_and_frequencies(top_p):
     assert np.abs(hits[nucleus] / n - p[nucleus] / mass).max() <= 1.0 / n + 1e-12
 
 
+def test_sampling_dist_is_the_renormalised_nucleus():
+    z = _logits_of({0: 0.5, 1: 0.25, 2: 0.125, 3: 0.125})
+    assert np.allclose(decide.sampling_dist(z, 1.0, 1.0)[:4], [0.5, 0.25, 0.125, 0.125])
+    assert np.allclose(decide.sampling_dist(z, 1.0, 0.7)[:4], [2 / 3, 1 / 3, 0, 0])
+    assert np.allclose(decide.sampling_dist(z, 0.5, 1.0)[:4], [8 / 11, 2 / 11, 1 / 22, 1 / 22])
+    assert decide.sampling_dist(z, 1.0, 1.0)[4:].max() < 1e-100
+
+
+def test_verify_sample_worked_example():
+    """Draft q = (1/2, 1/4, 1/8, 1/8), target p uniform on bytes 0..3: byte 0
+    is kept iff u < p/q = 1/2; the residual max(0, p - q) = (0, 0, 1/8, 1/8)
+    splits at u_next = 1/2; byte 2 (p/q = 2) is always kept; after a full
+    acceptance the free byte is drawn from the last target (ties by id)."""
+    q = np.zeros(256); q[:4] = [0.5, 0.25, 0.125, 0.125]
+    p = np.zeros(256); p[:4] = 0.25
+    assert decide.verify_sample([0], [q], [p, p], [0.49], 0.9)[:2] == (1, 3)
+    assert decide.verify_sample([0], [q], [p, p], [0.51], 0.49)[:2] == (0, 2)
+    assert decide.verify_sample([0], [q], [p, p], [0.51], 0.51)[:2] == (0, 3)
+    assert decide.verify_sample([2, 0], [q, q], [p, p, p], [0.999, 0.7], 0.3)[:2] == (1, 2)
+    assert decide.verify_sample([2, 2], [q, q], [p, p, p], [0.999, 0.999], 0.3)[:2] == (2, 1)
+
+
+def test_verify_sample_keeps_the_target_distribution():
+    """Speculative sampling emits the target distribution: with the draft
+    byte drawn from q, the first emitted byte follows p exactly, and after a
+    full acceptance the free byte follows the next target.  Checked by
+    enumerating the draft byte (weight q) over a grid of both uniforms."""
+    rng = np.random.default_rng(21)
+    zq = np.full(257, -1e4); zp = np.full(257, -1e4); zn = np.full(257, -1e4)
+    zq[:6] = rng.normal(0, 1, 6); zp[:6] = rng.normal(0, 1, 6); zn[:6] = rng.normal(0, 1, 6)
+    q = decide.sampling_dist(zq, 1.0, 0.9)
+    p = decide.sampling_dist(zp, 0.7, 1.0)
+    pn = decide.sampling_dist(zn, 1.0, 1.0)
+    n = 96
+    first = np.zeros(256)
+    free = np.zeros(256)
+    accepted = 0.0
+    for x in np.flatnonzero(q):
+        for i in range(n):
+            for k in range(n):
+                a, b, _ = decide.verify_sample([x], [q], [p, pn], [(i + 0.5) / n], (k + 0.5) / n)
+                w = q[x] / n / n
+                if a == 1:
+                    first[x] += w
+                    free[b] += w
+                    accepted += w
+                else:
+                    first[b] += w
+    assert np.abs(first - p).max() < 3.0 / n
+    assert np.abs(free / accepted - pn).max() < 3.0 / n
+
+
+def test_verify_sample_greedy_limit_is_exact_match():
+    """With one-hot distributions (a vanishing top_p) rejection sampling is
+    the greedy exact-match rule, correction and free byte included."""
+    rng = np.random.default_rng(8)
+    for _ in range(30):
+        r = 4
+        zq = rng.normal(0, 1, (r, 257))
+        zp = rng.normal(0, 1, (r + 1, 257))
+        y = [decide.byte_choice(zp[j])[0] for j in range(r + 1)]
+        draft = [decide.byte_choice(zq[j])[0] for j in range(r)]
+        for j in range(r):
+            if rng.random() < 0.6:
+                draft[j] = y[j]
+        q = [decide.sampling_dist(zq[j], 1.0, 1e-9) for j in range(r)]
+        for j in range(r):                        # the draft's own one-hot distribution
+            q[j] = np.eye(256)[draft[j]]
+        p = [decide.sampling_dist(zp[j], 1.0, 1e-9) for j in range(r + 1)]
+        got = decide.verify_sample(draft, q, p, list(rng.random(r)), float(rng.random()))[:2]
+        assert got == decide.verify_accept(draft, y)
+
+
 def test_targets_worked_example():
     with open(os.path.join(GOLDEN, "targets_example.json")) as f:
         g = json.load(f)
@@ -550,6 +623,33 @@ def test_sampled_blt_d_limits_and_determinism(tiny):
     assert a.out == b.out and a.out != g.out
     for d, rec in enumerate(a.passes):
         assert rec["u"] == [decide.uniform(99, d * loops.MAX_BLOCK + j) for j in range(4)]
+
+
+def test_sampled_blt_s_and_dv_limits_and_determinism(tiny):
+    """Sampled BLT-S / BLT-DV (drafts drawn, rejection-sampling verification):
+    a vanishing top_p reproduces greedy BLT-S (= greedy BLT) and greedy
+    BLT-DV exactly; a seed reproduces its run; the verify draws follow the
+    counter layout (pass d: d*64 + j, appended byte d*64 + r)."""
+    wl, W, inp = tiny
+    g = loops.greedy(W, wl, inp, 24)
+    gs = loops.blt_s(W, wl, inp, 24, 4)
+    gdv = loops.blt_dv(W, wl, inp, 24, 4, 0.7, one_step=True)
+    lim_s = loops.blt_s(W, wl, inp, 24, 4, sampling=(1.0, 1e-9, 5))
+    lim_dv = loops.blt_dv(W, wl, inp, 24, 4, 0.7, one_step=True, sampling=(1.0, 1e-9, 5))
+    assert lim_s.out == gs.out == g.out and lim_s.n_dec == gs.n_dec and lim_s.accept == gs.accept
+    assert lim_dv.out == gdv.out and lim_dv.n_dec == gdv.n_dec and lim_dv.accept == gdv.accept
+    a = loops.blt_s(W, wl, inp, 24, 4, sampling=(1.0, 0.9, 7), trace=True)
+    b = loops.blt_s(W, wl, inp, 24, 4, sampling=(1.0, 0.9, 7))
+    assert a.out == b.out and a.out != g.out and len(a.out) == 24
+    for d, rec in enumerate(a.passes):
+        if rec["kind"] == "draft":
+            assert rec["u"] == decide.uniform(7, d * loops.MAX_BLOCK)
+        else:
+            r = len(rec["tokens"]) - 1
+            assert rec["u_acc"] == [decide.uniform(7, d * loops.MAX_BLOCK + j) for j in range(r)]
+            assert rec["u_next"] == decide.uniform(7, d * loops.MAX_BLOCK + r)
+    c = loops.blt_dv(W, wl, inp, 24, 4, 0.7, one_step=True, sampling=(1.0, 0.9, 7))
+    assert len(c.out) == 24 and c.out != gdv.out
 
 
 def test_blt_d_peaked_head_commits_several_per_pass():
