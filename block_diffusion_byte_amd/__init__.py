@@ -31,7 +31,7 @@ VOCAB = 257
 
 EXPORTS = [
     "blt_state_size", "blt_create", "blt_destroy", "blt_last_error", "blt_latents_put",
-    "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_bw_model",
+    "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_verify_sample", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
     "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
 ]
@@ -101,10 +101,11 @@ def lib():
             "blt_create": [P, P, P, P],
             "blt_destroy": [P],
             "blt_latents_put": [P, P, I32, P, P, P, I64],
-            "blt_kv_append": [P, P, I32, P, P, P, I32, P, P, P, P, P, P],
+            "blt_kv_append": [P, P, I32, P, P, P, I32, P, P, P, P, P, P, P, P],
             "blt_decode_block_step": [P, P, I32, P, P, P, I32, P, P, P, I32, P, F, I32, I32,
                                       P, P, P, P, P, P],
             "blt_verify_accept": [P, I32, P, I32, P, I32, P, I32, P, P],
+            "blt_verify_sample": [P, I32, P, I32, P, I32, P, I32, P, I32, P, P, P, P],
             "blt_bw_model": [P, P, P, P],
             "blt_session_create": [P, P, I32, P, P, P, P, P, P, I32, P],
             "blt_session_prefill": [P],
@@ -172,8 +173,22 @@ def blt_latents_put(ctx, state: blt_state, slot, idx, table, seq_stride: int):
                                                     _ptr(table), seq_stride), ctx)
 
 
+def _sampling(sampling, draw):
+    smp = smpp = dr = drp = None
+    if sampling is not None:
+        smp = blt_sampling(C.c_float(sampling[0]), C.c_float(sampling[1]), int(sampling[2]))
+        smpp = C.byref(smp)
+    if draw is not None:
+        dr, drp = _i32(draw)
+    return (smp, dr), smpp, drp
+
+
 def blt_kv_append(ctx, state, slot, start_pos, n_rows, n_max, lat_idx, bytes_=None,
-                  tokens_dev=None, argmax_out=None, conf_out=None, logits_out=None):
+                  tokens_dev=None, argmax_out=None, conf_out=None, logits_out=None, sampling=None,
+                  draw=None):
+    """sampling: None (greedy) or (temperature, top_p, seed); draw: one draw
+    index per sequence (required with sampling)."""
+    keep, smpp, drp = _sampling(sampling, draw)
     s, sp = _i32(slot)
     st, stp = _i32(start_pos)
     n, np_ = _i32(n_rows)
@@ -184,7 +199,7 @@ def blt_kv_append(ctx, state, slot, start_pos, n_rows, n_max, lat_idx, bytes_=No
         b, bp = _u8(np.asarray(bytes_).reshape(-1))
     _check("blt_kv_append", lib().blt_kv_append(
         ctx, C.byref(state), len(s), sp, stp, np_, n_max, bp, _ptr(tokens_dev), lip,
-        _ptr(argmax_out), _ptr(conf_out), _ptr(logits_out)), ctx)
+        _ptr(argmax_out), _ptr(conf_out), _ptr(logits_out), smpp, drp), ctx)
 
 
 def blt_decode_block_step(ctx, state, slot, start_pos, block_tok, B, block_lat, alpha,
@@ -214,6 +229,20 @@ def blt_decode_block_step(ctx, state, slot, start_pos, block_tok, B, block_lat, 
         ctx, C.byref(state), len(s), sp, stp, nap, n_append_max, abp, alp, _ptr(block_tok), B,
         blp, C.c_float(alpha), mode, mask, _ptr(argmax_out), _ptr(conf_out), _ptr(logits_out),
         _ptr(masked_left), smpp, drp), ctx)
+
+
+def blt_verify_sample(ctx, r, draft, ld_draft, zq, ld_q, zp, ld_p, sampling, draw, accept_len,
+                      next_byte, slot=None, batch=None):
+    """Rejection-sampling verification; sampling = (temperature, top_p, seed),
+    draw: the verify pass's draw index per sequence."""
+    keep, smpp, drp = _sampling(sampling, draw)
+    sp = None
+    if slot is not None:
+        sl, sp = _i32(slot)
+        batch = len(sl)
+    _check("blt_verify_sample", lib().blt_verify_sample(
+        ctx, batch, sp, r, _ptr(draft), ld_draft, _ptr(zq), ld_q, _ptr(zp), ld_p, smpp, drp,
+        _ptr(accept_len), _ptr(next_byte)), ctx)
 
 
 def blt_verify_accept(ctx, r, draft, ld_draft, pred, ld_pred, accept_len, next_byte, slot=None,

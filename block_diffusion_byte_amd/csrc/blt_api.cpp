@@ -502,10 +502,24 @@ static blt_status check_slots(blt_ctx *c, int32_t batch, const int32_t *slot, co
   return BLT_OK;
 }
 
+// Validation of a sampling request shared by the decode calls.
+static blt_status check_sampling(blt_ctx *c, const blt_sampling *sampling, const int32_t *draw,
+                                 int32_t batch, const char *fn) {
+  if (!sampling) return BLT_OK;
+  if (!(sampling->temperature > 0.f) || !isfinite(sampling->temperature) ||
+      !(sampling->top_p > 0.f && sampling->top_p <= 1.f) || !draw)
+    return fail(c, BLT_EINVAL, std::string(fn) + ": sampling needs temperature > 0, 0 < top_p <= 1 and draw");
+  for (int b = 0; b < batch; ++b)
+    if (draw[b] < 0 || (int64_t)draw[b] * kMaxBlock + kMaxBlock > INT32_MAX)
+      return fail(c, BLT_EINVAL, std::string(fn) + ": draw out of range");
+  return BLT_OK;
+}
+
 blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
                          const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
                          const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
-                         int32_t *argmax_out, float *conf_out, float *logits_out) {
+                         int32_t *argmax_out, float *conf_out, float *logits_out,
+                         const blt_sampling *sampling, const int32_t *draw) {
   if (!c) return BLT_EINVAL;
   const blt_config &g = c->cfg;
   static const char *fn = "blt_kv_append";
@@ -514,6 +528,10 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
   if (bs != BLT_OK) return bs;
   if (!start_pos || !n_rows || !lat_idx || n_max < 1 || (!bytes && !tokens_dev))
     return fail(c, BLT_EINVAL, "blt_kv_append: NULL argument or n_max < 1");
+  bs = check_sampling(c, sampling, draw, batch, fn);
+  if (bs != BLT_OK) return bs;
+  if (sampling && n_max > kMaxBlock)
+    return fail(c, BLT_EINVAL, "blt_kv_append: sampled passes take at most 64 rows per sequence");
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
   for (int b = 0; b < batch; ++b) {
@@ -528,14 +546,14 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
       if (li < 0 || li >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_kv_append: latent index beyond max_latents");
       const int dj = slot[b] * n_max + j;  // device arrays are indexed by slot
       RowDesc rd{slot[b], s0 + j, bytes ? (int)bytes[(size_t)b * n_max + j] : kTokFromDev, dj, li,
-                 s0 + j + 1, dj, 0, -1};
+                 s0 + j + 1, dj, 0, sampling ? draw[b] * kMaxBlock + j : -1};
       rows.push_back(rd);
     }
     seqs.push_back(sd);
   }
   if (rows.empty()) return BLT_OK;
   return run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
-                  conf_out, logits_out, nullptr);
+                  conf_out, logits_out, sampling);
 }
 
 blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
@@ -563,14 +581,8 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
     return fail(c, BLT_EINVAL, "blt_decode_block_step: alpha must be finite (an entropy bound: >= 0, may be +inf)");
   if (n_append_max < 0 || (n_append_max > 0 && (!n_append || !append_bytes || !append_lat)))
     return fail(c, BLT_EINVAL, "blt_decode_block_step: bad append arguments");
-  if (sampling) {
-    if (!(sampling->temperature > 0.f) || !isfinite(sampling->temperature) ||
-        !(sampling->top_p > 0.f && sampling->top_p <= 1.f) || !draw)
-      return fail(c, BLT_EINVAL, "blt_decode_block_step: sampling needs temperature > 0, 0 < top_p <= 1 and draw");
-    for (int b = 0; b < batch; ++b)
-      if (draw[b] < 0 || (int64_t)draw[b] * kMaxBlock + kMaxBlock > INT32_MAX)
-        return fail(c, BLT_EINVAL, "blt_decode_block_step: draw out of range");
-  }
+  bs = check_sampling(c, sampling, draw, batch, fn);
+  if (bs != BLT_OK) return bs;
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
   for (int b = 0; b < batch; ++b) {
@@ -619,6 +631,34 @@ blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int
   if (bs != BLT_OK) return bs;
   HIP_TRY(c, launch_verify(batch, c->seqs_d, r, draft, ld_draft, pred, ld_pred, accept_len,
                            next_byte, c->stream));
+  return BLT_OK;
+}
+
+blt_status blt_verify_sample(blt_ctx *c, int32_t batch, const int32_t *slot, int32_t r,
+                             const int32_t *draft, int32_t ld_draft, const float *zq, int32_t ld_q,
+                             const float *zp, int32_t ld_p, const blt_sampling *sampling,
+                             const int32_t *draw, int32_t *accept_len, int32_t *next_byte) {
+  if (!c) return BLT_EINVAL;
+  static const char *fn = "blt_verify_sample";
+  if (batch < 1 || batch > c->cfg.max_batch || r < 0 || r >= kMaxBlock || !draft || !zq || !zp ||
+      !accept_len || !next_byte || !sampling || ld_draft < r || ld_q < r || ld_p < r + 1)
+    return fail(c, BLT_EINVAL, "blt_verify_sample: bad argument (r must be below 64)");
+  blt_status bs = check_sampling(c, sampling, draw, batch, fn);
+  if (bs != BLT_OK) return bs;
+  std::vector<SeqDesc> seqs(batch);
+  std::vector<int64_t> draws(batch);
+  for (int b = 0; b < batch; ++b) {
+    const int s = slot ? slot[b] : b;
+    if (s < 0 || s >= c->cfg.max_batch) return fail(c, BLT_EINVAL, "blt_verify_sample: slot out of range");
+    seqs[b] = SeqDesc{s, 0, 0, 0, 0, 0, 0, s};
+    draws[b] = draw[b];
+  }
+  std::vector<RowDesc> no_rows;
+  bs = stage_pass(c, no_rows, seqs, &draws);
+  if (bs != BLT_OK) return bs;
+  const SampleArgs smp{sampling->temperature, sampling->top_p, sampling->seed};
+  HIP_TRY(c, launch_verify_sample(batch, c->seqs_d, c->offs_d, r, draft, ld_draft, zq, ld_q, zp, ld_p,
+                                  smp, accept_len, next_byte, c->stream));
   return BLT_OK;
 }
 

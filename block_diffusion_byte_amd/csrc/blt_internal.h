@@ -138,6 +138,12 @@ hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *s
                                 float *ent_ws, int report_entropy, int32_t *argmax_out,
                                 float *conf_out, float *logits_out, int32_t *block_tok,
                                 float alpha, int mode, int32_t *masked_left, hipStream_t s);
+// Rejection-sampling verification: draws[b] = the verify pass's draw index d of
+// sequence b (uniforms d*64 + j and d*64 + r of the stream seed + slot).
+hipError_t launch_verify_sample(int batch, const SeqDesc *seqs, const int64_t *draws, int r,
+                                const int32_t *draft, int ld_draft, const float *zq, int ld_q,
+                                const float *zp, int ld_p, const SampleArgs &smp,
+                                int32_t *accept_len, int32_t *next_byte, hipStream_t s);
 // dst = src^T, n x n elements of the context's dtype (set-up only).
 hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStream_t s);
 hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,

@@ -1557,6 +1557,100 @@ __global__ __launch_bounds__(256) void k_decide_unmask(const float *logits, cons
   if (w == 0) unmask_seq(sd, argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left);
 }
 
+// Probability of byte t (this thread's) under the distribution the top-p
+// sampler draws from, for the logits row zr: the nucleus of softmax(z / T),
+// renormalised; 0 outside it.  All 256 threads of the workgroup take part.
+// ew, red: LDS scratch (256 and 4 floats).
+__device__ float nucleus_prob(const float *zr, float temperature, float top_p, float *ew,
+                              float *red) {
+  const int t = threadIdx.x;
+  const float z = zr[t];
+  const float best = block_max256(z, red);
+  const float eT = expf((z - best) / temperature);
+  ew[t] = eT;
+  const float sT = block_sum256(eT, red);      // its barriers also publish ew
+  float before = 0.f;
+  for (int k = 0; k < 256; ++k) {
+    const float ek = ew[k];
+    before += (ek > eT || (ek == eT && k < t)) ? ek : 0.f;
+  }
+  const bool in = before < top_p * sT && eT > 0.f;
+  const float mass = block_sum256(in ? eT : 0.f, red);
+  __syncthreads();                            // ew fully read before the next use
+  return in ? eT / mass : 0.f;
+}
+
+// Rejection-sampling verification of sampled drafts (speculative sampling):
+// workgroup b takes sequence b, thread t byte t.  For draft byte j (in
+// order) with draft distribution q (from the logits it was drawn from) and
+// target p (from verify row j): kept iff u_j * q(x) < p(x); at the first
+// rejection the appended byte is drawn from max(0, p - q) renormalised,
+// bytes in id order; after a full acceptance it is drawn from the last
+// target as the top-p sampler draws (bytes ranked by probability, ties by
+// id).  u_j: draw d*64 + j, the appended byte's uniform: draw d*64 + r, of
+// the stream seed + slot (SplitMix64 as in k_decide_sample), d = draws[b].
+__global__ __launch_bounds__(256) void k_verify_sample(const SeqDesc *seqs, const int64_t *draws,
+                                                      int r, const int32_t *draft, int ld_draft,
+                                                      const float *zq, int ld_q, const float *zp,
+                                                      int ld_p, SampleArgs smp,
+                                                      int32_t *accept_len, int32_t *next_byte) {
+  __shared__ float ew[256];
+  __shared__ float red[4];
+  __shared__ float px, qx;
+  const int t = threadIdx.x;
+  const int s = seqs[blockIdx.x].slot;
+  const uint64_t stream = smp.seed + (uint64_t)s, base = (uint64_t)draws[blockIdx.x] * kMaxBlock;
+  const float u_next = (float)(splitmix64_nth(stream, base + r + 1) >> 40) * (1.f / 16777216.f);
+  for (int j = 0; j < r; ++j) {
+    const int x = draft[(int64_t)s * ld_draft + j];
+    const float q = nucleus_prob(zq + ((int64_t)s * ld_q + j) * kVocab, smp.temperature, smp.top_p, ew, red);
+    const float p = nucleus_prob(zp + ((int64_t)s * ld_p + j) * kVocab, smp.temperature, smp.top_p, ew, red);
+    if (t == x) {
+      qx = q;
+      px = p;
+    }
+    __syncthreads();
+    const float u = (float)(splitmix64_nth(stream, base + j + 1) >> 40) * (1.f / 16777216.f);
+    if (u * qx < px) {                          // kept (uniform branch)
+      __syncthreads();                          // px, qx read before the next draft byte
+      continue;
+    }
+    // residual max(0, p - q): the first byte, in id order, whose cumulative
+    // residual mass exceeds u_next times the total
+    const float res = fmaxf(p - q, 0.f);
+    ew[t] = res;
+    const float total = block_sum256(res, red);
+    float cum = 0.f;
+    for (int k = 0; k <= t; ++k) cum += ew[k];
+    const float c = u_next * total;
+    const float pick = -block_max256(cum > c ? -(float)t : -256.f, red);
+    if (t == 0) {
+      accept_len[s] = j;
+      next_byte[s] = min((int)pick, 255);
+    }
+    return;
+  }
+  // all r kept: the free byte from the last target, ranked draw
+  const float p = nucleus_prob(zp + ((int64_t)s * ld_p + r) * kVocab, smp.temperature, smp.top_p, ew, red);
+  ew[t] = p;
+  __syncthreads();
+  float before = 0.f;
+  int rank = 0;
+  for (int k = 0; k < 256; ++k) {
+    const float pk = ew[k];
+    const bool prior = pk > p || (pk == p && k < t);
+    before += prior ? pk : 0.f;
+    rank += prior;
+  }
+  const bool cand = p > 0.f && before <= u_next;
+  const float top = block_max256(cand ? (float)rank : -1.f, red);
+  const float pick = block_max256(cand && (float)rank == top ? (float)t : -1.f, red);
+  if (t == 0) {
+    accept_len[s] = r;
+    next_byte[s] = (int)pick;
+  }
+}
+
 // Greedy exact-match acceptance: leading draft bytes equal to the prediction
 // made one position earlier; the prediction at the first mismatch (or after
 // the last draft byte) is appended.
@@ -1772,6 +1866,15 @@ hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *s
   hipLaunchKernelGGL(k_decide_unmask, dim3(n_seq), dim3(256), 0, s, logits, seqs, rows, argmax_ws,
                      conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, block_tok,
                      alpha, mode, masked_left);
+  return hipGetLastError();
+}
+
+hipError_t launch_verify_sample(int batch, const SeqDesc *seqs, const int64_t *draws, int r,
+                                const int32_t *draft, int ld_draft, const float *zq, int ld_q,
+                                const float *zp, int ld_p, const SampleArgs &smp,
+                                int32_t *accept_len, int32_t *next_byte, hipStream_t s) {
+  hipLaunchKernelGGL(k_verify_sample, dim3(batch), dim3(256), 0, s, seqs, draws, r, draft, ld_draft,
+                     zq, ld_q, zp, ld_p, smp, accept_len, next_byte);
   return hipGetLastError();
 }
 

@@ -162,11 +162,20 @@ blt_status blt_latents_put(blt_ctx *ctx, const blt_state *st, int32_t n, const i
  * runs as one causal (flash) pass over its keys, tiles of 128 rows at a
  * time; shorter ones take the split-K decode kernel.  Either way a row's
  * result depends only on its own inputs and on which of the two kernels its
- * sequence took (the two agree to rounding). */
+ * sequence took (the two agree to rounding).
+ * sampling (nullable; see blt_decode_block_step): argmax_out then receives
+ * each row's drawn byte (row j of sequence b draws n = draw[b]*64 + j; at
+ * most 64 rows per sequence) and conf_out the model probability of it. */
+typedef struct {
+  float temperature;
+  float top_p;
+  uint64_t seed;
+} blt_sampling;
 blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const int32_t *slot,
                          const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
                          const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
-                         int32_t *argmax_out, float *conf_out, float *logits_out);
+                         int32_t *argmax_out, float *conf_out, float *logits_out,
+                         const blt_sampling *sampling, const int32_t *draw);
 
 /* One BLT-D decoder pass (pytorch.kr summary, "BLT-D inference" and
  * "BLT-D attention mask").  For sequence b: n_append[b] clean rows at
@@ -197,11 +206,6 @@ blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const
  * (temperature 1): the probability of the drawn byte, and the entropy of
  * softmax(z).  Requires a bfloat16 or float32 context alike; temperature
  * > 0 and finite, 0 < top_p <= 1, draw[b] * 64 + 63 < 2^31. */
-typedef struct {
-  float temperature;
-  float top_p;
-  uint64_t seed;
-} blt_sampling;
 blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batch,
                                  const int32_t *slot, const int32_t *start_pos,
                                  const int32_t *n_append, int32_t n_append_max,
@@ -222,6 +226,25 @@ blt_status blt_decode_block_step(blt_ctx *ctx, const blt_state *st, int32_t batc
 blt_status blt_verify_accept(blt_ctx *ctx, int32_t batch, const int32_t *slot, int32_t r,
                              const int32_t *draft, int32_t ld_draft, const int32_t *pred,
                              int32_t ld_pred, int32_t *accept_len, int32_t *next_byte);
+
+/* Verification of sampled drafts by rejection sampling (pytorch.kr summary,
+ * "BLT-S and BLT-DV": sampling at temperature > 0 extends the verification
+ * with rejection sampling; the standard speculative-sampling rule is taken).
+ * For sequence slot s = slot[b] (slot NULL: s = b): draft[s*ld_draft+j]
+ * (device int32, j < r) the draft bytes; zq[(s*ld_q+j)*257+v] (device f32)
+ * the logits draft byte j was drawn from; zp[(s*ld_p+j)*257+v] (j <= r) the
+ * logits of causal verify row l+j.  With q_j, p_j the distributions the
+ * top-p sampler draws from (`sampling`), draft byte j is kept iff
+ * u_j * q_j(x) < p_j(x); at the first rejection the byte appended is drawn
+ * from max(0, p_j - q_j) renormalised (bytes in id order: the first whose
+ * cumulative mass exceeds u' times the total); if all r are kept it is drawn
+ * from p_r as the top-p sampler draws.  u_j = draw n = draw[b]*64 + j, u' =
+ * draw[b]*64 + r of the stream seed + s (as in blt_decode_block_step).
+ * Outputs accept_len[s], next_byte[s] (device int32).  r < 64. */
+blt_status blt_verify_sample(blt_ctx *ctx, int32_t batch, const int32_t *slot, int32_t r,
+                             const int32_t *draft, int32_t ld_draft, const float *zq, int32_t ld_q,
+                             const float *zp, int32_t ld_p, const blt_sampling *sampling,
+                             const int32_t *draw, int32_t *accept_len, int32_t *next_byte);
 
 /* Kernel timing with HIP events on the context's stream (profiling aid).
  * While a family is enabled, every launch of it is stamped by its own
@@ -290,11 +313,13 @@ typedef struct {
   blt_unmask unmask;
   blt_block_mask block_mask;
   int32_t n_gen;            /* bytes to generate per sequence */
-  /* Sampled BLT-D (temperature > 0): the bytes of sequence b are drawn as in
-   * blt_decode_block_step with seed `seed` (stream seed + b) and draw[b] =
-   * the sequence's decoder passes so far in this call.  temperature = 0:
-   * greedy.  Other policies with temperature > 0 return BLT_ENOTIMPL (their
-   * verification would need rejection sampling). */
+  /* Sampling (temperature > 0; 0 = greedy): bytes of sequence b are drawn
+   * as in blt_decode_block_step with stream seed + b, pass d of the
+   * sequence's generation (its decoder passes so far) drawing n = d*64 + j.
+   * Greedy BLT: each pass draws the next byte.  BLT-D: block positions draw
+   * their bytes.  BLT-S: draft bytes are drawn and the draft is verified by
+   * blt_verify_sample (the verify pass is pass d).  BLT-DV: one-step drafts
+   * only (unmask ONE_STEP, else BLT_ENOTIMPL), verified the same way. */
   float temperature;
   float top_p;
   uint64_t seed;

@@ -92,12 +92,14 @@ class Replayer:
             self.blt.blt_kv_append(self.dec.ctx, self.dec.state, [self.slot], [c0], [m], m,
                                    taus[c0:c0 + m], bytes_=x[c0:c0 + m])
 
-    def rows(self, rec):
-        """Run a clean-row pass; return (logits [n, 257], argmax [n])."""
+    def rows(self, rec, sampling=None, draw=None):
+        """Run a clean-row pass; return (logits [n, 257], argmax [n]) (the
+        drawn bytes when sampling)."""
         n = len(rec["tokens"])
         self.blt.blt_kv_append(self.dec.ctx, self.dec.state, [self.slot], [rec["start"]], [n], n,
                                rec["targets"], bytes_=rec["tokens"], argmax_out=self.argmax,
-                               logits_out=self.logits)
+                               logits_out=self.logits, sampling=sampling,
+                               draw=None if draw is None else [draw])
         self.torch.cuda.synchronize()
         base = self.slot * n
         z = self.logits[base * 257:(base + n) * 257].view(n, 257).cpu().numpy()

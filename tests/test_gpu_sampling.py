@@ -119,6 +119,87 @@ def test_mini_bf16_sampled_blt_d_entropy_teacher_forced():
     _replay_sampled(wl, "entropy", 3.0, (1.0, 0.8, 77), n_gen=24)
 
 
+def _replay_verify(wl, policy, r, sampling, n_gen=24):
+    """Teacher-forced replay of a sampled BLT-S (drafts of r bytes) or
+    one-step BLT-DV (blocks of r) oracle trace: draft passes draw on the GPU,
+    the verify pass runs the causal rows, then blt_verify_sample decides
+    from the GPU's own draft and verify logits.  The decision (accepted count
+    and appended byte) is compared with the oracle's rule applied to the
+    GPU's logits wherever that margin exceeds 1e-5, and with the oracle's own
+    decision wherever its margin exceeds the probability error the logit
+    tolerance allows."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    w = bltgen.make_weights(wl, gains="random")
+    W, inp, inp64 = oracle_inputs(wl, w)
+    temp, top_p, seed = sampling
+    if policy == "blt_s":
+        run = loops.blt_s(W, wl, inp64, n_gen, r, trace=True, sampling=sampling)
+    else:
+        run = loops.blt_dv(W, wl, inp64, n_gen, r, 0.0, one_step=True, trace=True, sampling=sampling)
+    dec = decoder_for(wl.replace(block=r), w, max_batch=1, max_rows=256)
+    dev = "cuda:0"
+    zq_d = torch.zeros((r, 257), dtype=torch.float32, device=dev)
+    zp_d = torch.zeros((r + 1, 257), dtype=torch.float32, device=dev)
+    draft_d = torch.zeros(r, dtype=torch.int32, device=dev)
+    acc_d = torch.zeros(1, dtype=torch.int32, device=dev)
+    nxt_d = torch.zeros(1, dtype=torch.int32, device=dev)
+    stats = dict(rounds=0, vs_rule=0, vs_oracle=0, worst=0.0)
+    try:
+        rp = Replayer(dec, wl, inp)
+        rp.prefill(inp)
+        zq = []
+        for d, rec in enumerate(run.passes):
+            if rec["kind"] == "draft":
+                z, am = rp.rows(rec, sampling=sampling, draw=d)
+                zq.append(z[0])
+                if rec["gap"][0] > 2.5 * FP32_REL * np.abs(np.asarray(rec["logits"])[0]).max() / temp:
+                    assert am[0] == rec["choice"][0], f"pass {d}: drew {am[0]}, oracle {rec['choice'][0]}"
+                continue
+            if rec["kind"] == "block":
+                z, am, _, after, _ = rp.block(rec, 0.0, "one_step", sampling=sampling, draw=d)
+                zq = [z[j] for j in range(r)]
+                continue
+            # verify pass: rows l..l+r, then the rejection-sampling decision
+            z, _ = rp.rows(rec)
+            ref = np.asarray(rec["logits"])
+            ok, err, tol = logits_ok(z, ref, wl.dtype, wl.head_scale)
+            assert ok, f"pass {d}: logits err {err} > {tol}"
+            stats["worst"] = max(stats["worst"], err)
+            draft = [int(t) for t in rec["tokens"][1:]]
+            zq_d.copy_(torch.from_numpy(np.stack(zq)).float())
+            zp_d.copy_(torch.from_numpy(z[:r + 1]).float())
+            draft_d.copy_(torch.tensor(draft, dtype=torch.int32))
+            blt.blt_verify_sample(dec.ctx, r, draft_d, r, zq_d, r, zp_d, r + 1, sampling, [d], acc_d,
+                                  nxt_d, slot=[0])
+            torch.cuda.synchronize()
+            got = (int(acc_d.item()), int(nxt_d.item()))
+            q = [decide.sampling_dist(zq[j], temp, top_p) for j in range(r)]
+            p = [decide.sampling_dist(z[j], temp, top_p) for j in range(r + 1)]
+            a, b, margin = decide.verify_sample(draft, q, p, rec["u_acc"], rec["u_next"])
+            if margin > 1e-5:
+                assert got == (a, b), f"pass {d}: GPU {got}, rule on GPU logits {(a, b)}"
+                stats["vs_rule"] += 1
+            eps = FP32_REL * np.abs(ref).max()
+            if rec["margin"] > 4 * 2.5 * eps / temp:
+                assert got == (rec["accept"], rec["next"]), f"pass {d}: GPU {got}, oracle {(rec['accept'], rec['next'])}"
+                stats["vs_oracle"] += 1
+            stats["rounds"] += 1
+            zq = []
+    finally:
+        dec.close()
+    say(f"sampled {policy} (r={r}, T={temp}, top_p={top_p}): {stats['rounds']} verifications, worst logit "
+        f"err {stats['worst']:.3g}, {stats['vs_rule']} decisions vs the rule on GPU logits, "
+        f"{stats['vs_oracle']} vs the oracle's")
+    assert stats["vs_rule"] > 0 and stats["vs_oracle"] > 0
+
+
+@pytest.mark.parametrize("policy,r", [("blt_s", 4), ("blt_dv", 4)])
+def test_tiny_fp32_rejection_sampling_verify_teacher_forced(policy, r):
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    _replay_verify(wl, policy, r, (0.8, 0.9, 4321))
+
+
 def _session(wl, w, inps, n_gen, block, alpha, unmask, temp, top_p, seed, policy=None):
     import torch
     import block_diffusion_byte_amd as blt
@@ -159,13 +240,39 @@ def test_sampled_sessions_are_seeded_and_reach_the_greedy_limit():
     say(f"sampled sessions: seeded, n_dec {[r['n_dec'] for r in a]}; top_p -> 0 equals greedy")
 
 
+@pytest.mark.parametrize("policy", ["greedy", "blt_s", "blt_dv"])
+def test_sampled_verified_sessions_are_seeded_and_reach_the_greedy_limit(policy):
+    """Sampled greedy BLT, BLT-S and one-step BLT-DV sessions (rejection-
+    sampling verification): a seed reproduces its bytes, another seed gives
+    others, and a vanishing top_p gives the greedy session exactly."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    w = bltgen.make_weights(wl, gains="random")
+    inps = [bltgen.make_sequence_inputs(wl, b) for b in range(3)]
+    pid = {"greedy": blt.BLT_POLICY_GREEDY, "blt_s": blt.BLT_POLICY_BLT_S,
+           "blt_dv": blt.BLT_POLICY_BLT_DV}[policy]
+    block = {"greedy": 1, "blt_s": 4, "blt_dv": 4}[policy]
+    O = blt.BLT_UNMASK_ONE_STEP
+    a = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 5, policy=pid)
+    b = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 5, policy=pid)
+    c = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 6, policy=pid)
+    assert [r["out"] for r in a] == [r["out"] for r in b]
+    assert [r["out"] for r in a] != [r["out"] for r in c]
+    assert all(r["n"] == 32 for r in a)
+    g = _session(wl, w, inps, 32, block, 0.0, O, 0.0, 1.0, 0, policy=pid)
+    lim = _session(wl, w, inps, 32, block, 0.0, O, 1.0, 1e-7, 5, policy=pid)
+    assert [(r["out"], r["n_dec"], r["accepted"]) for r in lim] == \
+        [(r["out"], r["n_dec"], r["accepted"]) for r in g]
+    say(f"sampled {policy} sessions: seeded; top_p -> 0 equals greedy; n_dec {[r['n_dec'] for r in a]}")
+
+
 def test_sampling_argument_errors():
     import block_diffusion_byte_amd as blt
     wl = bltgen.WORKLOADS[0]
     w = bltgen.make_weights(wl)
     inps = [bltgen.make_sequence_inputs(wl, 0)]
-    with pytest.raises(blt.BltError) as ei:
-        _session(wl, w, inps, 8, 8, 0.0, 0, 1.0, 0.9, 1, policy=blt.BLT_POLICY_BLT_S)
+    with pytest.raises(blt.BltError) as ei:       # threshold BLT-DV drafts are not verifiable here
+        _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.9, 1, policy=blt.BLT_POLICY_BLT_DV)
     assert ei.value.status == blt.BLT_ENOTIMPL
     with pytest.raises(blt.BltError) as ei:
         _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.0, 1)
