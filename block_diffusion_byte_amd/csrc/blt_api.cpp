@@ -173,8 +173,9 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     a.W = lw.wqkv; a.N = 3 * d; a.K = d;
     a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_attn;
     a.ep = EP_STORE_F32; a.out_f32 = c->qkv; a.ldo = 3 * d;
-    if (gemv_path(bf, R)) {
-      // RoPE and the KV write happen in the projection's epilogue
+    // RoPE and the KV write happen in the projection's epilogue (on the
+    // MFMA path when a 64-column tile holds whole heads)
+    if (gemv_path(bf, R) || geo.d_head <= 64) {
       a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
       a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = kv_rows(g.max_ctx); a.layer = l;
       HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));

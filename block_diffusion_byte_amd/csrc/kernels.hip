@@ -234,6 +234,34 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
   }
 }
 
+// The same epilogue for a pair addressed by its natural QKV column n (the
+// first half of a head; the second is n + d_h/2), as the MFMA path lays out
+// its outputs: q kept in f32 (RoPE), k (RoPE) and v written to the cache.
+template <bool BF>
+__device__ __forceinline__ void qkv_rope_store_col(const GemmArgs &a, int r, int n, float y0,
+                                                   float y1, int pos, int slot, float2 cs) {
+  using T = typename Act<BF>::T;
+  const int half = a.d_head >> 1, sec = n / a.d, c = n - sec * a.d;
+  const int hh = c / a.d_head, j = c - hh * a.d_head;
+  if (sec == 0) {
+    a.q_out[(int64_t)r * a.d + c] = y0 * cs.x - y1 * cs.y;
+    a.q_out[(int64_t)r * a.d + c + half] = y1 * cs.x + y0 * cs.y;
+    return;
+  }
+  const int64_t plane = (int64_t)a.max_ctx * a.d_head;
+  const int64_t head = (((int64_t)slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
+  T *kv = (T *)a.kv;
+  if (sec == 1) {
+    const int64_t base = head * plane + (int64_t)pos * a.d_head + j;
+    kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
+    kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
+  } else {
+    const int64_t vb = head * plane + (int64_t)j * a.max_ctx + pos;   // V transposed
+    kv[vb] = from_f<T>(y0);
+    kv[vb + (int64_t)half * a.max_ctx] = from_f<T>(y1);
+  }
+}
+
 // Raw activation data of one 16-byte staged chunk: the chunk itself (plain
 // input) or the f32 residual values it is made from (RMSNorm prologue).
 template <bool BF, int PRO> struct StageRaw;
@@ -469,8 +497,12 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   constexpr int LA = BM * CH / 256, LB = BN * CH / 256;  // chunks per thread per step
   constexpr int TM = BM / 32, TN = BN / 32;         // 16x16 tiles per wave
   static_assert(P % 2 == 0, "prefetch slots in pairs (two LDS buffers)");
-  __shared__ __align__(16) u32x4_t sa[2][BM * CH];
-  __shared__ __align__(16) u32x4_t sb[2][BN * CH];
+  // operand tiles (two buffers each); after the K loop the same LDS holds
+  // the f32 output tile for the QKV+RoPE epilogue
+  __shared__ __align__(16) u32x4_t smem[2 * BM * CH + 2 * BN * CH];
+  static_assert(BM * BN * 4 <= (int)sizeof(smem), "output tile fits the operand buffers");
+  u32x4_t (*sa)[BM * CH] = reinterpret_cast<u32x4_t (*)[BM * CH]>(smem);
+  u32x4_t (*sb)[BN * CH] = reinterpret_cast<u32x4_t (*)[BN * CH]>(smem + 2 * BM * CH);
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
   const int mt = (a.R + BM - 1) / BM, nt = (a.N + BN - 1) / BN, ntiles = mt * nt;
   const int tile = (ntiles & 7) ? (int)blockIdx.x
@@ -552,6 +584,31 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     });
   }
   // acc[i][j][v]: row wr+16i+4(l/16)+v, column wc+16j+l%16 of the tile
+  if (a.qkv_rope) {
+    // QKV projection with RoPE and the KV write: the tile goes through LDS
+    // so each thread can take (j, j + d_h/2) pairs of one head (the tile's
+    // columns start on a head boundary: BN is a multiple of d_h)
+    float *ct = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          ct[(wr + i * 16 + 4 * (l >> 4) + v) * BN + wc + j * 16 + (l & 15)] = acc[i][j][v];
+    __syncthreads();
+    const int half = a.d_head >> 1;
+    for (int it = t; it < BM * (BN / 2); it += 256) {
+      const int rr = it / (BN / 2), pc = it - rr * (BN / 2);
+      const int c = (pc / half) * a.d_head + pc % half;   // first column of the pair
+      const int m = m0 + rr, n = n0 + c;
+      if (m >= a.R || n >= a.N) continue;
+      const RowDesc rd = a.rows[m];
+      qkv_rope_store_col<true>(a, m, n, ct[rr * BN + c], ct[rr * BN + c + half], rd.pos, rd.slot,
+                               a.rope_tab[(int64_t)rd.pos * half + (n % a.d_head)]);
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
