@@ -164,6 +164,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
   HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, p.block_tok,
                           p.tokens_dev, c->h, s));
   KVGeom geo{L, g.n_heads, d / g.n_heads, kv_rows(g.max_ctx)};
+  c->split.splits = 0;               // no sum left pending by an interrupted pass
   for (int l = 0; l < L; ++l) {
     const blt_layer_weights &lw = c->layers[l];
     GemmArgs a = base_args(c);
@@ -178,9 +179,9 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     if (gemv_path(bf, R) || geo.d_head <= 64) {
       a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
       a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = kv_rows(g.max_ctx); a.layer = l;
-      HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+      HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
     } else {
-      HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+      HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
       HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
     }
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -197,27 +198,28 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     a.W = lw.wo; a.N = d; a.K = d;
     a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
     a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
-    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
     // f = SiLU(W1 RMSNorm(h))
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.w1; a.N = F; a.K = d;
     a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_ffn;
     a.ep = EP_SILU_ACT; a.out_act = c->xa; a.ldo = F;
-    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
     // h += W2 f (+ the next layer's cross-attention contribution)
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.w2; a.N = d; a.K = F;
     a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = F;
     a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
     if (l + 1 < L) { a.cross = cross; a.cross_layer = l + 1; }
-    HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
   }
   GemmArgs a = base_args(c);
   a.R = R; a.rows = c->rows_d;
   a.W = c->w.w_out; a.N = kVocab; a.K = d;
   a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
-  HIP_TRY(c, launch_gemm(bf, a, c->rinv, c->xb, s));
+  HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+  if (c->split.splits) return fail(c, BLT_EHIP, "enqueue_pass: a split residual sum was left pending");
   const int rep_ent = p.unmask && p.mode == BLT_UNMASK_ENTROPY;
   if (p.unmask && !p.sample) {
     HIP_TRY(c, launch_decide_unmask(c->logits, S, c->seqs_d, c->rows_d, c->argmax_ws, c->conf_ws,
@@ -370,7 +372,11 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(dalloc(&c->q, (size_t)R * d));
   chk(dalloc(&c->part, (size_t)R * H * c->max_chunks * (dh + 2)));
   chk(dalloc(&c->logits, (size_t)R * kVocab));
-  chk(dalloc(&c->rinv, (size_t)R));
+  // partial products of split-K residual GEMMs (MFMA path: bf16, >= 16 rows)
+  if (c->bf16 && R >= kGemvRows) {
+    c->split.cap = std::min<size_t>((size_t)8 * R * d, (size_t)1 << 22);
+    chk(dalloc(&c->split.ws, c->split.cap));
+  }
   chk(dalloc(&c->conf_ws, (size_t)R));
   chk(dalloc(&c->ent_ws, (size_t)R));
   chk(dalloc(&c->argmax_ws, (size_t)R));
@@ -418,7 +424,7 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
       a.R = d; a.W = tmp; a.N = d; a.K = d;
       a.pro = PRO_PLAIN; a.X = lw.wo_c; a.ldx = d;
       a.ep = EP_STORE_ACT; a.out_act = (char *)c->cross_w + (size_t)l * d * d * e; a.ldo = d;
-      chk(launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+      chk(launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
     }
     chk(hipStreamSynchronize(c->stream));
     if (tmp) (void)hipFree(tmp);
@@ -436,7 +442,7 @@ blt_status blt_destroy(blt_ctx *c) {
   (void)hipStreamSynchronize(c->stream);
   drop_graphs(c);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
-  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->rinv, c->conf_ws, c->ent_ws, c->argmax_ws,
+  void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->split.ws, c->conf_ws, c->ent_ws, c->argmax_ws,
                   c->xa, c->xb, c->desc_d, c->rope_tab, c->cross_w};
   for (void *p : bufs)
     if (p) (void)hipFree(p);
@@ -480,13 +486,13 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
     a.R = m; a.W = c->w.w_lat; a.N = d; a.K = g.d_global;
     a.pro = PRO_PLAIN; a.X = table; a.x_row_off = c->offs_d;
     a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
-    HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
     // cross[slot][idx][l][:] = C_l o~ for every layer at once (N = L*d)
     a = base_args(c);
     a.R = m; a.W = c->cross_w; a.N = L * d; a.K = d;
     a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
     a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = c->offs_d + m;
-    HIP_TRY(c, launch_gemm(c->bf16, a, c->rinv, c->xb, c->stream));
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
   }
   return BLT_OK;
 }

@@ -62,7 +62,7 @@ struct blt_ctx {
   float *q = nullptr;         // RoPE'd queries [R][d]
   float *part = nullptr;      // attention chunk partials [R][H][max_chunks][dh+2]
   float *logits = nullptr;    // [R][257]
-  float *rinv = nullptr;      // [R]
+  blt::SplitResid split;      // split-K residual products (MFMA path)
   float *conf_ws = nullptr;   // [R]
   float *ent_ws = nullptr;    // [R] entropy of each row (nats)
   int32_t *argmax_ws = nullptr;

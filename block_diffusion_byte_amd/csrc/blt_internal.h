@@ -56,7 +56,9 @@ struct SeqDesc {
   int32_t attn_flash;    // 1: self-attention by the causal kernel (clean rows only, >= kFlashMinRows)
 };
 
-enum Epilogue { EP_STORE_F32 = 0, EP_RESID = 1, EP_SILU_ACT = 2, EP_STORE_ACT = 3, EP_ROWOFF_F32 = 4 };
+// EP_PART (MFMA GEMM only): split y's partial product to out_f32[split][R][N]
+enum Epilogue { EP_STORE_F32 = 0, EP_RESID = 1, EP_SILU_ACT = 2, EP_STORE_ACT = 3, EP_ROWOFF_F32 = 4,
+                EP_PART = 5 };
 enum Prologue { PRO_PLAIN = 0, PRO_NORM = 1 };
 
 // y[r][o] = sum_i W[o][i] * x[r][i] for r < R, o < N.
@@ -104,8 +106,19 @@ struct KVGeom {
 };
 
 // Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.
-hipError_t launch_gemm(bool bf16, const GemmArgs &a, float *rinv_ws, void *xnorm_ws,
-                       hipStream_t s);
+// A residual product (EP_RESID) on the MFMA path whose K was split: its
+// partial products wait in ws[splits][R][N], and the next RMSNorm prologue
+// over the same residual adds them (in split order) and the cross term.
+struct SplitResid {
+  float *ws = nullptr;
+  size_t cap = 0;        // floats in ws
+  int splits = 0;        // 0: nothing pending
+  GemmArgs a{};          // the pending product's arguments
+};
+// sr (nullable) allows residual products to split K and carries a pending
+// sum to the RMSNorm prologue that must take it; xnorm_ws holds the
+// normalised activations of the MFMA path.
+hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr, hipStream_t s);
 hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
                         int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
                         const int32_t *tokens_dev, float *h, hipStream_t s);

@@ -508,7 +508,10 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   const int tile = (ntiles & 7) ? (int)blockIdx.x
                                 : (int)(blockIdx.x & 7) * (ntiles >> 3) + (int)(blockIdx.x >> 3);
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
-  const uint16_t *X = (const uint16_t *)a.X, *W = (const uint16_t *)a.W;
+  // split-K: workgroup row y of the grid takes K steps [y nk, (y+1) nk)
+  const int nk = a.K / kGemmBK / (int)gridDim.y;   // a multiple of P (checked at launch)
+  const int64_t k0 = (int64_t)blockIdx.y * nk * kGemmBK;
+  const uint16_t *X = (const uint16_t *)a.X + k0, *W = (const uint16_t *)a.W + k0;
   // this thread's chunks of each step: tile chunk q = t + 256 i (row q / CH,
   // column q % CH); rows past the matrix edge re-read its last row
   const uint16_t *ga[LA], *gb[LB];
@@ -531,7 +534,6 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int wr = (w >> 1) * (BM / 2), wc = (w & 1) * (BN / 2);
-  const int nk = a.K / kGemmBK;              // a multiple of P (K % 256 == 0)
   u32x4_t xa[P][LA], xb[P][LB];              // register slots: step s waits in slot s % P
 
   auto load = [&](u32x4_t (&ra)[LA], u32x4_t (&rb)[LB], int kt) {
@@ -617,22 +619,44 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
       for (int v = 0; v < 4; ++v) {
         const int m = m0 + wr + i * 16 + 4 * (l >> 4) + v;
         const int n = n0 + wc + j * 16 + (l & 15);
-        if (m < a.R && n < a.N)
+        if (m >= a.R || n >= a.N) continue;
+        if (a.ep == EP_PART)                 // this split's partial product
+          a.out_f32[((int64_t)blockIdx.y * a.R + m) * a.N + n] = acc[i][j][v];
+        else
           epilogue<true>(a, m, n, acc[i][j][v],
                          a.ep == EP_RESID ? resid_operands(a, m, n) : ResidEpi{0.f, 0.f});
       }
 }
 
-// RMSNorm rows into an activation buffer (MFMA path prologue).
-template <bool BF>
-__global__ __launch_bounds__(256) void k_rmsnorm_act(const float *H, int64_t ldh, const void *gain,
-                                                     int K, float eps, void *out) {
+// RMSNorm rows into an activation buffer (MFMA path prologue).  PEND: a
+// split-K residual product is pending (partial products p.out_f32[split][R][K],
+// its cross term per p.cross): the row first takes h += (sum + cross), the
+// partials added in split order, as the product's own epilogue would.
+template <bool BF, bool PEND>
+__global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, const void *gain,
+                                                     int K, float eps, void *out, GemmArgs p,
+                                                     int splits) {
   using T = typename Act<BF>::T;
   __shared__ float part[4];
   const int r = blockIdx.x, t = threadIdx.x;
-  const float *hr = H + (int64_t)r * ldh;
+  float *hr = H + (int64_t)r * ldh;
   float ss = 0.f;
-  for (int k = t; k < K; k += 256) ss = fmaf(hr[k], hr[k], ss);
+  if constexpr (PEND) {
+    const float *cr = nullptr;
+    if (p.cross) {
+      const RowDesc rd = p.rows[r];
+      cr = p.cross + (((int64_t)rd.slot * p.max_lat + rd.lat) * p.n_layers + p.cross_layer) * p.d;
+    }
+    for (int k = t; k < K; k += 256) {
+      float y = p.out_f32[(int64_t)r * K + k];
+      for (int sp = 1; sp < splits; ++sp) y += p.out_f32[((int64_t)sp * p.R + r) * K + k];
+      const float v = hr[k] + (y + (cr ? cr[k] : 0.f));
+      hr[k] = v;
+      ss = fmaf(v, v, ss);
+    }
+  } else {
+    for (int k = t; k < K; k += 256) ss = fmaf(hr[k], hr[k], ss);
+  }
   ss = wave_sum(ss);
   if ((t & 63) == 0) part[t >> 6] = ss;
   __syncthreads();
@@ -1794,15 +1818,45 @@ bool gemv_supported(bool bf16, int K) {
          nc == 24;  // 24: only as a 16-lane matrix (12 chunks per lane)
 }
 
-hipError_t launch_gemm(bool bf16, const GemmArgs &a, float * /*rinv_ws*/, void *xnorm_ws,
+// K splits of a residual product on the MFMA path: the fewest that give at
+// least 512 workgroups (about two per CU) with every split a multiple of four
+// K steps, within the partials' workspace.
+static int resid_splits(const GemmArgs &a, int tiles, size_t cap) {
+  int best = 1;
+  for (int sp = 2; sp <= 8; ++sp) {
+    if (tiles * best >= 512) break;
+    if (a.K % (sp * 4 * kGemmBK)) continue;
+    if ((size_t)sp * a.R * a.N > cap) break;
+    best = sp;
+  }
+  return best;
+}
+
+hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr,
                        hipStream_t s) {
   if (a.R <= 0) return hipSuccess;
-  if (!bf16) return gemv_dispatch<false>(a, s);
-  if (a.R < kGemvRows) return gemv_dispatch<true>(a, s);
+  const bool pending = sr && sr->splits > 0;
+  // a pending sum is taken only by the RMSNorm prologue over its residual,
+  // and nothing may write that residual first
+  if (pending && ((a.pro == PRO_NORM && (a.H != sr->a.resid || a.R != sr->a.R || a.K != sr->a.N)) ||
+                  (a.ep == EP_RESID && a.resid == sr->a.resid)))
+    return hipErrorInvalidValue;
+  if (!bf16 || a.R < kGemvRows) {
+    if (pending) return hipErrorInvalidValue;
+    return bf16 ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
+  }
   GemmArgs b = a;
   if (a.pro == PRO_NORM) {
-    hipLaunchKernelGGL((k_rmsnorm_act<true>), dim3(a.R), dim3(256), 0, s, a.H, a.ldh, a.gain, a.K,
-                       a.eps, xnorm_ws);
+    if (pending) {
+      hipLaunchKernelGGL((k_rmsnorm_act<true, true>), dim3(a.R), dim3(256), 0, s,
+                         const_cast<float *>(a.H), a.ldh, a.gain,
+                         a.K, a.eps, xnorm_ws, sr->a, sr->splits);
+      sr->splits = 0;
+    } else {
+      hipLaunchKernelGGL((k_rmsnorm_act<true, false>), dim3(a.R), dim3(256), 0, s,
+                         const_cast<float *>(a.H), a.ldh,
+                         a.gain, a.K, a.eps, xnorm_ws, a, 0);
+    }
     b.pro = PRO_PLAIN;
     b.X = xnorm_ws;
     b.ldx = a.K;
@@ -1812,11 +1866,21 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, float * /*rinv_ws*/, void *
   // 128x128 tiles only when they give every CU a workgroup (measured at the
   // decode and prefill shapes: below that the 64x64 tiles are faster)
   const int big = ((a.R + 127) / 128) * ((a.N + 127) / 128);
-  if (big >= 256)
+  if (big >= 256) {
     hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2>), dim3(big), dim3(256), 0, s, b);
-  else
-    hipLaunchKernelGGL((k_gemm_mfma<64, 64, 4>), dim3(((a.R + 63) / 64) * ((a.N + 63) / 64)),
-                       dim3(256), 0, s, b);
+    return hipGetLastError();
+  }
+  const int tiles = ((a.R + 63) / 64) * ((a.N + 63) / 64);
+  // A residual product with too few tiles to fill the chip splits K; its
+  // sum is left to the RMSNorm prologue that follows it
+  const int splits = (sr && sr->ws && a.ep == EP_RESID) ? resid_splits(a, tiles, sr->cap) : 1;
+  if (splits > 1) {
+    b.ep = EP_PART;
+    b.out_f32 = sr->ws;
+    sr->a = b;                               // the norm reads the partials at b.out_f32
+    sr->splits = splits;
+  }
+  hipLaunchKernelGGL((k_gemm_mfma<64, 64, 4>), dim3(tiles, splits), dim3(256), 0, s, b);
   return hipGetLastError();
 }
 
