@@ -152,6 +152,7 @@ struct PassLaunch {
   double flash_flops;                // per layer: the causal kernel's QK^T and PV flops
   bool sample;                       // block rows draw their bytes (smp)
   SampleArgs smp;
+  int attn_sub = 1;                  // kAttnChunk-key chunks per split-K attention workgroup
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
@@ -191,7 +192,8 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
       blt_status pb = prof_next(c, ev_flash ? p.flash_flops : p.split_bytes, &e0, &e1);
       if (pb != BLT_OK) return pb;
     }
-    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, c->max_chunks,
+    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, p.attn_sub,
+                                c->max_chunks,
                                 p.flash_tiles, c->rows_d, R, c->part, c->xa, e0, e1, ev_flash, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
@@ -257,7 +259,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   // rows below each of its sequences' kmax; the causal kernel does 4 d flops
   // per (row, key) pair (two multiply-adds per head dimension, QK^T and PV).
   const int d = c->cfg.d_model;
-  int kmax = 0, flash_tiles = 0;
+  int kmax = 0, flash_tiles = 0, split_rows = 0;
   double split_bytes = 0, flash_flops = 0;
   for (SeqDesc &sd : seqs) {
     sd.attn_flash = c->bf16 && sd.blk0 < 0 && sd.nrows >= kFlashMinRows;
@@ -269,6 +271,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
       flash_tiles = std::max(flash_tiles, (sd.nrows + kFlashRows - 1) / kFlashRows);
     } else {
       kmax = std::max(kmax, sd.kmax);
+      split_rows = std::max(split_rows, sd.nrows);
       split_bytes += (double)sd.kmax * 2.0 * d * (c->bf16 ? 2 : 4);
     }
   }
@@ -279,6 +282,14 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                argmax_out, conf_out, logits_out, split_bytes, flash_flops, smp != nullptr,
                SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
                           smp ? smp->seed : 0}};
+  // Split-K attention: a workgroup takes 8 or 4 consecutive chunks when a
+  // chunk each would give many workgroups (fewer partials to write and
+  // merge), one otherwise (small passes keep their parallelism); sequences of
+  // more than 16 split-K rows keep one chunk, held in registers for every
+  // 16-row group.  The choice depends on the pass's shape only.
+  const double split_wg = (double)p.grid_chunks * c->cfg.n_heads * p.S;
+  if (c->bf16 && d / c->cfg.n_heads <= 64 && split_rows <= 16)
+    p.attn_sub = split_wg >= 32768 ? 8 : (split_wg >= 4096 ? 4 : 1);
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
@@ -286,6 +297,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   PassKey key;
   memset(&key, 0, sizeof(key));
   key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.flash_tiles = p.flash_tiles;
+  key.attn_sub = p.attn_sub;
   key.unmask = unmask;
   key.mode = mode;
   memcpy(&key.alpha_bits, &alpha, sizeof(float));

@@ -128,11 +128,14 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 // ev0/ev1 (nullable) are stamped by the dispatch of the split-K partials
 // kernel, or of the causal kernel when ev_flash is set.  grid_chunks = 0
 // skips the split-K kernel and its merge (every sequence on the causal
-// kernel); flash_tiles = 0 skips the causal kernel.
+// kernel); flash_tiles = 0 skips the causal kernel.  nsub: chunks of
+// kAttnChunk keys per split-K workgroup (1, 4 or 8; bf16 with d_head <= 64
+// for 4 and 8), which must be 1 when a split-K sequence has more than 16 rows.
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            int flash_tiles, const RowDesc *rows, int R, float *part, void *a_out,
-                            hipEvent_t ev0, hipEvent_t ev1, bool ev_flash, hipStream_t s);
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub,
+                            int max_chunks, int flash_tiles, const RowDesc *rows, int R,
+                            float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
+                            hipStream_t s);
 bool gemv_supported(bool bf16, int K);
 // report_entropy: conf_out receives each row's entropy instead of its confidence.
 // smp (nullable): rows with ctr >= 0 draw their byte by temperature / top-p

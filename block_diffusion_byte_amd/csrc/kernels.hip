@@ -751,30 +751,39 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 }
 
 
-// bfloat16: each wave takes 32 keys of the chunk and up to 16 rows at a time.
-// Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_16x16x32_bf16;
-// the K rows are fed to the two 16-key score tiles permuted (row m of tile t
-// is key 8(m/4) + 4t + m%4) so that lane group q ends up holding keys
-// 8q..8q+7 of the wave's 32 for one row: exactly the A-operand layout
-// P[row][k-slot] of the P.V product with k-slot 8q+i = key 8q+i, and the V
-// operand of lane (dim, q) is one 16-byte piece of the transposed V row.  P is split into bf16 hi and lo parts, two MFMAs per output tile,
-// so the probabilities keep about 16 significant bits.  The four waves'
-// (o, m, l) are combined through LDS in wave order.
-template <int DH>
+// bfloat16: a workgroup takes NSUB consecutive chunks of kCK keys of one
+// (sequence, head), each wave 32 keys of every chunk, and up to 16 rows at a
+// time.  Scores are computed transposed, S^T = K Q^T, with
+// v_mfma_f32_16x16x32_bf16; the K rows are fed to the two 16-key score tiles
+// permuted (row m of tile t is key 8(m/4) + 4t + m%4) so that lane group q
+// ends up holding keys 8q..8q+7 of the wave's 32 for row lr: exactly the
+// B-operand layout of O^T += V^T P^T with k-slot 8q+i = key 8q+i, so the V
+// operand of lane (dim, q) is one 16-byte piece of the transposed V row and
+// the output O^T[dim][row] keeps each row's values in the lanes that hold
+// its running max and sum (the rescale between chunks is lane-local).  The
+// loads of chunk i+1 are issued before chunk i is computed; the softmax runs
+// in base-2 units (one multiply and one exp2 per score) over all NSUB
+// chunks, P is split into bf16 hi and lo parts (two MFMAs per output tile,
+// about 16 significant bits), and the four waves' (o, m, l) are combined
+// through LDS in wave order into one partial per workgroup (m stored in
+// natural-log units).  More chunks per workgroup mean fewer partials to
+// write and merge; one chunk keeps the most workgroups for small passes,
+// and stays in registers for every group of 16 rows.
+template <int DH, int NSUB>
 __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
                                                    int layer, const SeqDesc *seqs,
                                                    const RowDesc *rows, float *part,
                                                    int max_chunks) {
   constexpr int KS = DH / 32;                 // k-steps of the score product
   constexpr int DT = DH / 16;                 // 16-dim output tiles of P.V
-  constexpr int KW = 32;                      // keys per wave
+  constexpr int KW = 32;                      // keys per wave and chunk
   constexpr int OST = DH + 4;                 // LDS row stride of the wave outputs
   __shared__ float ow[4][16 * OST];
   __shared__ float mw[4][16], lw[4][16];
   __shared__ int kends[16];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
-  const int key0 = c * kCK;
+  const int key0 = c * kCK * NSUB;
   if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int d = g.n_heads * DH;
@@ -782,12 +791,24 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
   const uint16_t *Kp =
       (const uint16_t *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
   const uint16_t *Vt = Kp + (int64_t)g.n_heads * plane;
-  const int kw0 = key0 + w * KW;
   const int klast = sd.kmax - 1;              // every cache row below kmax holds data
+  const int nsub = min(NSUB, (sd.kmax - key0 + kCK - 1) / kCK);   // chunks holding keys
 
-  // q of the first row group, then K (A operand: key kw0+16kt+lr, dims
-  // 32ks+8lq..+8) and V (B operand: dim 16dt+lr, keys kw0+4lq..+4 and
-  // kw0+16+4lq..+4); key indices are clamped into the written cache rows
+  // K (A operand: key kw0 + 8(lr/4) + 4kt + lr%4, dims 32ks+8lq..+8) and the
+  // raw V rows (dims 16dt+lr, keys kw0+8lq..+8) of one chunk; key indices
+  // are clamped into the written cache rows
+  auto load = [&](int kw0, bf16x8_t (&ka)[2][KS], u32x4_t (&vg)[DT]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const uint16_t *kr = Kp + (int64_t)min(kw0 + 8 * (lr >> 2) + 4 * kt + (lr & 3), klast) * DH + 8 * lq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *(const bf16x8_t *)(kr + 32 * ks);
+    }
+    const int va = min(kw0 + 8 * lq, klast & ~7);   // a group clamped here lies wholly past kmax
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      vg[dt] = *(const u32x4_t *)(Vt + (int64_t)(16 * dt + lr) * g.max_ctx + va);
+  };
   int nr = min(16, sd.nrows);
   float4 qf[KS][2];
   {
@@ -799,33 +820,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
     }
   }
   int my_kend = rows[sd.row0 + min(lr, nr - 1)].kend;
-  bf16x8_t ka[2][KS];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) {
-    const uint16_t *kr = Kp + (int64_t)min(kw0 + 8 * (lr >> 2) + 4 * kt + (lr & 3), klast) * DH + 8 * lq;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *(const bf16x8_t *)(kr + 32 * ks);
-  }
-  const int kq = kw0 + 8 * lq;                // the lane group's first key
-  const int va = min(kq, klast & ~7);         // a group clamped here lies wholly past kmax
-  u32x4_t vg[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    vg[dt] = *(const u32x4_t *)(Vt + (int64_t)(16 * dt + lr) * g.max_ctx + va);
-  // V operand (k-slot 8q+i = key kq+i); keys at or past kmax (never written) become 0
-  bf16x8_t vb[DT];
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    u32x4_t o = vg[dt];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t lo = kq + 2 * i < sd.kmax ? (o[i] & 0xffffu) : 0u;
-      const uint32_t hi = kq + 2 * i + 1 < sd.kmax ? (o[i] & 0xffff0000u) : 0u;
-      o[i] = lo | hi;
-    }
-    vb[dt] = __builtin_bit_cast(bf16x8_t, o);
-  }
-  const float scale = 1.f / sqrtf((float)DH);
+  bf16x8_t ka[2][KS], kn[2][KS];
+  u32x4_t vg[DT], vn[DT];
+  load(key0 + w * KW, ka, vg);
+  const float c2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
 
   for (int rg = 0;;) {
     if (t < 16) kends[t] = rows[sd.row0 + rg + min(t, nr - 1)].kend;
@@ -839,55 +837,84 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       v[6] = (__bf16)qf[ks][1].z; v[7] = (__bf16)qf[ks][1].w;
       qb[ks] = v;
     }
-    // S^T tiles: acc[kt][v] = score of key kq+4kt+v for row lr
-    f32x4_t acc[2];
+    float m = -INFINITY, lp = 0.f;            // running max (base 2) and sum of row lr
+    f32x4_t o[DT];                            // o[dt][v]: row lr, dim 16dt+4lq+v
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int sb = 0; sb < nsub; ++sb) {
+      const int kw0 = key0 + kCK * sb + w * KW;
+      if (NSUB > 1 && sb + 1 < nsub) load(kw0 + kCK, kn, vn);
+      const int kq = kw0 + 8 * lq;            // the lane group's first key
+      // S^T tiles: acc[kt][v] = score of key kq+4kt+v for row lr
+      f32x4_t acc[2];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt][ks], qb[ks], acc[kt], 0, 0, 0);
-    }
-    float sv[8];
-    float m = -INFINITY;
+      for (int kt = 0; kt < 2; ++kt) {
+        acc[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int key = kq + 4 * kt + v;
-        const float x = key < my_kend ? acc[kt][v] * scale : -INFINITY;
-        sv[kt * 4 + v] = x;
-        m = fmaxf(m, x);
+        for (int ks = 0; ks < KS; ++ks)
+          acc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka[kt][ks], qb[ks], acc[kt], 0, 0, 0);
       }
-    m = max_lane_groups(m);                   // the four lane groups holding row lr
-    float l = 0.f;
-    float ph[8], pl[8];
+      float sv[8];
+      float mt = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = sv[i] == -INFINITY ? 0.f : expf(sv[i] - m);
-      l += p;
-      ph[i] = p;
-    }
-    l = sum_lane_groups(l);
-    bf16x8_t pa_hi, pa_lo;
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const __bf16 hb = (__bf16)ph[i];
-      pa_hi[i] = hb;
-      pl[i] = ph[i] - (float)hb;
-      pa_lo[i] = (__bf16)pl[i];
-    }
-    f32x4_t o[DT];
+        for (int v = 0; v < 4; ++v) {
+          const int key = kq + 4 * kt + v;
+          const float x = key < my_kend ? acc[kt][v] * c2 : -INFINITY;
+          sv[kt * 4 + v] = x;
+          mt = fmaxf(mt, x);
+        }
+      mt = max_lane_groups(mt);               // the four lane groups holding row lr
+      const float m_new = fmaxf(m, mt);
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m - m_new);
+      m = m_new;
+      float ps = 0.f;
+      bf16x8_t pa_hi, pa_lo;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_hi, vb[dt], f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa_lo, vb[dt], o[dt], 0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const float pv = sv[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sv[i] - m_new);
+        ps += pv;
+        const __bf16 hb = (__bf16)pv;
+        pa_hi[i] = hb;
+        pa_lo[i] = (__bf16)(pv - (float)hb);
+      }
+      lp = lp * alpha + ps;
+      // V operand (k-slot 8q+i = key kq+i); keys at or past kmax (never
+      // written) become 0
+      bf16x8_t vb[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        u32x4_t x = vg[dt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t lo = kq + 2 * i < sd.kmax ? (x[i] & 0xffffu) : 0u;
+          const uint32_t hi = kq + 2 * i + 1 < sd.kmax ? (x[i] & 0xffff0000u) : 0u;
+          x[i] = lo | hi;
+        }
+        vb[dt] = __builtin_bit_cast(bf16x8_t, x);
+      }
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        o[dt] = o[dt] * alpha;
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pa_hi, o[dt], 0, 0, 0);
+        o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb[dt], pa_lo, o[dt], 0, 0, 0);
+      }
+      if constexpr (NSUB > 1) {              // past the last chunk: unused
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = kn[kt][ks];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vg[dt] = vn[dt];
+      }
     }
-    // o[dt][v] = output of row 4lq+v, dim 16dt+lr
+    const float l = sum_lane_groups(lp);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) ow[w][(4 * lq + v) * OST + 16 * dt + lr] = o[dt][v];
+      for (int v = 0; v < 4; ++v) ow[w][lr * OST + 16 * dt + 4 * lq + v] = o[dt][v];
     if (lq == 0) {
       mw[w][lr] = m;
       lw[w][lr] = l;
@@ -898,16 +925,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       if (kends[r] <= key0) continue;
       const float m0 = mw[0][r], m1 = mw[1][r], m2 = mw[2][r], m3 = mw[3][r];
       const float M = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-      const float f0 = m0 == -INFINITY ? 0.f : expf(m0 - M);
-      const float f1 = m1 == -INFINITY ? 0.f : expf(m1 - M);
-      const float f2 = m2 == -INFINITY ? 0.f : expf(m2 - M);
-      const float f3 = m3 == -INFINITY ? 0.f : expf(m3 - M);
+      const float f0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
+      const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
+      const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
+      const float f3 = m3 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m3 - M);
       const float O = ((f0 * ow[0][r * OST + e] + f1 * ow[1][r * OST + e]) + f2 * ow[2][r * OST + e]) +
                       f3 * ow[3][r * OST + e];
       float *dst = part + (((int64_t)(sd.row0 + rg + r) * g.n_heads + h) * max_chunks + c) * (DH + 2);
       dst[e] = O;
       if (e == 0) {
-        dst[DH] = M;
+        dst[DH] = M * 0.6931471805599453f;    // natural-log units for the merge
         dst[DH + 1] = ((f0 * lw[0][r] + f1 * lw[1][r]) + f2 * lw[2][r]) + f3 * lw[3][r];
       }
     }
@@ -923,6 +950,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       }
     }
     my_kend = rows[sd.row0 + rg + min(lr, nr - 1)].kend;
+    // the first chunk again (one chunk per workgroup keeps it in registers)
+    if constexpr (NSUB > 1) load(key0 + w * KW, ka, vg);
     __syncthreads();                          // LDS of this row group fully read
   }
 }
@@ -1353,7 +1382,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 // descriptor, the statistics and the partials are all in flight at once.
 template <bool BF, int DH>
 __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
-                                                   int n_heads, int max_chunks, int gc,
+                                                   int n_heads, int max_chunks, int gc, int ck,
                                                    void *a_out) {
   using T = typename Act<BF>::T;
   __shared__ float fw[kMaxChunks];
@@ -1363,7 +1392,7 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   const float m0 = pb[c0 * (DH + 2) + DH], m1 = pb[c1 * (DH + 2) + DH];
   const float l0 = pb[c0 * (DH + 2) + DH + 1], l1 = pb[c1 * (DH + 2) + DH + 1];
   const RowDesc rd = rows[row];
-  const int nc = (rd.kend + kCK - 1) / kCK;
+  const int nc = (rd.kend + ck - 1) / ck;   // chunks of ck keys holding the row's keys
   // chunk weights f_c = exp(m_c - M) and L = sum_c l_c f_c, one chunk per lane
   const bool ok0 = l < nc, ok1 = l + 64 < nc;
   const float M = wave_max(fmaxf(ok0 ? m0 : -INFINITY, ok1 ? m1 : -INFINITY));
@@ -1910,7 +1939,7 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
-                        int n_seq, int grid_chunks, int max_chunks, int flash_tiles,
+                        int n_seq, int grid_chunks, int nsub, int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
                         hipEvent_t ev1, bool ev_flash, hipStream_t s) {
   if constexpr (BF) {
@@ -1926,15 +1955,26 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   }
   if (ev_flash) ev0 = ev1 = nullptr;
   if (grid_chunks <= 0) return;
-  const dim3 grid(grid_chunks, g.n_heads, n_seq);
+  if (!BF || DH > 64 || (nsub != 4 && nsub != 8)) nsub = 1;
+  const int gc = (grid_chunks + nsub - 1) / nsub;   // workgroups (partials) per (sequence, head)
+  const dim3 grid(gc, g.n_heads, n_seq);
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
-    if (ev0)
-      hipExtLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
-                            seqs, rows, part, max_chunks);
-    else
-      hipLaunchKernelGGL((k_attn_mfma<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
-                         part, max_chunks);
+#define BLT_SPLITK(NS)                                                                            \
+  if (ev0)                                                                                        \
+    hipExtLaunchKernelGGL((k_attn_mfma<DH, NS>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g,   \
+                          layer, seqs, rows, part, max_chunks);                                   \
+  else                                                                                            \
+    hipLaunchKernelGGL((k_attn_mfma<DH, NS>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows, \
+                       part, max_chunks);
+    if constexpr (DH <= 64) {
+      if (nsub == 8) { BLT_SPLITK(8) }
+      else if (nsub == 4) { BLT_SPLITK(4) }
+      else { BLT_SPLITK(1) }
+    } else {
+      BLT_SPLITK(1)
+    }
+#undef BLT_SPLITK
   } else {
     if (ev0)
       hipExtLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
@@ -1944,19 +1984,20 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                          part, max_chunks);
   }
   hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
-                     g.n_heads, max_chunks, grid_chunks, a_out);
+                     g.n_heads, max_chunks, gc, kCK * nsub, a_out);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int max_chunks,
-                            int flash_tiles, const RowDesc *rows, int R, float *part, void *a_out,
-                            hipEvent_t ev0, hipEvent_t ev1, bool ev_flash, hipStream_t s) {
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub,
+                            int max_chunks, int flash_tiles, const RowDesc *rows, int R,
+                            float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
+                            hipStream_t s) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
-  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks,          \
+  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, max_chunks,    \
                                   flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);      \
-  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, max_chunks, flash_tiles, \
-                              rows, R, part, a_out, ev0, ev1, ev_flash, s);
+  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, max_chunks,        \
+                              flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;
