@@ -628,34 +628,56 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
       }
 }
 
-// RMSNorm rows into an activation buffer (MFMA path prologue).  PEND: a
-// split-K residual product is pending (partial products p.out_f32[split][R][K],
+// RMSNorm rows into an activation buffer (MFMA path prologue).  SPLITS > 0:
+// a split-K residual product is pending (partial products p.out_f32[split][R][K],
 // its cross term per p.cross): the row first takes h += (sum + cross), the
-// partials added in split order, as the product's own epilogue would.
-template <bool BF, bool PEND>
+// partials added in split order, as the product's own epilogue would.  Each
+// thread takes elements t + 256 i of blocks of 2048, every load of a block
+// issued before the first is used.
+template <bool BF, int SPLITS>
 __global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, const void *gain,
-                                                     int K, float eps, void *out, GemmArgs p,
-                                                     int splits) {
+                                                     int K, float eps, void *out, GemmArgs p) {
   using T = typename Act<BF>::T;
+  constexpr int E = 8;                       // elements per thread and block
+  constexpr int NS = SPLITS > 0 ? SPLITS : 1;
   __shared__ float part[4];
   const int r = blockIdx.x, t = threadIdx.x;
   float *hr = H + (int64_t)r * ldh;
-  float ss = 0.f;
-  if constexpr (PEND) {
-    const float *cr = nullptr;
-    if (p.cross) {
-      const RowDesc rd = p.rows[r];
-      cr = p.cross + (((int64_t)rd.slot * p.max_lat + rd.lat) * p.n_layers + p.cross_layer) * p.d;
+  RowDesc rd{};
+  if (SPLITS > 0 && p.cross) rd = p.rows[r];   // first, so it lands while the rest is in flight
+  float ss = 0.f, v[E];
+  for (int kb = 0; kb < K; kb += 256 * E) {
+    float hv[E], y[E][NS], cv[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k = min(kb + t + 256 * i, K - 1);   // past the row: re-reads, dropped below
+      hv[i] = hr[k];
+      if constexpr (SPLITS > 0) {
+#pragma unroll
+        for (int sp = 0; sp < SPLITS; ++sp) y[i][sp] = p.out_f32[((int64_t)sp * p.R + r) * K + k];
+      }
     }
-    for (int k = t; k < K; k += 256) {
-      float y = p.out_f32[(int64_t)r * K + k];
-      for (int sp = 1; sp < splits; ++sp) y += p.out_f32[((int64_t)sp * p.R + r) * K + k];
-      const float v = hr[k] + (y + (cr ? cr[k] : 0.f));
-      hr[k] = v;
-      ss = fmaf(v, v, ss);
+    if constexpr (SPLITS > 0) {
+      const float *cr =
+          p.cross ? p.cross + (((int64_t)rd.slot * p.max_lat + rd.lat) * p.n_layers + p.cross_layer) * p.d
+                  : nullptr;
+#pragma unroll
+      for (int i = 0; i < E; ++i) cv[i] = cr ? cr[min(kb + t + 256 * i, K - 1)] : 0.f;
     }
-  } else {
-    for (int k = t; k < K; k += 256) ss = fmaf(hr[k], hr[k], ss);
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k = kb + t + 256 * i;
+      float x = hv[i];
+      if constexpr (SPLITS > 0) {
+        float sum = y[i][0];
+#pragma unroll
+        for (int sp = 1; sp < SPLITS; ++sp) sum += y[i][sp];
+        x = x + (sum + cv[i]);
+        if (k < K) hr[k] = x;
+      }
+      v[i] = x;
+      if (k < K) ss = fmaf(x, x, ss);
+    }
   }
   ss = wave_sum(ss);
   if ((t & 63) == 0) part[t >> 6] = ss;
@@ -664,7 +686,14 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, cons
   const float rinv = 1.f / sqrtf(tot / (float)K + eps);
   const T *g = (const T *)gain;
   T *o = (T *)out + (int64_t)r * K;
-  for (int k = t; k < K; k += 256) o[k] = from_f<T>(to_f(g[k]) * hr[k] * rinv);
+  for (int kb = 0; kb < K; kb += 256 * E) {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      const int k = kb + t + 256 * i;
+      // one block: the values are still in registers; else this thread's own writes
+      if (k < K) o[k] = from_f<T>(to_f(g[k]) * (K <= 256 * E ? v[i] : hr[k]) * rinv);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1876,16 +1905,24 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
   }
   GemmArgs b = a;
   if (a.pro == PRO_NORM) {
-    if (pending) {
-      hipLaunchKernelGGL((k_rmsnorm_act<true, true>), dim3(a.R), dim3(256), 0, s,
-                         const_cast<float *>(a.H), a.ldh, a.gain,
-                         a.K, a.eps, xnorm_ws, sr->a, sr->splits);
-      sr->splits = 0;
-    } else {
-      hipLaunchKernelGGL((k_rmsnorm_act<true, false>), dim3(a.R), dim3(256), 0, s,
-                         const_cast<float *>(a.H), a.ldh,
-                         a.gain, a.K, a.eps, xnorm_ws, a, 0);
+    float *H = const_cast<float *>(a.H);
+    const GemmArgs &pa = pending ? sr->a : a;
+#define BLT_NORM(SP)                                                                             \
+  hipLaunchKernelGGL((k_rmsnorm_act<true, SP>), dim3(a.R), dim3(256), 0, s, H, a.ldh, a.gain, a.K, \
+                     a.eps, xnorm_ws, pa);
+    switch (pending ? sr->splits : 0) {
+      case 0: BLT_NORM(0) break;
+      case 2: BLT_NORM(2) break;
+      case 3: BLT_NORM(3) break;
+      case 4: BLT_NORM(4) break;
+      case 5: BLT_NORM(5) break;
+      case 6: BLT_NORM(6) break;
+      case 7: BLT_NORM(7) break;
+      case 8: BLT_NORM(8) break;
+      default: return hipErrorInvalidValue;
     }
+#undef BLT_NORM
+    if (pending) sr->splits = 0;
     b.pro = PRO_PLAIN;
     b.X = xnorm_ws;
     b.ldx = a.K;
