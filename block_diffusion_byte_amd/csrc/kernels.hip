@@ -1404,19 +1404,28 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
   }
 }
 
-// Merge of the chunk partials of (row, head) in chunk order, 32 chunks at a
-// time with a running max; chunk c's partial sits at [row][h][c][d_h + 2].
-// Every load is addressed by the pass's chunk count gc alone (chunks past the
-// row's own count are read but weighted by an exact 0), so the row
-// descriptor, the statistics and the partials are all in flight at once.
-template <bool BF, int DH>
+// Merge of the chunk partials of (row, head) in chunk order; chunk c's
+// partial sits at [row][h][c][d_h + 2].  Every load is addressed by the
+// pass's chunk count gc alone (chunks past the row's own count are read but
+// weighted by an exact 0), so the partial outputs of the first PRE chunks,
+// the statistics and the row descriptor are all in flight at once; chunks
+// past PRE follow 32 at a time.
+template <bool BF, int DH, int PRE>
 __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
                                                    int n_heads, int max_chunks, int gc, int ck,
                                                    void *a_out) {
   using T = typename Act<BF>::T;
+  static_assert(PRE % 32 == 0 || PRE < 32, "later chunks go 32 at a time");
+  constexpr int EPL = (DH + 63) / 64;       // output dims per lane
   __shared__ float fw[kMaxChunks];
   const int row = blockIdx.x, h = blockIdx.y, l = threadIdx.x;
   const float *pb = part + ((int64_t)row * n_heads + h) * max_chunks * (DH + 2);
+  // the lanes of a chunk read one contiguous row of the partials
+  float ov[EPL][PRE];
+#pragma unroll
+  for (int j = 0; j < EPL; ++j)
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) ov[j][u] = pb[min(u, gc - 1) * (DH + 2) + min(l + 64 * j, DH - 1)];
   const int c0 = min(l, gc - 1), c1 = min(l + 64, gc - 1);
   const float m0 = pb[c0 * (DH + 2) + DH], m1 = pb[c1 * (DH + 2) + DH];
   const float l0 = pb[c0 * (DH + 2) + DH + 1], l1 = pb[c1 * (DH + 2) + DH + 1];
@@ -1430,19 +1439,22 @@ __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowD
   fw[l] = f0;
   fw[l + 64] = f1;
   __syncthreads();
-  // O[e] = sum_c o_c[e] f_c in chunk order; the lanes of a chunk read one
-  // contiguous row of the partials, 32 chunks in flight at a time
-  for (int e = l; e < DH; e += 64) {
-    float O = 0.f;
-    for (int cb = 0; cb < gc; cb += 32) {
-      float ov[32];
+  // O[e] = sum_c o_c[e] f_c in chunk order
 #pragma unroll
-      for (int u = 0; u < 32; ++u) ov[u] = pb[min(cb + u, gc - 1) * (DH + 2) + e];
+  for (int j = 0; j < EPL; ++j) {
+    const int e = l + 64 * j;
+    float O = 0.f;
+#pragma unroll
+    for (int u = 0; u < PRE; ++u) O = fmaf(u < nc ? ov[j][u] : 0.f, fw[u], O);
+    for (int cb = PRE; cb < gc; cb += 32) {
+      float ol[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) ol[u] = pb[min(cb + u, gc - 1) * (DH + 2) + min(e, DH - 1)];
 #pragma unroll
       for (int u = 0; u < 32; ++u)
-        O = fmaf(cb + u < nc ? ov[u] : 0.f, fw[min(cb + u, kMaxChunks - 1)], O);
+        O = fmaf(cb + u < nc ? ol[u] : 0.f, fw[min(cb + u, kMaxChunks - 1)], O);
     }
-    if (!rd.attn_flash)                       // else written by the causal kernel
+    if (e < DH && !rd.attn_flash)             // else written by the causal kernel
       ((T *)a_out)[(int64_t)row * n_heads * DH + h * DH + e] = from_f<T>(O / L);
   }
 }
@@ -2020,8 +2032,13 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
       hipLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
                          part, max_chunks);
   }
-  hipLaunchKernelGGL((k_attn_merge<BF, DH>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
-                     g.n_heads, max_chunks, gc, kCK * nsub, a_out);
+  // the merge takes its first 16 (or 64) chunks in one round of loads
+  if (gc <= 16)
+    hipLaunchKernelGGL((k_attn_merge<BF, DH, 16>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
+                       g.n_heads, max_chunks, gc, kCK * nsub, a_out);
+  else
+    hipLaunchKernelGGL((k_attn_merge<BF, DH, (DH > 64 ? 32 : 64)>), dim3(R, g.n_heads), dim3(64), 0,
+                       s, part, rows, g.n_heads, max_chunks, gc, kCK * nsub, a_out);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
