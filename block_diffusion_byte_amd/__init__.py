@@ -34,6 +34,7 @@ EXPORTS = [
     "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_verify_sample", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
     "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
+    "blt_attention_chunks",
 ]
 
 
@@ -115,6 +116,7 @@ def lib():
             "blt_profile_enable": [P, I32],
             "blt_profile_read": [P, P, P, P, I32],
             "blt_graphs_enable": [P, I32],
+            "blt_attention_chunks": [P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -258,6 +260,10 @@ def blt_verify_accept(ctx, r, draft, ld_draft, pred, ld_pred, accept_len, next_b
 
 def blt_graphs_enable(ctx, enable):
     _check("blt_graphs_enable", lib().blt_graphs_enable(ctx, 1 if enable else 0), ctx)
+
+
+def blt_attention_chunks(ctx, chunks):
+    _check("blt_attention_chunks", lib().blt_attention_chunks(ctx, chunks), ctx)
 
 
 def blt_profile_enable(ctx, family):

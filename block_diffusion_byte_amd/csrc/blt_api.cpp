@@ -289,7 +289,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   // 16-row group.  The choice depends on the pass's shape only.
   const double split_wg = (double)p.grid_chunks * c->cfg.n_heads * p.S;
   if (c->bf16 && d / c->cfg.n_heads <= 64 && split_rows <= 16)
-    p.attn_sub = split_wg >= 32768 ? 8 : (split_wg >= 4096 ? 4 : 1);
+    p.attn_sub = c->attn_chunks ? c->attn_chunks : (split_wg >= 32768 ? 8 : (split_wg >= 4096 ? 4 : 1));
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
@@ -701,6 +701,14 @@ blt_status blt_graphs_enable(blt_ctx *c, int32_t enable) {
   if (!c) return BLT_EINVAL;
   if (!enable) drop_graphs(c);
   c->graphs = enable != 0;
+  return BLT_OK;
+}
+
+blt_status blt_attention_chunks(blt_ctx *c, int32_t chunks) {
+  if (!c) return BLT_EINVAL;
+  if (chunks != 0 && chunks != 1 && chunks != 4 && chunks != 8)
+    return fail(c, BLT_EINVAL, "blt_attention_chunks: chunks must be 0, 1, 4 or 8");
+  c->attn_chunks = chunks;
   return BLT_OK;
 }
 

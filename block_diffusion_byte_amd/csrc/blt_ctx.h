@@ -81,6 +81,8 @@ struct blt_ctx {
   std::string err;
   // replay of decoder passes from cached HIP graphs (captured on cap_stream)
   bool graphs = false;
+  // split-K attention chunks per workgroup forced by blt_attention_chunks (0: per pass)
+  int attn_chunks = 0;
   hipStream_t cap_stream = nullptr;
   std::unordered_map<blt::PassKey, blt::GraphEntry, blt::PassKeyHash> graph_cache;
   // profiling: family being timed, event pool, pending and accumulated figures

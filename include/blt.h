@@ -278,6 +278,17 @@ blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, 
  * enable = 0 launches every pass directly and frees the cached graphs. */
 blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
 
+/* Keys per split-K self-attention workgroup, in chunks of 128 keys.
+ * chunks = 0 (the default) lets each pass choose from its shape: 8 or 4
+ * when one chunk per workgroup would give at least 32768 or 4096
+ * workgroups (fewer partial results to write and merge), else 1.  chunks =
+ * 1, 4 or 8 forces that count.  Counts above 1 apply only to bfloat16
+ * contexts with d_model / n_heads <= 64 and to passes whose split-K
+ * sequences have at most 16 rows; other passes take 1.  The count changes
+ * the rounding of the softmax sums, not what is computed.  BLT_EINVAL for
+ * any other value. */
+blt_status blt_attention_chunks(blt_ctx *ctx, int32_t chunks);
+
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
  * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),
  * gb_per_seq = bytes_total / 1e9 / n_seq.  Host-only, exact integers;

@@ -1,5 +1,6 @@
-"""GPU parity of long clean-row passes (prompt prefill, KV rebuild) against the
-CPU oracle.
+"""GPU parity of long clean-row passes (prompt prefill, KV rebuild) and of the
+split-K decode attention at each chunk count per workgroup, against the CPU
+oracle.
 
 A bf16 sequence with at least 64 clean rows in a pass takes the causal
 (flash) attention kernel; shorter ones and block passes take the split-K
@@ -9,6 +10,11 @@ in one pass, and a pass that mixes both kernels) and compare every row's
 logits with the float64 oracle's cached decoder (bf16 tolerance: 2e-2
 absolute), and every greedy byte whose oracle top-2 gap is outside the
 rounding band.
+
+The split-K kernel walks 1, 4 or 8 chunks of 128 keys per workgroup; the
+last test forces each count on short appends after contexts whose chunk
+counts are not multiples of 4 or 8 (one sequence shorter than a whole
+workgroup's span), with 1 to 9 rows per sequence whose key counts differ.
 """
 import numpy as np
 import pytest
@@ -136,3 +142,46 @@ def test_causal_kernel_matches_split_k_pass_by_pass():
     err = np.abs(res[0] - res[1]).max()
     say(f"causal kernel vs split-K over 200 rows: max logit difference {err:.3g}")
     assert err <= BF16_ABS
+
+
+LONG = MINI.replace(name="mini_chunks_bf16", prompt_len=1400, prompt_patches=350, batch=3)
+
+
+def test_split_k_chunks_per_workgroup_match_the_oracle():
+    """Appends of 9, 1 and 6 rows after 700-, 1030- and 1385-byte contexts
+    (6, 9 and 12 chunks of keys) with 1, 4 and 8 chunks per workgroup, and
+    the default choice: every row's logits match the oracle, and the counts
+    agree with each other to well within the bf16 tolerance."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = LONG
+    w = bltgen.make_weights(wl, gains="random")
+    seqs = [_Seq(wl, w, s) for s in range(3)]
+    ctx = [700, 1030, 1385]
+    n_new = [9, 1, 6]
+    dec = decoder_for(wl, w, max_batch=3, max_rows=1400)
+    try:
+        for s in range(3):
+            table = torch.from_numpy(seqs[s].inp["latents"]).to("cuda:0", dec.torch_dtype)
+            blt.blt_latents_put(dec.ctx, dec.state, [s] * wl.n_latents, list(range(wl.n_latents)),
+                                table, 0)
+        z = torch.zeros(3 * 1400 * 257, device="cuda:0")
+        for s in range(3):   # contexts through the causal kernel, one sequence at a time
+            _append(blt, torch, dec, seqs, [(s, 0, ctx[s])], z)
+            seqs[s].expect(0, ctx[s])
+        ref = {s: seqs[s].expect(ctx[s], n_new[s]) for s in range(3)}
+        plan = [(s, ctx[s], n_new[s]) for s in range(3)]
+        got = {}
+        for chunks in (1, 4, 8, 0):
+            blt.blt_attention_chunks(dec.ctx, chunks)
+            got[chunks] = _append(blt, torch, dec, seqs, plan, z)   # rewrites the same rows
+            for s in range(3):
+                _check(got[chunks][s], ref[s], f"{chunks} chunks per workgroup, seq {s}")
+        for chunks in (4, 8, 0):
+            err = max(np.abs(got[chunks][s] - got[1][s]).max() for s in range(3))
+            say(f"{chunks} vs 1 chunks per workgroup: max logit difference {err:.3g}")
+            assert err <= BF16_ABS / 4
+        with pytest.raises(blt.BltError):
+            blt.blt_attention_chunks(dec.ctx, 3)
+    finally:
+        dec.close()
