@@ -469,16 +469,19 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
 // ---------------------------------------------------------------------------
 // MFMA GEMM (bf16 x bf16 -> f32) for passes of >= 16 rows: Y[R][N] = X[R][K] W[N][K]^T.
 //
-// BM x BN output tile per workgroup: 4 waves as 2x2, each a (BM/2) x (BN/2)
-// block of 16x16 v_mfma_f32_16x16x32_bf16 tiles; K in steps of 64.  The
-// global loads of step k+2 are issued while step k computes (two register
-// slots) and each step's tile is stored to one of two LDS buffers, so the
-// load latency overlaps the MFMAs of the steps before.  An LDS tile row holds
-// its eight 16-byte chunks XOR-swizzled by the row index, so the 16 lanes
-// that read one chunk column of 16 rows hit distinct banks.  Workgroups are
-// dispatched round-robin over the 8 XCDs; tiles are ordered so that the
-// workgroups of one XCD take all row tiles of consecutive column tiles and
-// share those W tiles in the XCD's L2.
+// BM x BN output tile per workgroup of 8 waves: a WM x WN grid of wave tiles
+// of 16x16 v_mfma_f32_16x16x32_bf16 blocks, and KH groups of waves that
+// split each 64-wide K step between them (KH = 2: two 32-wide halves, the
+// groups' sums added through LDS after the loop), so every SIMD runs two
+// waves that hide each other's LDS and MFMA latencies.  The global loads of
+// step k+2 are issued while step k computes (two register slots) and each
+// step's tile is stored to one of two LDS buffers, so the load latency
+// overlaps the MFMAs of the steps before.  An LDS tile row holds its eight
+// 16-byte chunks XOR-swizzled by the row index, so the 16 lanes that read one
+// chunk column of 16 rows hit distinct banks.  Workgroups are dispatched
+// round-robin over the 8 XCDs; tiles are numbered so that the workgroups of
+// one XCD take a contiguous run of them (all row tiles of consecutive column
+// tiles) and share those W tiles in the XCD's L2.
 constexpr int kGemmBK = 64;
 
 // f(integral_constant<int, I>) for I = 0..N-1: indices stay compile-time
@@ -491,40 +494,44 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-template <int BM, int BN, int P>
-__global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
+template <int BM, int BN, int WM, int WN, int KH>
+__global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
+  constexpr int NT = 512, P = 2;                    // threads; register slots of prefetched steps
   constexpr int CH = kGemmBK / 8;                   // 16-byte chunks per tile row
-  constexpr int LA = BM * CH / 256, LB = BN * CH / 256;  // chunks per thread per step
-  constexpr int TM = BM / 32, TN = BN / 32;         // 16x16 tiles per wave
-  static_assert(P % 2 == 0, "prefetch slots in pairs (two LDS buffers)");
+  constexpr int LA = BM * CH / NT, LB = BN * CH / NT;  // chunks per thread per step
+  constexpr int TM = BM / WM / 16, TN = BN / WN / 16;  // 16x16 tiles per wave
+  constexpr int KSUB = 2 / KH;                      // 32-wide k-steps per group and step
+  static_assert(WM * WN * KH == 8 && LA >= 1 && LB >= 1, "8 waves");
   // operand tiles (two buffers each); after the K loop the same LDS holds
-  // the f32 output tile for the QKV+RoPE epilogue
+  // the second group's sums and then the f32 output tile of the QKV+RoPE epilogue
   __shared__ __align__(16) u32x4_t smem[2 * BM * CH + 2 * BN * CH];
   static_assert(BM * BN * 4 <= (int)sizeof(smem), "output tile fits the operand buffers");
   u32x4_t (*sa)[BM * CH] = reinterpret_cast<u32x4_t (*)[BM * CH]>(smem);
   u32x4_t (*sb)[BN * CH] = reinterpret_cast<u32x4_t (*)[BN * CH]>(smem + 2 * BM * CH);
   const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int kg = w / (WM * WN), wt = w % (WM * WN);   // K group, wave tile
   const int mt = (a.R + BM - 1) / BM, nt = (a.N + BN - 1) / BN, ntiles = mt * nt;
-  const int tile = (ntiles & 7) ? (int)blockIdx.x
-                                : (int)(blockIdx.x & 7) * (ntiles >> 3) + (int)(blockIdx.x >> 3);
+  // XCD x = blockIdx % 8 takes tiles [x * (ntiles/8) + min(x, ntiles%8), ...)
+  const int xcd = (int)blockIdx.x & 7;
+  const int tile = xcd * (ntiles >> 3) + min(xcd, ntiles & 7) + ((int)blockIdx.x >> 3);
   const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
   // split-K: workgroup row y of the grid takes K steps [y nk, (y+1) nk)
   const int nk = a.K / kGemmBK / (int)gridDim.y;   // a multiple of P (checked at launch)
   const int64_t k0 = (int64_t)blockIdx.y * nk * kGemmBK;
   const uint16_t *X = (const uint16_t *)a.X + k0, *W = (const uint16_t *)a.W + k0;
-  // this thread's chunks of each step: tile chunk q = t + 256 i (row q / CH,
+  // this thread's chunks of each step: tile chunk q = t + NT i (row q / CH,
   // column q % CH); rows past the matrix edge re-read its last row
   const uint16_t *ga[LA], *gb[LB];
   int sla[LA], slb[LB];
 #pragma unroll
   for (int i = 0; i < LA; ++i) {
-    const int q = t + 256 * i, r = q / CH, c = q % CH, rr = min(m0 + r, a.R - 1);
+    const int q = t + NT * i, r = q / CH, c = q % CH, rr = min(m0 + r, a.R - 1);
     ga[i] = X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx) + c * 8;
     sla[i] = r * CH + (c ^ (r & 7));
   }
 #pragma unroll
   for (int i = 0; i < LB; ++i) {
-    const int q = t + 256 * i, r = q / CH, c = q % CH, nn = min(n0 + r, a.N - 1);
+    const int q = t + NT * i, r = q / CH, c = q % CH, nn = min(n0 + r, a.N - 1);
     gb[i] = W + (int64_t)nn * a.K + c * 8;
     slb[i] = r * CH + (c ^ (r & 7));
   }
@@ -533,7 +540,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const int wr = (w >> 1) * (BM / 2), wc = (w & 1) * (BN / 2);
+  const int wr = (wt / WN) * (BM / WM), wc = (wt % WN) * (BN / WN);
   u32x4_t xa[P][LA], xb[P][LB];              // register slots: step s waits in slot s % P
 
   auto load = [&](u32x4_t (&ra)[LA], u32x4_t (&rb)[LB], int kt) {
@@ -547,8 +554,8 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
   };
   auto compute = [&](const u32x4_t *s_a, const u32x4_t *s_b) {
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int c = ks * 4 + (l >> 4);
+    for (int ss = 0; ss < KSUB; ++ss) {
+      const int c = (kg * KSUB + ss) * 4 + (l >> 4);
       bf16x8_t af[TM], bw[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
@@ -585,22 +592,47 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
       __syncthreads();
     });
   }
-  // acc[i][j][v]: row wr+16i+4(l/16)+v, column wc+16j+l%16 of the tile
+  // acc[i][j][v]: row wr+16i+4(l/16)+v, column wc+16j+l%16 of the tile; with
+  // two K groups the second's sums join the first's (a fixed order)
+  const bool lead = KH == 1 || kg == 0;
+  if constexpr (KH == 2) {
+    float *red = reinterpret_cast<float *>(smem);
+    if (!lead) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) red[((wt * TM + i) * TN + j) * 256 + v * 64 + l] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (lead) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[i][j][v] += red[((wt * TM + i) * TN + j) * 256 + v * 64 + l];
+    }
+  }
   if (a.qkv_rope) {
     // QKV projection with RoPE and the KV write: the tile goes through LDS
     // so each thread can take (j, j + d_h/2) pairs of one head (the tile's
     // columns start on a head boundary: BN is a multiple of d_h)
     float *ct = reinterpret_cast<float *>(smem);
+    if (KH == 2) __syncthreads();            // the sums above are read
+    if (lead) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int v = 0; v < 4; ++v)
-          ct[(wr + i * 16 + 4 * (l >> 4) + v) * BN + wc + j * 16 + (l & 15)] = acc[i][j][v];
+          for (int v = 0; v < 4; ++v)
+            ct[(wr + i * 16 + 4 * (l >> 4) + v) * BN + wc + j * 16 + (l & 15)] = acc[i][j][v];
+    }
     __syncthreads();
     const int half = a.d_head >> 1;
-    for (int it = t; it < BM * (BN / 2); it += 256) {
+    for (int it = t; it < BM * (BN / 2); it += NT) {
       const int rr = it / (BN / 2), pc = it - rr * (BN / 2);
       const int c = (pc / half) * a.d_head + pc % half;   // first column of the pair
       const int m = m0 + rr, n = n0 + c;
@@ -611,6 +643,7 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(GemmArgs a) {
     }
     return;
   }
+  if (!lead) return;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -1940,25 +1973,27 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     b.ldx = a.K;
     b.x_row_off = nullptr;
   }
-  if (b.K % (4 * kGemmBK)) return hipErrorInvalidValue;  // the pipeline takes K steps in fours
-  // 128x128 tiles only when they give every CU a workgroup (measured at the
-  // decode and prefill shapes: below that the 64x64 tiles are faster)
-  const int big = ((a.R + 127) / 128) * ((a.N + 127) / 128);
-  if (big >= 256) {
-    hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2>), dim3(big), dim3(256), 0, s, b);
-    return hipGetLastError();
-  }
-  const int tiles = ((a.R + 63) / 64) * ((a.N + 63) / 64);
+  const int t64 = ((a.R + 63) / 64) * ((a.N + 63) / 64);
   // A residual product with too few tiles to fill the chip splits K; its
   // sum is left to the RMSNorm prologue that follows it
-  const int splits = (sr && sr->ws && a.ep == EP_RESID) ? resid_splits(a, tiles, sr->cap) : 1;
+  const int splits = (sr && sr->ws && a.ep == EP_RESID) ? resid_splits(a, t64, sr->cap) : 1;
+  if (b.K % (splits * 2 * kGemmBK)) return hipErrorInvalidValue;  // K steps in pairs per split
   if (splits > 1) {
     b.ep = EP_PART;
     b.out_f32 = sr->ws;
     sr->a = b;                               // the norm reads the partials at b.out_f32
     sr->splits = splits;
   }
-  hipLaunchKernelGGL((k_gemm_mfma<64, 64, 4>), dim3(tiles, splits), dim3(256), 0, s, b);
+  // the largest tile that still gives about 150-180 workgroups (measured at
+  // the batch-16, batch-64 and prefill shapes)
+  const int t128 = ((a.R + 127) / 128) * ((a.N + 127) / 128);
+  const int t64w = ((a.R + 63) / 64) * ((a.N + 127) / 128);
+  if (t128 * splits >= 176)
+    hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2, 4, 1>), dim3(t128, splits), dim3(512), 0, s, b);
+  else if (t64w * splits >= 150)
+    hipLaunchKernelGGL((k_gemm_mfma<64, 128, 2, 4, 1>), dim3(t64w, splits), dim3(512), 0, s, b);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<64, 64, 2, 2, 2>), dim3(t64, splits), dim3(512), 0, s, b);
   return hipGetLastError();
 }
 

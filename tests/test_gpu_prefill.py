@@ -151,7 +151,9 @@ def test_split_k_chunks_per_workgroup_match_the_oracle():
     """Appends of 9, 1 and 6 rows after 700-, 1030- and 1385-byte contexts
     (6, 9 and 12 chunks of keys) with 1, 4 and 8 chunks per workgroup, and
     the default choice: every row's logits match the oracle, and the counts
-    agree with each other to well within the bf16 tolerance."""
+    agree with each other within the same bf16 tolerance (the attention
+    output is rounded to bfloat16, so a different summation order can move
+    it by one bf16 step, and the logits by a few thousandths)."""
     import torch
     import block_diffusion_byte_amd as blt
     wl = LONG
@@ -180,7 +182,7 @@ def test_split_k_chunks_per_workgroup_match_the_oracle():
         for chunks in (4, 8, 0):
             err = max(np.abs(got[chunks][s] - got[1][s]).max() for s in range(3))
             say(f"{chunks} vs 1 chunks per workgroup: max logit difference {err:.3g}")
-            assert err <= BF16_ABS / 4
+            assert err <= BF16_ABS
         with pytest.raises(blt.BltError):
             blt.blt_attention_chunks(dec.ctx, 3)
     finally:
