@@ -282,18 +282,29 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                argmax_out, conf_out, logits_out, split_bytes, flash_flops, smp != nullptr,
                SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
                           smp ? smp->seed : 0}};
-  // Split-K attention: a workgroup takes 8 or 4 consecutive chunks when a
-  // chunk each would give many workgroups (fewer partials to write and
-  // merge), one otherwise (small passes keep their parallelism); sequences of
-  // more than 16 split-K rows keep one chunk, held in registers for every
-  // 16-row group.  The choice depends on the pass's shape only.
-  const double split_wg = (double)p.grid_chunks * c->cfg.n_heads * p.S;
-  if (c->bf16 && d / c->cfg.n_heads <= 64 && split_rows <= 16)
-    p.attn_sub = c->attn_chunks ? c->attn_chunks : (split_wg >= 32768 ? 8 : (split_wg >= 4096 ? 4 : 1));
-  if (!c->graphs || c->prof_family != BLT_PROF_OFF) return enqueue_pass(c, p, c->stream);
+  // Split-K attention: the workgroups of a (sequence, head) share its chunks
+  // evenly, as many workgroups as give about 768 in the pass (three per CU):
+  // partials written to memory slow the key stream far beyond their size,
+  // so large passes take many chunks per workgroup (all of them, and no
+  // merge, when the pass alone fills the chip), small ones one chunk each.
+  // Sequences of more than 16 split-K rows keep one chunk, held in
+  // registers for every 16-row group.  The choice depends on the pass's
+  // shape only.
+  auto chunks_per_wg = [&](int grid_chunks) {
+    if (!c->bf16 || d / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return 1;
+    if (c->attn_chunks) return c->attn_chunks;
+    const int units = c->cfg.n_heads * p.S;
+    const int wg = std::min(grid_chunks, std::max(1, (768 + units - 1) / units));
+    return (grid_chunks + wg - 1) / wg;
+  };
+  if (!c->graphs || c->prof_family != BLT_PROF_OFF) {
+    p.attn_sub = chunks_per_wg(p.grid_chunks);
+    return enqueue_pass(c, p, c->stream);
+  }
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
   p.grid_chunks = std::min((p.grid_chunks + 3) / 4 * 4, c->max_chunks);
+  p.attn_sub = chunks_per_wg(p.grid_chunks);
   PassKey key;
   memset(&key, 0, sizeof(key));
   key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.flash_tiles = p.flash_tiles;
@@ -706,8 +717,7 @@ blt_status blt_graphs_enable(blt_ctx *c, int32_t enable) {
 
 blt_status blt_attention_chunks(blt_ctx *c, int32_t chunks) {
   if (!c) return BLT_EINVAL;
-  if (chunks != 0 && chunks != 1 && chunks != 4 && chunks != 8)
-    return fail(c, BLT_EINVAL, "blt_attention_chunks: chunks must be 0, 1, 4 or 8");
+  if (chunks < 0) return fail(c, BLT_EINVAL, "blt_attention_chunks: chunks must be >= 0");
   c->attn_chunks = chunks;
   return BLT_OK;
 }

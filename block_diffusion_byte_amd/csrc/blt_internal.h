@@ -129,8 +129,10 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 // kernel, or of the causal kernel when ev_flash is set.  grid_chunks = 0
 // skips the split-K kernel and its merge (every sequence on the causal
 // kernel); flash_tiles = 0 skips the causal kernel.  nsub: chunks of
-// kAttnChunk keys per split-K workgroup (1, 4 or 8; bf16 with d_head <= 64
-// for 4 and 8), which must be 1 when a split-K sequence has more than 16 rows.
+// kAttnChunk keys per split-K workgroup (above 1 only for bf16 with d_head
+// <= 64), which must be 1 when a split-K sequence has more than 16 rows; when
+// one workgroup covers every chunk the kernel writes the output and no merge
+// runs.
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub,
                             int max_chunks, int flash_tiles, const RowDesc *rows, int R,

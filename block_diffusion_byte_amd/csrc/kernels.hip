@@ -813,9 +813,9 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 }
 
 
-// bfloat16: a workgroup takes NSUB consecutive chunks of kCK keys of one
-// (sequence, head), each wave 32 keys of every chunk, and up to 16 rows at a
-// time.  Scores are computed transposed, S^T = K Q^T, with
+// bfloat16: a workgroup takes nsub consecutive chunks of kCK keys of one
+// (sequence, head) (PIPE: nsub > 1), each wave 32 keys of every chunk, and up
+// to 16 rows at a time.  Scores are computed transposed, S^T = K Q^T, with
 // v_mfma_f32_16x16x32_bf16; the K rows are fed to the two 16-key score tiles
 // permuted (row m of tile t is key 8(m/4) + 4t + m%4) so that lane group q
 // ends up holding keys 8q..8q+7 of the wave's 32 for row lr: exactly the
@@ -824,18 +824,22 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // the output O^T[dim][row] keeps each row's values in the lanes that hold
 // its running max and sum (the rescale between chunks is lane-local).  The
 // loads of chunk i+1 are issued before chunk i is computed; the softmax runs
-// in base-2 units (one multiply and one exp2 per score) over all NSUB
-// chunks, P is split into bf16 hi and lo parts (two MFMAs per output tile,
-// about 16 significant bits), and the four waves' (o, m, l) are combined
-// through LDS in wave order into one partial per workgroup (m stored in
-// natural-log units).  More chunks per workgroup mean fewer partials to
-// write and merge; one chunk keeps the most workgroups for small passes,
-// and stays in registers for every group of 16 rows.
-template <int DH, int NSUB>
+// in base-2 units (one multiply and one exp2 per score) over all the
+// workgroup's chunks, P is split into bf16 hi and lo parts (two MFMAs per
+// output tile, about 16 significant bits), and the four waves' (o, m, l) are
+// combined through LDS in wave order into one partial per workgroup (m
+// stored in natural-log units) or, when one workgroup covers all of a
+// sequence's keys (direct), into the normalised output itself.  Partials
+// written to HBM slow the key stream far beyond their size, so large passes
+// take many chunks per workgroup; one chunk keeps the most workgroups for
+// small passes, and stays in registers for every group of 16 rows.
+template <int DH, bool PIPE>
 __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
                                                    int layer, const SeqDesc *seqs,
                                                    const RowDesc *rows, float *part,
-                                                   int max_chunks) {
+                                                   int max_chunks, int chunks_per_wg,
+                                                   int direct, void *a_out) {
+  constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
   constexpr int KS = DH / 32;                 // k-steps of the score product
   constexpr int DT = DH / 16;                 // 16-dim output tiles of P.V
   constexpr int KW = 32;                      // keys per wave and chunk
@@ -845,7 +849,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
   __shared__ int kends[16];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
-  const int key0 = c * kCK * NSUB;
+  const int key0 = c * kCK * chunks_per_wg;
   if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int d = g.n_heads * DH;
@@ -854,7 +858,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       (const uint16_t *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
   const uint16_t *Vt = Kp + (int64_t)g.n_heads * plane;
   const int klast = sd.kmax - 1;              // every cache row below kmax holds data
-  const int nsub = min(NSUB, (sd.kmax - key0 + kCK - 1) / kCK);   // chunks holding keys
+  // chunks holding keys (one without PIPE: the launcher passes chunks_per_wg = 1)
+  const int nsub = PIPE ? min(chunks_per_wg, (sd.kmax - key0 + kCK - 1) / kCK) : 1;
 
   // K (A operand: key kw0 + 8(lr/4) + 4kt + lr%4, dims 32ks+8lq..+8) and the
   // raw V rows (dims 16dt+lr, keys kw0+8lq..+8) of one chunk; key indices
@@ -993,11 +998,16 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       const float f3 = m3 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m3 - M);
       const float O = ((f0 * ow[0][r * OST + e] + f1 * ow[1][r * OST + e]) + f2 * ow[2][r * OST + e]) +
                       f3 * ow[3][r * OST + e];
+      const float L = ((f0 * lw[0][r] + f1 * lw[1][r]) + f2 * lw[2][r]) + f3 * lw[3][r];
+      if (direct) {                           // every key of the row: the output itself
+        ((uint16_t *)a_out)[(int64_t)(sd.row0 + rg + r) * d + h * DH + e] = f2bf(O / L);
+        continue;
+      }
       float *dst = part + (((int64_t)(sd.row0 + rg + r) * g.n_heads + h) * max_chunks + c) * (DH + 2);
       dst[e] = O;
       if (e == 0) {
         dst[DH] = M * 0.6931471805599453f;    // natural-log units for the merge
-        dst[DH + 1] = ((f0 * lw[0][r] + f1 * lw[1][r]) + f2 * lw[2][r]) + f3 * lw[3][r];
+        dst[DH + 1] = L;
       }
     }
     rg += 16;
@@ -2039,24 +2049,25 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   }
   if (ev_flash) ev0 = ev1 = nullptr;
   if (grid_chunks <= 0) return;
-  if (!BF || DH > 64 || (nsub != 4 && nsub != 8)) nsub = 1;
+  if (!BF || DH > 64 || nsub < 1) nsub = 1;
   const int gc = (grid_chunks + nsub - 1) / nsub;   // workgroups (partials) per (sequence, head)
   const dim3 grid(gc, g.n_heads, n_seq);
+  // one workgroup per (sequence, head): the output is written directly
+  const int direct = gc == 1;
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
-#define BLT_SPLITK(NS)                                                                            \
+#define BLT_SPLITK(PIPE)                                                                          \
   if (ev0)                                                                                        \
-    hipExtLaunchKernelGGL((k_attn_mfma<DH, NS>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g,   \
-                          layer, seqs, rows, part, max_chunks);                                   \
+    hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g,  \
+                          layer, seqs, rows, part, max_chunks, nsub, direct, a_out);              \
   else                                                                                            \
-    hipLaunchKernelGGL((k_attn_mfma<DH, NS>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows, \
-                       part, max_chunks);
+    hipLaunchKernelGGL((k_attn_mfma<DH, PIPE>), grid, dim3(256), 0, s, q, kv, g, layer, seqs,    \
+                       rows, part, max_chunks, nsub, direct, a_out);
     if constexpr (DH <= 64) {
-      if (nsub == 8) { BLT_SPLITK(8) }
-      else if (nsub == 4) { BLT_SPLITK(4) }
-      else { BLT_SPLITK(1) }
+      if (nsub > 1) { BLT_SPLITK(true) }
+      else { BLT_SPLITK(false) }
     } else {
-      BLT_SPLITK(1)
+      BLT_SPLITK(false)
     }
 #undef BLT_SPLITK
   } else {
@@ -2067,6 +2078,7 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
       hipLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
                          part, max_chunks);
   }
+  if (BF && direct) return;                 // no partials to merge
   // the merge takes its first 16 (or 64) chunks in one round of loads
   if (gc <= 16)
     hipLaunchKernelGGL((k_attn_merge<BF, DH, 16>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,

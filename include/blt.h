@@ -279,14 +279,16 @@ blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, 
 blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
 
 /* Keys per split-K self-attention workgroup, in chunks of 128 keys.
- * chunks = 0 (the default) lets each pass choose from its shape: 8 or 4
- * when one chunk per workgroup would give at least 32768 or 4096
- * workgroups (fewer partial results to write and merge), else 1.  chunks =
- * 1, 4 or 8 forces that count.  Counts above 1 apply only to bfloat16
+ * chunks = 0 (the default) lets each pass choose from its shape: the
+ * workgroups of a (sequence, head) share its chunks evenly, as many as give
+ * about 768 workgroups in the pass, so small passes take one chunk per
+ * workgroup and large ones many (all of a sequence's keys in one workgroup,
+ * with no merge of partial results, when sequences times heads reach 768).
+ * chunks >= 1 forces that count.  Counts above 1 apply only to bfloat16
  * contexts with d_model / n_heads <= 64 and to passes whose split-K
  * sequences have at most 16 rows; other passes take 1.  The count changes
- * the rounding of the softmax sums, not what is computed.  BLT_EINVAL for
- * any other value. */
+ * the rounding of the softmax sums, not what is computed.  BLT_EINVAL for a
+ * negative count. */
 blt_status blt_attention_chunks(blt_ctx *ctx, int32_t chunks);
 
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):

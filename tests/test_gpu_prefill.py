@@ -11,10 +11,12 @@ logits with the float64 oracle's cached decoder (bf16 tolerance: 2e-2
 absolute), and every greedy byte whose oracle top-2 gap is outside the
 rounding band.
 
-The split-K kernel walks 1, 4 or 8 chunks of 128 keys per workgroup; the
-last test forces each count on short appends after contexts whose chunk
-counts are not multiples of 4 or 8 (one sequence shorter than a whole
-workgroup's span), with 1 to 9 rows per sequence whose key counts differ.
+The split-K kernel walks one or more chunks of 128 keys per workgroup (all
+of a sequence's chunks, with the output written directly and no merge, when
+one workgroup covers them); the last test forces several counts on short
+appends after contexts whose chunk counts are not multiples of them (one
+sequence shorter than a whole workgroup's span), with 1 to 9 rows per
+sequence whose key counts differ.
 """
 import numpy as np
 import pytest
@@ -149,8 +151,9 @@ LONG = MINI.replace(name="mini_chunks_bf16", prompt_len=1400, prompt_patches=350
 
 def test_split_k_chunks_per_workgroup_match_the_oracle():
     """Appends of 9, 1 and 6 rows after 700-, 1030- and 1385-byte contexts
-    (6, 9 and 12 chunks of keys) with 1, 4 and 8 chunks per workgroup, and
-    the default choice: every row's logits match the oracle, and the counts
+    (6, 9 and 12 chunks of keys) with 1, 3, 4, 8 and 64 chunks per workgroup
+    (64: one workgroup per sequence and head, no merge), and the default
+    choice: every row's logits match the oracle, and the counts
     agree with each other within the same bf16 tolerance (the attention
     output is rounded to bfloat16, so a different summation order can move
     it by one bf16 step, and the logits by a few thousandths)."""
@@ -174,16 +177,16 @@ def test_split_k_chunks_per_workgroup_match_the_oracle():
         ref = {s: seqs[s].expect(ctx[s], n_new[s]) for s in range(3)}
         plan = [(s, ctx[s], n_new[s]) for s in range(3)]
         got = {}
-        for chunks in (1, 4, 8, 0):
+        for chunks in (1, 3, 4, 8, 64, 0):
             blt.blt_attention_chunks(dec.ctx, chunks)
             got[chunks] = _append(blt, torch, dec, seqs, plan, z)   # rewrites the same rows
             for s in range(3):
                 _check(got[chunks][s], ref[s], f"{chunks} chunks per workgroup, seq {s}")
-        for chunks in (4, 8, 0):
+        for chunks in (3, 4, 8, 64, 0):
             err = max(np.abs(got[chunks][s] - got[1][s]).max() for s in range(3))
             say(f"{chunks} vs 1 chunks per workgroup: max logit difference {err:.3g}")
             assert err <= BF16_ABS
         with pytest.raises(blt.BltError):
-            blt.blt_attention_chunks(dec.ctx, 3)
+            blt.blt_attention_chunks(dec.ctx, -1)
     finally:
         dec.close()
