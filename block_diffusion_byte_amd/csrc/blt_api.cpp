@@ -282,19 +282,22 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                argmax_out, conf_out, logits_out, split_bytes, flash_flops, smp != nullptr,
                SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
                           smp ? smp->seed : 0}};
-  // Split-K attention: the workgroups of a (sequence, head) share its chunks
-  // evenly, as many workgroups as give about 768 in the pass (three per CU):
-  // partials written to memory slow the key stream far beyond their size,
-  // so large passes take many chunks per workgroup (all of them, and no
-  // merge, when the pass alone fills the chip), small ones one chunk each.
-  // Sequences of more than 16 split-K rows keep one chunk, held in
-  // registers for every 16-row group.  The choice depends on the pass's
-  // shape only.
+  // Split-K attention: a pass whose chunks number at most 1024 in all takes
+  // one chunk per workgroup (small passes need the parallelism); in larger
+  // ones the workgroups of a (sequence, head) share its chunks evenly, as
+  // many workgroups as give about 512 in the pass: partials written to
+  // memory slow the key stream far beyond their size, so they take many
+  // chunks per workgroup (all of them, and no merge, when sequences times
+  // heads reach 512).  Sequences of more than 16 split-K rows keep one
+  // chunk, held in registers for every 16-row group.  The choice depends on
+  // the pass's shape only (measured at the batch-1, batch-16 and batch-64
+  // shapes).
   auto chunks_per_wg = [&](int grid_chunks) {
     if (!c->bf16 || d / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return 1;
     if (c->attn_chunks) return c->attn_chunks;
     const int units = c->cfg.n_heads * p.S;
-    const int wg = std::min(grid_chunks, std::max(1, (768 + units - 1) / units));
+    if ((int64_t)units * grid_chunks <= 1024) return 1;
+    const int wg = std::min(grid_chunks, std::max(1, (512 + units - 1) / units));
     return (grid_chunks + wg - 1) / wg;
   };
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) {
