@@ -279,11 +279,12 @@ blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, 
 blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
 
 /* Keys per split-K self-attention workgroup, in chunks of 128 keys.
- * chunks = 0 (the default) lets each pass choose from its shape: the
- * workgroups of a (sequence, head) share its chunks evenly, as many as give
- * about 768 workgroups in the pass, so small passes take one chunk per
- * workgroup and large ones many (all of a sequence's keys in one workgroup,
- * with no merge of partial results, when sequences times heads reach 768).
+ * chunks = 0 (the default) lets each pass choose from its shape: a pass
+ * whose chunks number at most 1024 (summed over its sequences and heads)
+ * takes one chunk per workgroup; in larger ones the workgroups of a
+ * (sequence, head) share its chunks evenly, as many as give about 512
+ * workgroups in the pass (all of a sequence's keys in one workgroup, with
+ * no merge of partial results, when sequences times heads reach 512).
  * chunks >= 1 forces that count.  Counts above 1 apply only to bfloat16
  * contexts with d_model / n_heads <= 64 and to passes whose split-K
  * sequences have at most 16 rows; other passes take 1.  The count changes
