@@ -812,6 +812,111 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
   return __uint_as_float(c[0]) + __uint_as_float(c[1]);
 }
 
+// ---------------------------------------------------------------------------
+// GEMV on MFMA for bfloat16 passes of 1..15 rows (weight-streaming bound).
+//
+// A workgroup of 4 waves takes 16 output columns; wave w takes K quarter w
+// in 32-wide steps of v_mfma_f32_16x16x32_bf16, with the activations as the A
+// operand (lane l: row l%16, k 8(l/16)..+8; rows past the pass are zeros and
+// read nothing) and the weight rows as the B operand (lane l: column l%16),
+// so each lane's weight piece is 16 contiguous bytes and SB steps' pieces are
+// in flight at once.  The four waves' 16x16 sums are added through LDS in
+// wave order.  With the RMSNorm prologue the A operand is gain*h rounded to
+// bf16, each lane sums the squares of the h values it loads (in step order),
+// lane groups and waves add them in a fixed order, and the row's 1/rms
+// scales its outputs.  A row's result does not depend on the other rows of
+// the pass: the MFMA keeps rows apart and no order depends on the row count.
+// Its cost hardly grows with the row count (a cold pass of 1 to 9 rows at the
+// 1B-class shapes runs in the time of a plain read of the weights).
+template <int PRO, int SB>
+__global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
+  const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l & 15, lq = l >> 4;
+  const int n0 = blockIdx.x * 16;
+  const int kq = a.K / 4, steps = kq / 32;  // this wave's K range in 32-wide steps (a multiple of SB)
+  const int kw = w * kq + 8 * lq;
+  const bool live = lr < a.R;
+  const int row = min(lr, a.R - 1);
+  // the lane's weight row: output column n0 + lr (QKV+RoPE: the permuted row
+  // that keeps both halves of a rotation pair in one workgroup)
+  const int col = min(n0 + lr, a.N - 1);
+  const uint16_t *wp =
+      (const uint16_t *)a.W + (int64_t)(a.qkv_rope ? qkv_rope_row(a, col) : col) * a.K + kw;
+  const uint16_t *xp = nullptr, *gp = nullptr;
+  const float *hp = nullptr;
+  if constexpr (PRO == PRO_PLAIN) {
+    xp = (const uint16_t *)a.X + (a.x_row_off ? a.x_row_off[row] : (int64_t)row * a.ldx) + kw;
+  } else {
+    hp = a.H + (int64_t)row * a.ldh + kw;
+    gp = (const uint16_t *)a.gain + kw;
+  }
+  __shared__ float red[4][16][17];
+  __shared__ float ssq[4][16];
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float ss = 0.f;
+  for (int s0 = 0; s0 < steps; s0 += SB) {
+    u32x4_t wv[SB], xv[SB], gv[SB];
+    float4 h0[SB], h1[SB];
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      const int k = (s0 + j) * 32;
+      wv[j] = *(const u32x4_t *)(wp + k);
+      if constexpr (PRO == PRO_PLAIN) {
+        xv[j] = live ? *(const u32x4_t *)(xp + k) : u32x4_t{0u, 0u, 0u, 0u};
+      } else {
+        h0[j] = live ? *(const float4 *)(hp + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+        h1[j] = live ? *(const float4 *)(hp + k + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+        gv[j] = *(const u32x4_t *)(gp + k);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SB; ++j) {
+      u32x4_t av;
+      if constexpr (PRO == PRO_PLAIN) {
+        av = xv[j];
+      } else {
+        const float hv[8] = {h0[j].x, h0[j].y, h0[j].z, h0[j].w, h1[j].x, h1[j].y, h1[j].z, h1[j].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ss = fmaf(hv[2 * i], hv[2 * i], ss);
+          ss = fmaf(hv[2 * i + 1], hv[2 * i + 1], ss);
+          av[i] = f2bf2(__uint_as_float(gv[j][i] << 16) * hv[2 * i],
+                        __uint_as_float(gv[j][i] & 0xffff0000u) * hv[2 * i + 1]);
+        }
+      }
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                     __builtin_bit_cast(bf16x8_t, wv[j]), acc, 0, 0, 0);
+    }
+  }
+  // acc[v]: row 4(l/16)+v, column l%16 of the tile
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[w][4 * lq + v][lr] = acc[v];
+  if constexpr (PRO == PRO_NORM) {
+    ss = sum_lane_groups(ss);               // the four lane groups holding row lr
+    if (lq == 0) ssq[w][lr] = ss;
+  }
+  __syncthreads();
+  const int r = t >> 4, c = t & 15;         // one output per thread: row r, column n0 + c
+  if (r >= a.R) return;
+  float rinv = 1.f;
+  if constexpr (PRO == PRO_NORM)
+    rinv = 1.f / sqrtf((((ssq[0][r] + ssq[1][r]) + ssq[2][r]) + ssq[3][r]) / (float)a.K + a.eps);
+  auto out = [&](int cc) {
+    return (((red[0][r][cc] + red[1][r][cc]) + red[2][r][cc]) + red[3][r][cc]) * rinv;
+  };
+  if (a.qkv_rope) {
+    // outputs (n0+c, n0+c+1), c even: the (j, j + d_h/2) pair of one head
+    const int i0 = n0 + c;
+    if ((c & 1) || i0 + 1 >= a.N) return;
+    const RowDesc rd = a.rows[r];
+    const QkvEpi qe{rd.pos, rd.slot, a.rope_tab[(int64_t)rd.pos * (a.d_head >> 1) + qkv_pair_j(a, i0)]};
+    qkv_rope_store<true>(a, r, i0, out(c), out(c + 1), qe);
+    return;
+  }
+  const int n = n0 + c;
+  if (n >= a.N) return;
+  epilogue<true>(a, r, n, out(c), a.ep == EP_RESID ? resid_operands(a, r, n) : ResidEpi{0.f, 0.f});
+}
+
 
 // bfloat16: a workgroup takes nsub consecutive chunks of kCK keys of one
 // (sequence, head) (PIPE: nsub > 1), each wave 32 keys of every chunk, and up
@@ -1956,6 +2061,23 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     return hipErrorInvalidValue;
   if (!bf16 || a.R < kGemvRows) {
     if (pending) return hipErrorInvalidValue;
+    // bfloat16: the MFMA GEMV up to K = 1536 (with longer rows its
+    // workgroups of 16 columns are too few for the weight stream, and the
+    // dot-product GEMV is faster: measured at K = 2048 and 4096).  The
+    // choice depends on the matrix only, never on the row count.
+    if (bf16 && a.K <= 1536 && a.K % 128 == 0) {
+      const int steps = a.K / 128;
+      const dim3 g((a.N + 15) / 16);
+#define BLT_GEMV_MFMA(SB)                                                                        \
+  if (a.pro == PRO_NORM) hipLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB>), g, dim3(256), 0, s, a); \
+  else hipLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB>), g, dim3(256), 0, s, a);
+      if (steps % 8 == 0) { BLT_GEMV_MFMA(8) }
+      else if (steps % 4 == 0) { BLT_GEMV_MFMA(4) }
+      else if (steps % 2 == 0) { BLT_GEMV_MFMA(2) }
+      else { BLT_GEMV_MFMA(1) }
+#undef BLT_GEMV_MFMA
+      return hipGetLastError();
+    }
     return bf16 ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
   }
   GemmArgs b = a;
