@@ -244,6 +244,42 @@ def test_blt_s_equals_greedy_on_gpu_full_size():
         f"encoder/global passes {s['n_eg']} vs {g['n_eg']}, mean accepted {s['accepted'] / s['rounds']:.2f}")
 
 
+def test_row_result_does_not_depend_on_the_pass():
+    """A row's logits are bit-identical whether it is appended alone or with
+    eight other rows in one pass (GEMVs on MFMA and on dot products, split-K
+    attention): the property BLT-S relies on to reproduce greedy decoding,
+    checked directly at the 1B-class decoder width (d_model 1024, so every
+    GEMV kernel of the batch-1 path runs)."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[1].replace(n_layers=2, prompt_len=160, prompt_patches=40, n_gen=8, block=4)
+    w = bltgen.make_weights(wl, gains="random")
+    inp = bltgen.make_sequence_inputs(wl, 0)
+    lat = [min(i // 4, 39) for i in range(160)]
+    outs = []
+    for split in (False, True):
+        dec = decoder_for(wl, w, max_batch=1, max_rows=160)
+        try:
+            table = torch.from_numpy(inp["latents"]).to("cuda:0", dec.torch_dtype)
+            blt.blt_latents_put(dec.ctx, dec.state, [0] * 40, list(range(40)), table, 0)
+            z = torch.zeros(160 * 257, device="cuda:0")
+            # a 100-row prefix (causal kernel), then rows 100..108 in one pass or one by one
+            blt.blt_kv_append(dec.ctx, dec.state, [0], [0], [100], 100, lat[:100],
+                              bytes_=inp["prompt"][:100], logits_out=z)
+            got = []
+            starts = [(100 + j, 1) for j in range(9)] if split else [(100, 9)]
+            for st, n in starts:
+                blt.blt_kv_append(dec.ctx, dec.state, [0], [st], [n], n, lat[st:st + n],
+                                  bytes_=inp["prompt"][st:st + n], logits_out=z)
+                torch.cuda.synchronize()
+                got.append(z[:n * 257].view(n, 257).cpu().numpy().copy())
+            outs.append(np.concatenate(got))
+        finally:
+            dec.close()
+    assert np.array_equal(outs[0], outs[1]), np.abs(outs[0] - outs[1]).max()
+    say("9 rows in one pass vs one by one: logits bit-identical")
+
+
 def test_pass_is_deterministic():
     import torch
     import block_diffusion_byte_amd as blt
