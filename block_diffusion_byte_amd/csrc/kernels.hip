@@ -1148,8 +1148,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
 // staged through LDS (double-buffered: the next tile's loads are in flight
 // during the current tile's products).  Same MFMA formulation as the split-K
 // kernel: S^T = K Q^T leaves each lane with scores of one row, which are
-// already the B operand of O^T += V^T P^T (P split into bf16 hi and lo
-// parts), and the lane's O^T entries belong to that same row, so the softmax
+// already the B operand of O^T += V^T P^T (P rounded to bf16 for the
+// product, its sum kept in f32: the kernel is bound by its MFMA and softmax
+// work, and the hi + lo split of the split-K kernel would double the P.V
+// products), and the lane's O^T entries belong to that same row, so the softmax
 // bookkeeping is lane-local apart from the row max over the four lane groups
 // (two permlane swaps).  Each K and V operand read from LDS serves both row
 // groups.  Scores are taken in base-2 units (times log2(e) / sqrt(d_h)), so
@@ -1312,7 +1314,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
               for (int v = 0; v < 4; ++v)
                 if (key0 + 16 * k16 + 4 * lq + v >= my_kend[gi]) acc[gi][k16][v] = -INFINITY;
         }
-        u32x4_t ph[2][NJ], pl[2][NJ];
+        u32x4_t ph[2][NJ];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
           float mt = -INFINITY;
@@ -1331,10 +1333,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
             const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4], c2, -m_new));
             const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4 + 1], c2, -m_new));
             ps += p0 + p1;
-            const uint32_t hb = f2bf2(p0, p1);
-            ph[gi][i / 8][(i % 8) / 2] = hb;
-            pl[gi][i / 8][(i % 8) / 2] =
-                f2bf2(p0 - __uint_as_float(hb << 16), p1 - __uint_as_float(hb & 0xffff0000u));
+            ph[gi][i / 8][(i % 8) / 2] = f2bf2(p0, p1);
           }
           l_run[gi] = l_run[gi] * alpha + ps;
           if (__ballot(alpha != 1.f)) {       // the running max moved for some row of the wave
@@ -1355,8 +1354,6 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
             for (int gi = 0; gi < 2; ++gi) {
               o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                   va, __builtin_bit_cast(bf16x8_t, ph[gi][j]), o[gi][dt], 0, 0, 0);
-              o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                  va, __builtin_bit_cast(bf16x8_t, pl[gi][j]), o[gi][dt], 0, 0, 0);
             }
           }
       }
