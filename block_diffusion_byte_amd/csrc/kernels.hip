@@ -2058,11 +2058,13 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     return hipErrorInvalidValue;
   if (!bf16 || a.R < kGemvRows) {
     if (pending) return hipErrorInvalidValue;
-    // bfloat16: the MFMA GEMV up to K = 1536 (with longer rows its
-    // workgroups of 16 columns are too few for the weight stream, and the
-    // dot-product GEMV is faster: measured at K = 2048 and 4096).  The
-    // choice depends on the matrix only, never on the row count.
-    if (bf16 && a.K <= 1536 && a.K % 128 == 0) {
+    // bfloat16: the MFMA GEMV for K <= 1536 and N >= 2048 (QKV, W1, the
+    // cross-vector product).  With longer rows or fewer columns its
+    // workgroups of 16 columns are too few for the weight stream and the
+    // dot-product GEMV is faster (measured: K = 2048 and 4096; W_o and the
+    // head in decode passes).  The choice depends on the matrix only, never
+    // on the row count.
+    if (bf16 && a.K <= 1536 && a.K % 128 == 0 && a.N >= 2048) {
       const int steps = a.K / 128;
       const dim3 g((a.N + 15) / 16);
 #define BLT_GEMV_MFMA(SB)                                                                        \
