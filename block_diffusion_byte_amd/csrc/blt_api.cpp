@@ -153,6 +153,7 @@ struct PassLaunch {
   bool sample;                       // block rows draw their bytes (smp)
   SampleArgs smp;
   int attn_sub = 1;                  // kAttnChunk-key chunks per split-K attention workgroup
+  int attn_wg = 1;                   // 2: eight-wave workgroups, one per (sequence, head)
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
@@ -193,7 +194,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
       if (pb != BLT_OK) return pb;
     }
     HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, p.attn_sub,
-                                c->max_chunks,
+                                p.attn_wg, c->max_chunks,
                                 p.flash_tiles, c->rows_d, R, c->part, c->xa, e0, e1, ev_flash, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
@@ -283,35 +284,46 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
                           smp ? smp->seed : 0}};
   // Split-K attention: a pass whose chunks number at most 1024 in all takes
-  // one chunk per workgroup (small passes need the parallelism); in larger
-  // ones the workgroups of a (sequence, head) share its chunks evenly, as
-  // many workgroups as give about 512 in the pass: partials written to
-  // memory slow the key stream far beyond their size, so they take many
-  // chunks per workgroup (all of them, and no merge, when sequences times
-  // heads reach 512).  Sequences of more than 16 split-K rows keep one
-  // chunk, held in registers for every 16-row group.  The choice depends on
-  // the pass's shape only (measured at the batch-1, batch-16 and batch-64
-  // shapes).
-  auto chunks_per_wg = [&](int grid_chunks) {
-    if (!c->bf16 || d / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return 1;
-    if (c->attn_chunks) return c->attn_chunks;
+  // one chunk per workgroup (small passes need the parallelism).  In larger
+  // ones, when sequences times heads reach 256, one eight-wave workgroup per
+  // (sequence, head) walks all of its chunks and writes the output (no
+  // partials, no merge); below that the workgroups of a (sequence, head)
+  // share its chunks evenly, as many as give about 512 in the pass: partials
+  // written to memory slow the key stream far beyond their size, so they
+  // take many chunks per workgroup.  Sequences of more than 16 split-K rows
+  // keep one chunk, held in registers for every 16-row group.  The choice
+  // depends on the pass's shape only (measured at the batch-1, batch-16 and
+  // batch-64 shapes).
+  auto attn_policy = [&](int grid_chunks) {
+    p.attn_sub = 1;
+    p.attn_wg = 1;
+    if (!c->bf16 || d / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return;
+    if (c->attn_chunks) {
+      p.attn_sub = c->attn_chunks;
+      return;
+    }
     const int units = c->cfg.n_heads * p.S;
-    if ((int64_t)units * grid_chunks <= 1024) return 1;
+    if ((int64_t)units * grid_chunks <= 1024) return;
+    if (units >= 256) {
+      p.attn_sub = grid_chunks;
+      p.attn_wg = 2;
+      return;
+    }
     const int wg = std::min(grid_chunks, std::max(1, (512 + units - 1) / units));
-    return (grid_chunks + wg - 1) / wg;
+    p.attn_sub = (grid_chunks + wg - 1) / wg;
   };
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) {
-    p.attn_sub = chunks_per_wg(p.grid_chunks);
+    attn_policy(p.grid_chunks);
     return enqueue_pass(c, p, c->stream);
   }
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
   p.grid_chunks = std::min((p.grid_chunks + 3) / 4 * 4, c->max_chunks);
-  p.attn_sub = chunks_per_wg(p.grid_chunks);
+  attn_policy(p.grid_chunks);
   PassKey key;
   memset(&key, 0, sizeof(key));
   key.R = p.R; key.S = p.S; key.grid_chunks = p.grid_chunks; key.flash_tiles = p.flash_tiles;
-  key.attn_sub = p.attn_sub;
+  key.attn_sub = p.attn_sub; key.attn_wg = p.attn_wg;
   key.unmask = unmask;
   key.mode = mode;
   memcpy(&key.alpha_bits, &alpha, sizeof(float));

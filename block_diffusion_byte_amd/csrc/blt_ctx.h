@@ -28,7 +28,7 @@ struct StageSlot {
 // Everything the kernel sequence of a decoder pass depends on besides the
 // staged descriptors: passes with equal keys replay one HIP graph.
 struct PassKey {
-  int R, S, grid_chunks, flash_tiles, unmask, mode, sample, attn_sub;
+  int R, S, grid_chunks, flash_tiles, unmask, mode, sample, attn_sub, attn_wg;
   uint32_t alpha_bits, temp_bits, top_p_bits;
   uint64_t seed;
   const void *kv, *cross, *block_tok, *tokens_dev, *masked_left, *argmax_out, *conf_out,

@@ -132,9 +132,11 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 // kAttnChunk keys per split-K workgroup (above 1 only for bf16 with d_head
 // <= 64), which must be 1 when a split-K sequence has more than 16 rows; when
 // one workgroup covers every chunk the kernel writes the output and no merge
-// runs.
+// runs.  wg = 2 (bf16, d_head <= 64, at most 16 split-K rows per sequence):
+// one eight-wave workgroup per (sequence, head) over all grid_chunks chunks,
+// writing the output directly; nsub is then ignored.
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub,
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub, int wg,
                             int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
                             hipStream_t s);

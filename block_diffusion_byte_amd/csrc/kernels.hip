@@ -937,26 +937,31 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
 // sequence's keys (direct), into the normalised output itself.  Partials
 // written to HBM slow the key stream far beyond their size, so large passes
 // take many chunks per workgroup; one chunk keeps the most workgroups for
-// small passes, and stays in registers for every group of 16 rows.
-template <int DH, bool PIPE>
-__global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
-                                                   int layer, const SeqDesc *seqs,
-                                                   const RowDesc *rows, float *part,
-                                                   int max_chunks, int chunks_per_wg,
-                                                   int direct, void *a_out) {
+// small passes, and stays in registers for every group of 16 rows.  WG = 2:
+// eight waves in two groups that take alternate chunks (group 0 the even
+// ones), so one workgroup covers a (sequence, head) with twice the loads in
+// flight; their eight (o, m, l) are combined the same way.
+template <int DH, bool PIPE, int WG>
+__global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
+                                                        int layer, const SeqDesc *seqs,
+                                                        const RowDesc *rows, float *part,
+                                                        int max_chunks, int chunks_per_wg,
+                                                        int direct, void *a_out) {
   constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
+  constexpr int NWV = 4 * WG;                 // waves
   constexpr int KS = DH / 32;                 // k-steps of the score product
   constexpr int DT = DH / 16;                 // 16-dim output tiles of P.V
   constexpr int KW = 32;                      // keys per wave and chunk
   constexpr int OST = DH + 4;                 // LDS row stride of the wave outputs
-  __shared__ float ow[4][16 * OST];
-  __shared__ float mw[4][16], lw[4][16];
+  __shared__ float ow[NWV][16 * OST];
+  __shared__ float mw[NWV][16], lw[NWV][16];
   __shared__ int kends[16];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const SeqDesc sd = seqs[b];
   const int key0 = c * kCK * chunks_per_wg;
   if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+  const int grp = w >> 2, wq = w & 3;         // chunk group (chunks grp, grp + WG, ...), 32-key slice
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
   const uint16_t *Kp =
@@ -994,7 +999,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
   int my_kend = rows[sd.row0 + min(lr, nr - 1)].kend;
   bf16x8_t ka[2][KS], kn[2][KS];
   u32x4_t vg[DT], vn[DT];
-  load(key0 + w * KW, ka, vg);
+  if (grp < nsub) load(key0 + kCK * grp + wq * KW, ka, vg);
   const float c2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
 
   for (int rg = 0;;) {
@@ -1014,9 +1019,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
-    for (int sb = 0; sb < nsub; ++sb) {
-      const int kw0 = key0 + kCK * sb + w * KW;
-      if (NSUB > 1 && sb + 1 < nsub) load(kw0 + kCK, kn, vn);
+    for (int sb = grp; sb < nsub; sb += WG) {
+      const int kw0 = key0 + kCK * sb + wq * KW;
+      if (NSUB > 1 && sb + WG < nsub) load(kw0 + WG * kCK, kn, vn);
       const int kq = kw0 + 8 * lq;            // the lane group's first key
       // S^T tiles: acc[kt][v] = score of key kq+4kt+v for row lr
       f32x4_t acc[2];
@@ -1092,18 +1097,19 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
       lw[w][lr] = l;
     }
     __syncthreads();
-    for (int i = t; i < nr * DH; i += 256) {
+    for (int i = t; i < nr * DH; i += 256 * WG) {
       const int r = i / DH, e = i - r * DH;
       if (kends[r] <= key0) continue;
-      const float m0 = mw[0][r], m1 = mw[1][r], m2 = mw[2][r], m3 = mw[3][r];
-      const float M = fmaxf(fmaxf(m0, m1), fmaxf(m2, m3));
-      const float f0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - M);
-      const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - M);
-      const float f2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - M);
-      const float f3 = m3 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m3 - M);
-      const float O = ((f0 * ow[0][r * OST + e] + f1 * ow[1][r * OST + e]) + f2 * ow[2][r * OST + e]) +
-                      f3 * ow[3][r * OST + e];
-      const float L = ((f0 * lw[0][r] + f1 * lw[1][r]) + f2 * lw[2][r]) + f3 * lw[3][r];
+      float M = -INFINITY;
+#pragma unroll
+      for (int x = 0; x < NWV; ++x) M = fmaxf(M, mw[x][r]);
+      float O = 0.f, L = 0.f;                 // in wave order
+#pragma unroll
+      for (int x = 0; x < NWV; ++x) {
+        const float f = mw[x][r] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mw[x][r] - M);
+        O += f * ow[x][r * OST + e];
+        L += f * lw[x][r];
+      }
       if (direct) {                           // every key of the row: the output itself
         ((uint16_t *)a_out)[(int64_t)(sd.row0 + rg + r) * d + h * DH + e] = f2bf(O / L);
         continue;
@@ -1128,7 +1134,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(const float *q, const void *k
     }
     my_kend = rows[sd.row0 + rg + min(lr, nr - 1)].kend;
     // the first chunk again (one chunk per workgroup keeps it in registers)
-    if constexpr (NSUB > 1) load(key0 + w * KW, ka, vg);
+    if constexpr (NSUB > 1)
+      if (grp < nsub) load(key0 + kCK * grp + wq * KW, ka, vg);
     __syncthreads();                          // LDS of this row group fully read
   }
 }
@@ -2154,7 +2161,7 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
-                        int n_seq, int grid_chunks, int nsub, int max_chunks, int flash_tiles,
+                        int n_seq, int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
                         hipEvent_t ev1, bool ev_flash, hipStream_t s) {
   if constexpr (BF) {
@@ -2171,24 +2178,27 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   if (ev_flash) ev0 = ev1 = nullptr;
   if (grid_chunks <= 0) return;
   if (!BF || DH > 64 || nsub < 1) nsub = 1;
+  if (!BF || DH > 64) wg = 1;
+  if (wg == 2) nsub = grid_chunks;
   const int gc = (grid_chunks + nsub - 1) / nsub;   // workgroups (partials) per (sequence, head)
   const dim3 grid(gc, g.n_heads, n_seq);
   // one workgroup per (sequence, head): the output is written directly
   const int direct = gc == 1;
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
-#define BLT_SPLITK(PIPE)                                                                          \
+#define BLT_SPLITK(PIPE, WG)                                                                      \
   if (ev0)                                                                                        \
-    hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g,  \
-                          layer, seqs, rows, part, max_chunks, nsub, direct, a_out);              \
+    hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, ev0, ev1, 0,   \
+                          q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out);    \
   else                                                                                            \
-    hipLaunchKernelGGL((k_attn_mfma<DH, PIPE>), grid, dim3(256), 0, s, q, kv, g, layer, seqs,    \
-                       rows, part, max_chunks, nsub, direct, a_out);
+    hipLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, q, kv, g, layer,  \
+                       seqs, rows, part, max_chunks, nsub, direct, a_out);
     if constexpr (DH <= 64) {
-      if (nsub > 1) { BLT_SPLITK(true) }
-      else { BLT_SPLITK(false) }
+      if (wg == 2) { BLT_SPLITK(true, 2) }
+      else if (nsub > 1) { BLT_SPLITK(true, 1) }
+      else { BLT_SPLITK(false, 1) }
     } else {
-      BLT_SPLITK(false)
+      BLT_SPLITK(false, 1)
     }
 #undef BLT_SPLITK
   } else {
@@ -2210,15 +2220,16 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub,
+                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub, int wg,
                             int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
                             hipStream_t s) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
-  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, max_chunks,    \
-                                  flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);      \
-  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, max_chunks,        \
+  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, wg,            \
+                                  max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1,        \
+                                  ev_flash, s);                                                   \
+  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, wg, max_chunks,    \
                               flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;

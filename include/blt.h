@@ -281,11 +281,12 @@ blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
 /* Keys per split-K self-attention workgroup, in chunks of 128 keys.
  * chunks = 0 (the default) lets each pass choose from its shape: a pass
  * whose chunks number at most 1024 (summed over its sequences and heads)
- * takes one chunk per workgroup; in larger ones the workgroups of a
- * (sequence, head) share its chunks evenly, as many as give about 512
- * workgroups in the pass (all of a sequence's keys in one workgroup, with
- * no merge of partial results, when sequences times heads reach 512).
- * chunks >= 1 forces that count.  Counts above 1 apply only to bfloat16
+ * takes one chunk per workgroup; in larger ones, when sequences times heads
+ * reach 256, one eight-wave workgroup per (sequence, head) takes all of its
+ * keys and writes the output (no merge of partial results); otherwise the
+ * workgroups of a (sequence, head) share its chunks evenly, as many as give
+ * about 512 workgroups in the pass.  chunks >= 1 forces that count (on
+ * four-wave workgroups).  Counts above 1 apply only to bfloat16
  * contexts with d_model / n_heads <= 64 and to passes whose split-K
  * sequences have at most 16 rows; other passes take 1.  The count changes
  * the rounding of the softmax sums, not what is computed.  BLT_EINVAL for a
