@@ -961,7 +961,8 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
   const int key0 = c * kCK * chunks_per_wg;
   if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
-  const int grp = w >> 2, wq = w & 3;         // chunk group (chunks grp, grp + WG, ...), 32-key slice
+  // chunk group (chunks grp, grp + WG, ...) and 32-key slice of the wave
+  const int grp = WG == 1 ? 0 : w >> 2, wq = WG == 1 ? w : w & 3;
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
   const uint16_t *Kp =
