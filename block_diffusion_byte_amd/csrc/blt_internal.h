@@ -105,6 +105,16 @@ struct KVGeom {
   int n_layers, n_heads, d_head, max_ctx;  // max_ctx: cache rows, kv_rows(cfg.max_ctx)
 };
 
+// Element offset of (key, dim) in a head's V plane.  The plane is cut into
+// tiles of kVTile keys, each stored [d_h][kVTile]: the kVTile keys of every
+// dimension that one attention wave reads form a single contiguous block
+// (d_h * kVTile elements), and 8 consecutive keys of one dimension are one
+// 16-byte piece.
+constexpr int kVTile = 32;
+__host__ __device__ inline int64_t v_off(int key, int dim, int d_head) {
+  return ((int64_t)(key / kVTile) * d_head + dim) * kVTile + key % kVTile;
+}
+
 // Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.
 // A residual product (EP_RESID) on the MFMA path whose K was split: its
 // partial products wait in ws[splits][R][N], and the next RMSNorm prologue

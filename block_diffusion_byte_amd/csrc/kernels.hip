@@ -227,10 +227,8 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
     kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
     kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
-    // V is stored transposed: [dim][position]
-    const int64_t vb = head * plane + (int64_t)j * a.max_ctx + e.pos;
-    kv[vb] = from_f<T>(y0);
-    kv[vb + (int64_t)half * a.max_ctx] = from_f<T>(y1);
+    kv[head * plane + v_off(e.pos, j, a.d_head)] = from_f<T>(y0);
+    kv[head * plane + v_off(e.pos, j + half, a.d_head)] = from_f<T>(y1);
   }
 }
 
@@ -256,9 +254,8 @@ __device__ __forceinline__ void qkv_rope_store_col(const GemmArgs &a, int r, int
     kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
     kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
-    const int64_t vb = head * plane + (int64_t)j * a.max_ctx + pos;   // V transposed
-    kv[vb] = from_f<T>(y0);
-    kv[vb + (int64_t)half * a.max_ctx] = from_f<T>(y1);
+    kv[head * plane + v_off(pos, j, a.d_head)] = from_f<T>(y0);
+    kv[head * plane + v_off(pos, j + half, a.d_head)] = from_f<T>(y1);
   }
 }
 
@@ -772,12 +769,11 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
     const float k1 = src[d + lo], k2 = src[d + hi];
     const int64_t kb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + hh) * plane +
                        (int64_t)rd.pos * dh;
-    // V transposed: [dim][position] of the head's V plane
-    const int64_t vb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 1) * g.n_heads + hh) * plane + rd.pos;
+    const int64_t vb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 1) * g.n_heads + hh) * plane;
     kv[kb + j] = from_f<T>(k1 * cs.x - k2 * cs.y);
     kv[kb + j + half] = from_f<T>(k2 * cs.x + k1 * cs.y);
-    kv[vb + (int64_t)j * g.max_ctx] = from_f<T>(src[2 * d + lo]);
-    kv[vb + (int64_t)(j + half) * g.max_ctx] = from_f<T>(src[2 * d + hi]);
+    kv[vb + v_off(rd.pos, j, dh)] = from_f<T>(src[2 * d + lo]);
+    kv[vb + v_off(rd.pos, j + half, dh)] = from_f<T>(src[2 * d + hi]);
   }
 }
 
@@ -785,8 +781,10 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
 // Split-K attention partials.
 //
 // Cache layout per (sequence, layer, head): K as [position][d_head] and V
-// transposed, [d_head][max_ctx], so that both products below read their
-// operands straight from HBM with 8- or 16-byte loads.
+// transposed in tiles of 32 positions, [max_ctx / 32][d_head][32] (v_off), so
+// that both products below read their operands straight from HBM with 8- or
+// 16-byte loads, and a wave's 32 keys of K and of V are each one contiguous
+// block.
 //
 // Workgroup (chunk c, head h, sequence b) owns keys [c*128, c*128+128) of
 // that sequence, for every row of the sequence in the pass; row r reads keys
@@ -925,7 +923,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
 // permuted (row m of tile t is key 8(m/4) + 4t + m%4) so that lane group q
 // ends up holding keys 8q..8q+7 of the wave's 32 for row lr: exactly the
 // B-operand layout of O^T += V^T P^T with k-slot 8q+i = key 8q+i, so the V
-// operand of lane (dim, q) is one 16-byte piece of the transposed V row and
+// operand of lane (dim, q) is one 16-byte piece of the transposed V tile and
 // the output O^T[dim][row] keeps each row's values in the lanes that hold
 // its running max and sum (the rescale between chunks is lane-local).  The
 // loads of chunk i+1 are issued before chunk i is computed; the softmax runs
@@ -973,7 +971,7 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
   const int nsub = PIPE ? min(chunks_per_wg, (sd.kmax - key0 + kCK - 1) / kCK) : 1;
 
   // K (A operand: key kw0 + 8(lr/4) + 4kt + lr%4, dims 32ks+8lq..+8) and the
-  // raw V rows (dims 16dt+lr, keys kw0+8lq..+8) of one chunk; key indices
+  // raw V pieces (dims 16dt+lr, keys kw0+8lq..+8) of one chunk; key indices
   // are clamped into the written cache rows
   auto load = [&](int kw0, bf16x8_t (&ka)[2][KS], u32x4_t (&vg)[DT]) {
 #pragma unroll
@@ -985,7 +983,7 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
     const int va = min(kw0 + 8 * lq, klast & ~7);   // a group clamped here lies wholly past kmax
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      vg[dt] = *(const u32x4_t *)(Vt + (int64_t)(16 * dt + lr) * g.max_ctx + va);
+      vg[dt] = *(const u32x4_t *)(Vt + v_off(va, 16 * dt + lr, DH));
   };
   int nr = min(16, sd.nrows);
   float4 qf[KS][2];
@@ -1201,7 +1199,12 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
   const float c2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
 
   // staging: thread t moves NK 16-byte pieces of K ([key][dim]) and of V^T
-  // ([dim][key]) per tile; pieces past kmax become zeros
+  // ([dim][key]) per tile; pieces past kmax become zeros.  V piece i is
+  // dimension vdim(i), keys 8 vpiece(i)..+8 of the tile: consecutive pieces
+  // run through the V plane's memory in order (its 32-key tiles are
+  // [dim][32 keys])
+  auto vdim = [](int i) { return (i % (DH * 4)) >> 2; };
+  auto vpiece = [](int i) { return 4 * (i / (DH * 4)) + (i & 3); };
   u32x4_t kr[NK], vr[NK];
   auto load = [&](int tk) {
     const int key0 = tk * KT;
@@ -1210,8 +1213,8 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
       const int i = t + 256 * j;
       const int kk = i / (DH / 8), kp = i % (DH / 8);
       kr[j] = *(const u32x4_t *)(Kp + (int64_t)(key0 + kk) * DH + 8 * kp);
-      const int dd = i / (KT / 8), vp = i % (KT / 8);
-      vr[j] = *(const u32x4_t *)(Vt + (int64_t)dd * g.max_ctx + key0 + 8 * vp);
+      const int dd = vdim(i), vp = vpiece(i);
+      vr[j] = *(const u32x4_t *)(Vt + v_off(key0 + 8 * vp, dd, DH));
     }
   };
   auto store = [&](int tk, int buf) {
@@ -1223,7 +1226,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
       u32x4_t kv = kr[j];
       if (key0 + kk >= kmax) kv = u32x4_t{0u, 0u, 0u, 0u};
       *(u32x4_t *)(&kt_s[buf][kk * KST + 8 * kp]) = kv;
-      const int dd = i / (KT / 8), vp = i % (KT / 8);
+      const int dd = vdim(i), vp = vpiece(i);
       u32x4_t vv = vr[j];
       const int k0 = key0 + 8 * vp;
       if (k0 + 8 > kmax) {
@@ -1437,11 +1440,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
   }
   const int kk = t >> 1, hf = t & 1;                  // score phase: key kk, half hf
   const int e = t % DH, kp = t / DH;                  // P.V phase: dim e, partition kp
-  // this thread's V column over its key partition: a contiguous run of V^T
+  // this thread's V column over its key partition (a row of the transposed V)
   float vcol[KPP];
 #pragma unroll
   for (int j = 0; j < KPP; ++j)
-    vcol[j] = Vt[(int64_t)e * g.max_ctx + key0 + min(kp * KPP + j, nkeys - 1)];
+    vcol[j] = Vt[v_off(key0 + min(kp * KPP + j, nkeys - 1), e, DH)];
 #pragma unroll
   for (int k = 0; k < QPT; ++k) {
     const int idx = t + 256 * k, r = idx / DH, ee = idx - r * DH;

@@ -113,8 +113,9 @@ typedef struct {
 /* Caller-owned decode state (device), sized by blt_state_size:
  *   kv    : keys (after RoPE) and values of cached rows, per
  *           [max_batch][n_layers] a K plane [n_heads][ctx][d_model/n_heads]
- *           and a transposed V plane [n_heads][d_model/n_heads][ctx], dtype,
- *           with ctx = max_ctx rounded up to a multiple of 128;
+ *           and a V plane [n_heads][ctx/32][d_model/n_heads][32] (V
+ *           transposed in tiles of 32 positions), dtype, with ctx = max_ctx
+ *           rounded up to a multiple of 128;
  *   cross : per-latent cross-attention contributions W_o^c W_v^c W_lat o_m,
  *           [max_batch][max_latents][n_layers][d_model], float32.
  * Rows beyond a sequence's committed length hold scratch (the current
