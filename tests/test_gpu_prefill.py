@@ -16,7 +16,9 @@ of a sequence's chunks, with the output written directly and no merge, when
 one workgroup covers them); the last test forces several counts on short
 appends after contexts whose chunk counts are not multiples of them (one
 sequence shorter than a whole workgroup's span), with 1 to 9 rows per
-sequence whose key counts differ.
+sequence whose key counts differ.  The last test takes a batch wide enough
+(sequences x heads = 256) for the eight-wave workgroup per (sequence, head),
+with ragged contexts and appends.
 """
 import numpy as np
 import pytest
@@ -188,5 +190,50 @@ def test_split_k_chunks_per_workgroup_match_the_oracle():
             assert err <= BF16_ABS
         with pytest.raises(blt.BltError):
             blt.blt_attention_chunks(dec.ctx, -1)
+    finally:
+        dec.close()
+
+
+WIDE = MINI.replace(name="mini_wide_bf16", d_model=512, n_heads=8, prompt_len=900, prompt_patches=225,
+                    batch=32)
+
+
+def test_eight_wave_attention_ragged_batch_matches_the_oracle():
+    """32 sequences x 8 heads (256 pairs): a split-K pass of more than 1024
+    chunks in all takes one eight-wave workgroup per (sequence, head) with
+    the output written directly.  Contexts of 260..880 bytes (3 to 7 chunks,
+    odd and even counts, so the two wave groups get unequal shares) and
+    appends of 1 to 9 rows: every row's logits match the oracle, and agree
+    with one chunk per workgroup (partials and the merge kernel) within the
+    same bf16 tolerance."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = WIDE
+    w = bltgen.make_weights(wl, gains="random")
+    n = wl.batch
+    seqs = [_Seq(wl, w, s) for s in range(n)]
+    ctx = [260 + 20 * s for s in range(n)]
+    n_new = [1 + s % 9 for s in range(n)]
+    dec = decoder_for(wl, w, max_batch=n, max_rows=max(ctx))
+    try:
+        for s in range(n):
+            table = torch.from_numpy(seqs[s].inp["latents"]).to("cuda:0", dec.torch_dtype)
+            blt.blt_latents_put(dec.ctx, dec.state, [s] * wl.n_latents, list(range(wl.n_latents)),
+                                table, 0)
+        z = torch.zeros(n * max(ctx) * 257, device="cuda:0")
+        for s in range(n):   # contexts through the causal kernel, one sequence at a time
+            _append(blt, torch, dec, seqs, [(s, 0, ctx[s])], z)
+            seqs[s].expect(0, ctx[s])
+        ref = {s: seqs[s].expect(ctx[s], n_new[s]) for s in range(n)}
+        plan = [(s, ctx[s], n_new[s]) for s in range(n)]
+        got = {}
+        for chunks in (0, 1):   # the shape's own choice (eight waves), then one chunk
+            blt.blt_attention_chunks(dec.ctx, chunks)
+            got[chunks] = _append(blt, torch, dec, seqs, plan, z)   # rewrites the same rows
+            for s in range(n):
+                _check(got[chunks][s], ref[s], f"{chunks} chunks per workgroup, seq {s}")
+        err = max(np.abs(got[0][s] - got[1][s]).max() for s in range(n))
+        say(f"eight-wave vs one chunk per workgroup: max logit difference {err:.3g}")
+        assert err <= BF16_ABS
     finally:
         dec.close()
