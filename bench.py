@@ -132,7 +132,7 @@ def prefill_report(rows, seconds, max_rows, launches, ms, flops):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (this build has no multi-GPU path); got --gpus {args.gpus}",
+        print(f"bench.py measures one GPU only (the decoder path runs on a single GPU); got --gpus {args.gpus}",
               file=sys.stderr)
         sys.exit(2)
     import numpy as np
