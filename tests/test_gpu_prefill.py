@@ -205,7 +205,7 @@ def test_eight_wave_attention_ragged_batch_matches_the_oracle():
     odd and even counts, so the two wave groups get unequal shares) and
     appends of 1 to 9 rows: every row's logits match the oracle, and agree
     with one chunk per workgroup (partials and the merge kernel) within the
-    same bf16 tolerance."""
+    same bf16 tolerance; graph replays of the pass match it exactly."""
     import torch
     import block_diffusion_byte_amd as blt
     wl = WIDE
@@ -235,5 +235,14 @@ def test_eight_wave_attention_ragged_batch_matches_the_oracle():
         err = max(np.abs(got[0][s] - got[1][s]).max() for s in range(n))
         say(f"eight-wave vs one chunk per workgroup: max logit difference {err:.3g}")
         assert err <= BF16_ABS
+        # graph capture and replay of the same pass (its chunk grid rounded
+        # up to a bucket) reproduce the direct launch bit for bit
+        blt.blt_attention_chunks(dec.ctx, 0)
+        blt.blt_graphs_enable(dec.ctx, True)
+        for rep in range(3):     # direct, captured, replayed
+            again = _append(blt, torch, dec, seqs, plan, z)
+            for s in range(n):
+                assert np.array_equal(again[s], got[0][s]), (rep, s)
+        blt.blt_graphs_enable(dec.ctx, False)
     finally:
         dec.close()
