@@ -847,6 +847,18 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
     hp = a.H + (int64_t)row * a.ldh + kw;
     gp = (const uint16_t *)a.gain + kw;
   }
+  // QKV + RoPE epilogue operands of this thread's output (row t/16, the pair
+  // at column n0 + t%16): the row's position and slot go out first, the
+  // rotation's cos/sin right after the first weight loads, so that neither
+  // dependent load is waited for after the products
+  const int erow = min(t >> 4, a.R - 1);
+  int epos = 0, eslot = 0;
+  float2 ecs = make_float2(1.f, 0.f);
+  if (a.qkv_rope) {
+    epos = a.rows[erow].pos;
+    eslot = a.rows[erow].slot;
+  }
+  __builtin_amdgcn_sched_barrier(0);
   __shared__ float red[4][16][17];
   __shared__ float ssq[4][16];
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -865,6 +877,11 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
         h1[j] = live ? *(const float4 *)(hp + k + 4) : make_float4(0.f, 0.f, 0.f, 0.f);
         gv[j] = *(const u32x4_t *)(gp + k);
       }
+    }
+    if (a.qkv_rope && s0 == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      ecs = a.rope_tab[(int64_t)epos * (a.d_head >> 1) + qkv_pair_j(a, min(n0 + (t & 15), a.N - 2))];
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int j = 0; j < SB; ++j) {
@@ -905,9 +922,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
     // outputs (n0+c, n0+c+1), c even: the (j, j + d_h/2) pair of one head
     const int i0 = n0 + c;
     if ((c & 1) || i0 + 1 >= a.N) return;
-    const RowDesc rd = a.rows[r];
-    const QkvEpi qe{rd.pos, rd.slot, a.rope_tab[(int64_t)rd.pos * (a.d_head >> 1) + qkv_pair_j(a, i0)]};
-    qkv_rope_store<true>(a, r, i0, out(c), out(c + 1), qe);
+    qkv_rope_store<true>(a, r, i0, out(c), out(c + 1), QkvEpi{epos, eslot, ecs});
     return;
   }
   const int n = n0 + c;
