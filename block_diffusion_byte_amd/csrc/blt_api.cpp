@@ -154,6 +154,7 @@ struct PassLaunch {
   SampleArgs smp;
   int attn_sub = 1;                  // kAttnChunk-key chunks per split-K attention workgroup
   int attn_wg = 1;                   // 2: eight-wave workgroups, one per (sequence, head)
+  const SeqDesc *seq1 = nullptr;     // host copy of a one-sequence pass's descriptor (direct launches)
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
@@ -193,8 +194,8 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
       blt_status pb = prof_next(c, ev_flash ? p.flash_flops : p.split_bytes, &e0, &e1);
       if (pb != BLT_OK) return pb;
     }
-    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.grid_chunks, p.attn_sub,
-                                p.attn_wg, c->max_chunks,
+    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.seq1, p.grid_chunks,
+                                p.attn_sub, p.attn_wg, c->max_chunks,
                                 p.flash_tiles, c->rows_d, R, c->part, c->xa, e0, e1, ev_flash, s));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = c->rows_d;
@@ -314,6 +315,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
   };
   if (!c->graphs || c->prof_family != BLT_PROF_OFF) {
     attn_policy(p.grid_chunks);
+    if (seqs.size() == 1) p.seq1 = &seqs[0];
     return enqueue_pass(c, p, c->stream);
   }
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the

@@ -144,10 +144,13 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 // one workgroup covers every chunk the kernel writes the output and no merge
 // runs.  wg = 2 (bf16, d_head <= 64, at most 16 split-K rows per sequence):
 // one eight-wave workgroup per (sequence, head) over all grid_chunks chunks,
-// writing the output directly; nsub is then ignored.
+// writing the output directly; nsub is then ignored.  sd_host (nullable): the
+// host copy of seqs[0] for a one-sequence pass, handed to the split-K kernel
+// with its launch (never for a captured launch, whose arguments would go
+// stale on replay).
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub, int wg,
-                            int max_chunks, int flash_tiles, const RowDesc *rows, int R,
+                            const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
+                            int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
                             hipStream_t s);
 bool gemv_supported(bool bf16, int K);

@@ -959,7 +959,8 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
                                                         int layer, const SeqDesc *seqs,
                                                         const RowDesc *rows, float *part,
                                                         int max_chunks, int chunks_per_wg,
-                                                        int direct, void *a_out) {
+                                                        int direct, void *a_out, SeqDesc sd_arg,
+                                                        int use_sd_arg) {
   constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
   constexpr int NWV = 4 * WG;                 // waves
   constexpr int KS = DH / 32;                 // k-steps of the score product
@@ -970,7 +971,9 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
   __shared__ float mw[NWV][16], lw[NWV][16];
   __shared__ int kends[16];
   const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const SeqDesc sd = seqs[b];
+  // a single sequence's descriptor may come with the launch: the key and
+  // query loads then need no memory round trip before them
+  const SeqDesc sd = use_sd_arg ? sd_arg : seqs[b];
   const int key0 = c * kCK * chunks_per_wg;
   if (key0 >= sd.kmax || sd.attn_flash) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
@@ -2180,7 +2183,8 @@ hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *row
 
 template <bool BF, int DH>
 static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, const SeqDesc *seqs,
-                        int n_seq, int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles,
+                        int n_seq, const SeqDesc *sd_host, int grid_chunks, int nsub, int wg,
+                        int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
                         hipEvent_t ev1, bool ev_flash, hipStream_t s) {
   if constexpr (BF) {
@@ -2203,15 +2207,18 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   const dim3 grid(gc, g.n_heads, n_seq);
   // one workgroup per (sequence, head): the output is written directly
   const int direct = gc == 1;
+  const SeqDesc sd_arg = sd_host && n_seq == 1 ? *sd_host : SeqDesc{};
+  const int use_sd_arg = sd_host && n_seq == 1;
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
 #define BLT_SPLITK(PIPE, WG)                                                                      \
   if (ev0)                                                                                        \
     hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, ev0, ev1, 0,   \
-                          q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out);    \
+                          q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out,     \
+                          sd_arg, use_sd_arg);                                                    \
   else                                                                                            \
     hipLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, q, kv, g, layer,  \
-                       seqs, rows, part, max_chunks, nsub, direct, a_out);
+                       seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg, use_sd_arg);
     if constexpr (DH <= 64) {
       if (wg == 2) { BLT_SPLITK(true, 2) }
       else if (nsub > 1) { BLT_SPLITK(true, 1) }
@@ -2239,17 +2246,17 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
-                            const SeqDesc *seqs, int n_seq, int grid_chunks, int nsub, int wg,
-                            int max_chunks, int flash_tiles, const RowDesc *rows, int R,
+                            const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
+                            int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
                             hipStream_t s) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
-  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, wg,            \
+  if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,   \
                                   max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1,        \
                                   ev_flash, s);                                                   \
-  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, grid_chunks, nsub, wg, max_chunks,    \
-                              flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);
+  else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,       \
+                              max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;
