@@ -426,7 +426,9 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
   chk(hipStreamCreateWithFlags(&c->cap_stream, hipStreamNonBlocking));
   c->row_off = ((size_t)cfg->max_batch * sizeof(SeqDesc) + 255) & ~(size_t)255;
   c->off_off = (c->row_off + (size_t)R * sizeof(RowDesc) + 255) & ~(size_t)255;
-  const size_t stage = c->off_off + 2 * (size_t)R * sizeof(int64_t);
+  // offsets area: the two row-offset lists of a latent batch (2 per row) or
+  // one draw index per sequence of a sampled verification
+  const size_t stage = c->off_off + std::max<size_t>(2 * (size_t)R, cfg->max_batch) * sizeof(int64_t);
   chk(hipMalloc(&c->desc_d, stage));
   if (he == hipSuccess) {
     c->seqs_d = (SeqDesc *)c->desc_d;
@@ -581,10 +583,13 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
     return fail(c, BLT_EINVAL, "blt_kv_append: sampled passes take at most 64 rows per sequence");
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
+  int32_t *wr = c->written_rows(st);
   for (int b = 0; b < batch; ++b) {
     const int n = n_rows[b], s0 = start_pos[b];
     if (n < 0 || n > n_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_kv_append: bad n_rows or start_pos");
     if ((int64_t)s0 + n > g.max_ctx) return fail(c, BLT_ECAPACITY, "blt_kv_append: rows beyond max_ctx");
+    if (n > 0 && s0 > wr[slot[b]])
+      return fail(c, BLT_EINVAL, "blt_kv_append: start_pos beyond the rows already written for the slot");
     if (n == 0) continue;
     if ((int64_t)rows.size() + n > g.max_rows) return fail(c, BLT_ECAPACITY, "blt_kv_append: more rows than max_rows");
     SeqDesc sd{slot[b], (int)rows.size(), n, s0 + n, -1, -1, 0, slot[b]};
@@ -599,8 +604,11 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
     seqs.push_back(sd);
   }
   if (rows.empty()) return BLT_OK;
-  return run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
-                  conf_out, logits_out, sampling);
+  bs = run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
+                conf_out, logits_out, sampling);
+  if (bs == BLT_OK)
+    for (const SeqDesc &sd : seqs) wr[sd.slot] = rows[sd.row0].pos + sd.nrows;
+  return bs;
 }
 
 blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
@@ -632,11 +640,14 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
   if (bs != BLT_OK) return bs;
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
+  int32_t *wr = c->written_rows(st);
   for (int b = 0; b < batch; ++b) {
     const int na = n_append_max > 0 ? n_append[b] : 0, s0 = start_pos[b];
     if (na < 0 || na > n_append_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad n_append or start_pos");
     const int64_t end = (int64_t)s0 + na + B;
     if (end > g.max_ctx) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: block beyond max_ctx");
+    if (s0 > wr[slot[b]])
+      return fail(c, BLT_EINVAL, "blt_decode_block_step: start_pos beyond the rows already written for the slot");
     if ((int64_t)rows.size() + na + B > g.max_rows) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: more rows than max_rows");
     const int bl = block_lat[b];
     if (bl < 0 || bl >= g.max_latents) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: latent index beyond max_latents");
@@ -656,8 +667,11 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
     }
     seqs.push_back(sd);
   }
-  return run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, (int)mode,
-                  masked_left, argmax_out, conf_out, logits_out, sampling);
+  bs = run_pass(c, st, rows, seqs, block_tok, nullptr, true, alpha, (int)mode,
+                masked_left, argmax_out, conf_out, logits_out, sampling);
+  if (bs == BLT_OK)
+    for (const SeqDesc &sd : seqs) wr[sd.slot] = rows[sd.row0].pos + (sd.nrows - sd.nblk);
+  return bs;
 }
 
 blt_status blt_verify_accept(blt_ctx *c, int32_t batch, const int32_t *slot, int32_t r,

@@ -91,6 +91,15 @@ struct blt_ctx {
   size_t prof_used = 0;
   uint64_t prof_launches = 0;
   double prof_ms = 0, prof_bytes = 0;
+  // clean cache rows written so far per (state, slot), keyed by the state's
+  // kv buffer: a pass may start at most at that count (rows past it were
+  // never written and would enter the softmax)
+  std::unordered_map<const void *, std::vector<int32_t>> written;
+  int32_t *written_rows(const blt_state *st) {
+    std::vector<int32_t> &v = written[st->kv];
+    if (v.empty()) v.assign(cfg.max_batch, 0);
+    return v.data();
+  }
 };
 
 namespace blt {

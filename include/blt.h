@@ -139,19 +139,37 @@ blt_status blt_destroy(blt_ctx *ctx);
 const char *blt_last_error(const blt_ctx *ctx);
 
 /* Make latents available to the decoder (one encoder/global pass delivers
- * them).  For entry i: latent vector o = table + (slot[i] * seq_stride +
+ * them).  pytorch.kr summary, "BLT-D attention mask": every decoder row
+ * reads exactly one latent (a clean byte o_{p(i)-1}, the last byte of a
+ * patch o_{p(i)}, block bytes o_M), so the cross-attention softmax over its
+ * single key is 1 and the read is the value path alone; it is computed here
+ * once per latent for every layer (the layer equation of "BLT
+ * architecture": B_l = D_{l-1} + W_o softmax(.) V).
+ * For entry i: latent vector o = table + (slot[i] * seq_stride +
  * idx[i]) * d_global (device, dtype), written as latent idx[i] of sequence
  * slot[i]: cross[slot][idx][l] = W_o^c_l W_v^c_l W_lat o for every layer l.
- * slot, idx: host arrays of n entries. */
+ * slot, idx: host arrays of n entries (any n: processed max_rows at a time).
+ * Errors: BLT_EINVAL for a NULL argument or a slot outside 0..max_batch-1,
+ * BLT_ECAPACITY for an index outside 0..max_latents-1; nothing is enqueued
+ * then. */
 blt_status blt_latents_put(blt_ctx *ctx, const blt_state *st, int32_t n, const int32_t *slot,
                            const int32_t *idx, const void *table, int64_t seq_stride);
 
 /* One decoder pass over clean rows only (prefill, autoregressive steps,
  * BLT-S drafts and the causal verification pass of BLT-S / BLT-DV).
+ * pytorch.kr summary, "BLT-D inference": the clean prefix is cached, so a
+ * pass computes only rows not cached yet (prefix caching); "BLT-S and
+ * BLT-DV": verification runs the full model causally over the draft once,
+ * which is this call over rows l..l+r; "BLT-S": each draft byte is one such
+ * pass of one row.
  * For sequence b of the batch: rows start_pos[b] .. start_pos[b]+n_rows[b]-1
  * of state slot slot[b] are computed causally over the cached prefix
  * [0, start_pos[b]) and each other, and their keys/values are written to the
  * cache (a start_pos below the previous length overwrites: rollback).
+ * start_pos[b] may not exceed the clean rows written so far for that slot
+ * of that state (by this call or blt_decode_block_step's appended rows, on
+ * this context; a state starts empty): rows past them hold no keys, and the
+ * call returns BLT_EINVAL.  The count is kept per state kv buffer address.
  * Row j of sequence b has token bytes[b*n_max+j] (host) -- or, if `bytes` is
  * NULL, tokens_dev[slot[b]*n_max+j] (device int32, e.g. the argmax of a
  * previous pass) -- and reads latent lat_idx[b*n_max+j] (host).
@@ -182,7 +200,8 @@ blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const
  * "BLT-D attention mask").  For sequence b: n_append[b] clean rows at
  * start_pos[b].. (tokens append_bytes[b*n_append_max+j], latents
  * append_lat[...], host) are appended to the cache as in blt_kv_append; then
- * B block rows at the following positions, tokens block_tok[slot[b]*B+j]
+ * B block rows at the following positions (start_pos[b] at most the rows
+ * written so far, as in blt_kv_append), tokens block_tok[slot[b]*B+j]
  * (device int32, 256 = [MASK]) and latent block_lat[b] (host), read every
  * cached row and every block row (BIDIR) or the block rows up to themselves
  * (CAUSAL).  Block rows are not kept as clean rows (their cache rows are

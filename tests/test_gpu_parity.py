@@ -324,5 +324,27 @@ def test_argument_errors_enqueue_nothing():
             assert ei.value.status == code
         with pytest.raises(blt.BltError):
             blt.blt_kv_append(dec.ctx, dec.state, [0], [0], [17], 17, [0] * 17, bytes_=[1] * 17)
+        # a pass may not start past the rows written for its slot: nothing
+        # is cached yet, so start 1 is rejected before anything runs; after
+        # 3 rows, start 3 is accepted and start 4 rejected, for both calls
+        for call in ("append", "block"):
+            def run(start, n=1):
+                if call == "append":
+                    blt.blt_kv_append(dec.ctx, dec.state, [1], [start], [n], n, [0] * n,
+                                      bytes_=[7] * n)
+                else:
+                    blt.blt_decode_block_step(dec.ctx, dec.state, [1], [start], bt, 4, [0], 0.7,
+                                              masked_left=ml)
+            with pytest.raises(blt.BltError) as ei:
+                run(4 if call == "block" else 1)
+            assert ei.value.status == blt.BLT_EINVAL
+        blt.blt_kv_append(dec.ctx, dec.state, [1], [0], [3], 3, [0] * 3, bytes_=[7] * 3)
+        blt.blt_kv_append(dec.ctx, dec.state, [1], [3], [1], 1, [0], bytes_=[7])
+        blt.blt_decode_block_step(dec.ctx, dec.state, [1], [4], bt, 4, [0], 0.7, masked_left=ml)
+        for bad in (5, 9):
+            with pytest.raises(blt.BltError) as ei:
+                blt.blt_kv_append(dec.ctx, dec.state, [1], [bad], [1], 1, [0], bytes_=[7])
+            assert ei.value.status == blt.BLT_EINVAL
+        torch.cuda.synchronize()
     finally:
         dec.close()

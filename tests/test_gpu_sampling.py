@@ -277,3 +277,48 @@ def test_sampling_argument_errors():
     with pytest.raises(blt.BltError) as ei:
         _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.0, 1)
     assert ei.value.status == blt.BLT_EINVAL
+
+
+def test_verify_sample_batch_above_twice_max_rows():
+    """blt_verify_sample stages one draw index per sequence: a batch of 64 on
+    a context of max_rows 16 (more sequences than the latent-offset lists
+    hold) must stay within the staging area and decide every sequence as
+    the oracle's rule does on the same float32 logits."""
+    import torch
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    w = bltgen.make_weights(wl)
+    batch, r, temp, top_p, seed = 64, 4, 0.9, 0.95, 77
+    dec = decoder_for(wl.replace(block=r), w, max_batch=batch, max_rows=16)
+    rng = np.random.default_rng(5)
+    zq = (3.0 * rng.standard_normal((batch, r, 257))).astype(np.float32)
+    zp = (3.0 * rng.standard_normal((batch, r + 1, 257))).astype(np.float32)
+    draft = rng.integers(0, 256, (batch, r)).astype(np.int32)
+    # half the drafts copy the verify rows' top byte, so acceptances happen
+    draft[::2] = np.argmax(zp[::2, :r, :256], axis=2)
+    draws = [int(v) for v in rng.integers(0, 1000, batch)]
+    dev = "cuda:0"
+    acc = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+    nxt = torch.full((batch,), -1, dtype=torch.int32, device=dev)
+    try:
+        blt.blt_verify_sample(dec.ctx, r, torch.from_numpy(draft).to(dev), r,
+                              torch.from_numpy(zq).to(dev), r, torch.from_numpy(zp).to(dev), r + 1,
+                              (temp, top_p, seed), draws, acc, nxt, slot=list(range(batch)))
+        torch.cuda.synchronize()
+        got_a, got_n = acc.cpu().numpy(), nxt.cpu().numpy()
+    finally:
+        dec.close()
+    compared = accepted = 0
+    for s in range(batch):
+        q = [decide.sampling_dist(zq[s, j].astype(np.float64), temp, top_p) for j in range(r)]
+        p = [decide.sampling_dist(zp[s, j].astype(np.float64), temp, top_p) for j in range(r + 1)]
+        u_acc = [decide.uniform(seed + s, draws[s] * loops.MAX_BLOCK + j) for j in range(r)]
+        u_next = decide.uniform(seed + s, draws[s] * loops.MAX_BLOCK + r)
+        a, b, margin = decide.verify_sample(list(draft[s]), q, p, u_acc, u_next)
+        if margin > 1e-5:
+            assert (int(got_a[s]), int(got_n[s])) == (a, b), f"sequence {s}"
+            compared += 1
+            accepted += a
+    say(f"verify_sample batch {batch} on max_rows 16: {compared} of {batch} decisions compared, "
+        f"{accepted} draft bytes accepted")
+    assert compared >= batch // 2 and accepted > 0
