@@ -678,3 +678,158 @@ def test_proxy_worked_example():
 
 def test_decoder_param_count():
     assert proxy.decoder_params(bltgen.WORKLOADS[1]) == 153_637_888
+
+
+# ---------------------------------------------------------------- BLT-S bookkeeping
+class _ScriptedDecoder:
+    """Stand-in for the cached decoder in the loops (same interface): row i
+    with token x_i and latent target t predicts stream[i+1] when x_i is the
+    stream's byte and t is row i's causal target in the stream's own
+    segmentation, else (stream[i+1] + 1) mod 256.  A draft row that reads a
+    stale latent therefore drafts a wrong byte, so accept lengths and pass
+    counts expose which latent every row read."""
+    stream = None
+    ctarget = None
+
+    def __init__(self, W, wl, latents, capacity):
+        self.length = 0
+        self.tau = np.full(capacity, -1, dtype=np.int64)
+
+    def run(self, tokens, start, targets, n_append, block_causal=False):
+        n = len(tokens)
+        z = np.zeros((n, 257))
+        for j in range(n):
+            i = start + j
+            right = int(tokens[j]) == self.stream[i] and int(targets[j]) == self.ctarget[i]
+            z[j, self.stream[i + 1] if right else (self.stream[i + 1] + 1) % 256] = 1.0
+        self.length = start + n_append
+        return z
+
+    def truncate(self, length):
+        self.length = length
+
+
+def test_blt_s_latent_bookkeeping_worked_example(monkeypatch):
+    """Hand-worked BLT-S rounds (k = 4) on a segmentation whose patch
+    boundaries fall inside drafts and on appended bytes: every draft row reads
+    the newest latent produced before the round (stale past the boundary),
+    the verify rows read their causal targets over the draft, and after a
+    round only patches ending inside the accepted bytes are available (the
+    appended correction or free byte was never seen by the encoder/global
+    pass).  Dropping the stale cap, or counting the appended byte's patch as
+    available, changes the accept lengths."""
+    with open(os.path.join(GOLDEN, "blts_targets_example.json")) as f:
+        g = json.load(f)
+    stream = g["prompt"] + g["continuation"] + g["extension"]
+    patch, ends = patcher.segment(stream, g["prompt_patches"], g["salt"])
+    assert [int(i) for i in np.flatnonzero(ends)] == g["patch_ends"]
+    # causal targets written from the definition: byte i reads the latent of
+    # the previous patch, the last byte of a patch reads its own
+    pe = set(g["patch_ends"])
+    ctarget = []
+    for i in range(len(stream)):
+        p = sum(1 for e in pe if e < i)
+        ctarget.append(p if i in pe else p - 1)
+    _ScriptedDecoder.stream, _ScriptedDecoder.ctarget = stream, ctarget
+    monkeypatch.setattr(loops, "CachedDecoder", _ScriptedDecoder)
+    wl = bltgen.WORKLOADS[0]
+    inp = {"prompt": np.array(g["prompt"]), "prompt_patches": np.array(g["prompt_patches"]),
+           "salt": g["salt"], "latents": None}
+    n_gen, k = len(g["continuation"]), g["k"]
+    run = loops.blt_s(None, wl, inp, n_gen, k, trace=True)
+    assert run.out == g["continuation"]                     # identical to greedy decoding
+    assert run.accept == [r["accept"] for r in g["rounds"]]
+    assert (run.n_dec, run.n_eg) == (g["n_dec"], g["n_eg"])
+    recs = run.passes
+    assert len(recs) == len(g["rounds"]) * (k + 1)
+    for ri, r in enumerate(g["rounds"]):
+        drafts, ver = recs[ri * (k + 1):ri * (k + 1) + k], recs[ri * (k + 1) + k]
+        assert [d["kind"] for d in drafts] == ["draft"] * k and ver["kind"] == "verify"
+        assert [d["start"] for d in drafts] == [r["l"] + j for j in range(k)]
+        assert [d["targets"] for d in drafts] == [[r["draft_target"]]] * k, f"round {ri}"
+        a = r["accept"]
+        assert ver["start"] == r["l"] and ver["targets"][:a + 1] == r["verify_targets"], f"round {ri}"
+        assert (ver["accept"], ver["next"]) == (a, r["next"])
+
+
+def test_blt_s_bookkeeping_matches_greedy_targets_on_the_tiny_model(tiny):
+    """On the real tiny decoder: BLT-S verify rows of the accepted prefix read
+    the same latents the greedy decoder's rows read for those positions."""
+    wl, W, inp = tiny
+    g = loops.greedy(W, wl, inp, 40, trace=True)
+    s = loops.blt_s(W, wl, inp, 40, 4, trace=True)
+    assert s.out == g.out
+    gt = {rec["start"]: rec["targets"][0] for rec in g.passes}
+    checked = 0
+    for rec in s.passes:
+        if rec["kind"] == "verify":
+            for j in range(rec["accept"] + 1):
+                pos = rec["start"] + j
+                if pos in gt:
+                    assert rec["targets"][j] == gt[pos]
+                    checked += 1
+    assert checked > 20
+
+
+# ---------------------------------------------------------------- full layer composition
+def _torch_decoder(W, wl, latents, toks, pos, taus, allow):
+    """Independent composition with torch routines of the BLT decoder layer
+    (pytorch.kr summary, "BLT architecture": the cross-attention residual
+    B_l = D_{l-1} + W_o^c softmax(.) V, then D_l = DecoderTransformerLayer(B_l),
+    pre-norm self-attention then pre-norm FFN); every sublayer active."""
+    t = lambda a: torch.tensor(np.asarray(a), dtype=torch.float64)
+    d, H = wl.d_model, wl.n_heads
+    dh = d // H
+    n = len(toks)
+    h = t(W["embed"])[torch.tensor(toks)]
+    o = t(latents)[torch.tensor(taus)]                       # each row's single latent
+    f = wl.rope_theta ** (-2.0 * torch.arange(dh // 2, dtype=torch.float64) / dh)
+    rot = torch.polar(torch.ones(n, 1, dh // 2, dtype=torch.float64),
+                      t(pos)[:, None, None] * f)
+
+    def rope(x):
+        x = x.view(n, H, dh)
+        zc = torch.complex(x[..., :dh // 2], x[..., dh // 2:]) * rot
+        return torch.cat([zc.real, zc.imag], -1).transpose(0, 1)
+
+    for lw in W["layers"]:
+        # cross-attention: SDPA over the one allowed latent key per row
+        ot = Fnn.linear(o, t(W["w_lat"]))
+        qc = Fnn.linear(h, t(lw["wq_c"])).view(n, H, 1, dh)
+        kc = Fnn.linear(ot, t(lw["wk_c"])).view(n, H, 1, dh)
+        vc = Fnn.linear(ot, t(lw["wv_c"])).view(n, H, 1, dh)
+        c = Fnn.scaled_dot_product_attention(qc, kc, vc).reshape(n, d)
+        h = h + Fnn.linear(c, t(lw["wo_c"]))
+        u = Fnn.rms_norm(h, (d,), weight=t(lw["g_attn"]), eps=wl.rms_eps)
+        qkv = Fnn.linear(u, t(lw["wqkv"]))
+        q, k = rope(qkv[:, :d]), rope(qkv[:, d:2 * d])
+        v = qkv[:, 2 * d:].reshape(n, H, dh).transpose(0, 1)
+        a = Fnn.scaled_dot_product_attention(q, k, v, attn_mask=torch.tensor(allow))
+        h = h + Fnn.linear(a.transpose(0, 1).reshape(n, d), t(lw["wo"]))
+        u = Fnn.rms_norm(h, (d,), weight=t(lw["g_ffn"]), eps=wl.rms_eps)
+        h = h + Fnn.linear(Fnn.silu(Fnn.linear(u, t(lw["w1"]))), t(lw["w2"]))
+    u = Fnn.rms_norm(h, (d,), weight=t(W["g_out"]), eps=wl.rms_eps)
+    return Fnn.linear(u, t(W["w_out"])).numpy()
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_two_layer_forward_every_sublayer_matches_torch_composition(causal):
+    """Two layers with cross-attention, self-attention and FFN all active
+    (random gains, random weights scaled up so every sublayer moves the
+    logits): the oracle's forward equals the torch composition; and each
+    sublayer matters (zeroing its output projection moves the logits), so a
+    reordered or dropped sublayer fails this pin."""
+    wl, W, inp = micro(n_layers=2)
+    for lw in W["layers"]:
+        for key in ("wo_c", "wv_c", "wqkv", "wo", "w1", "w2"):
+            lw[key] = lw[key] * 8.0
+    toks = [5, 200, 17, 256, 31, 256]
+    pos = np.array([7, 8, 9, 10, 11, 12])
+    taus = [1, 1, 2, 3, 3, 3]
+    allow = model.blt_d_mask(3, 3, causal)
+    z = model.forward(W, wl, inp["latents"], toks, pos, [[t] for t in taus], allow)
+    want = _torch_decoder(W, wl, inp["latents"], toks, pos, taus, allow)
+    np.testing.assert_allclose(z, want, rtol=1e-10, atol=1e-11)
+    for key in ("wo_c", "wo", "w2"):
+        zz = model.forward(_zero(W, {key}), wl, inp["latents"], toks, pos, [[t] for t in taus], allow)
+        assert np.abs(zz - z).max() > 1e-3 * np.abs(z).max(), key
