@@ -26,6 +26,7 @@ BLT_UNMASK_THRESHOLD, BLT_UNMASK_ONE_STEP, BLT_UNMASK_ENTROPY = 0, 1, 2
 BLT_BLOCK_BIDIR, BLT_BLOCK_CAUSAL = 0, 1
 BLT_POLICY_GREEDY, BLT_POLICY_BLT_D, BLT_POLICY_BLT_S, BLT_POLICY_BLT_DV = 0, 1, 2, 3
 BLT_PROF_OFF, BLT_PROF_ATTENTION, BLT_PROF_ATTENTION_CAUSAL = 0, 1, 2
+BLT_PROF_GEMV_MFMA, BLT_PROF_GEMV, BLT_PROF_GEMM = 3, 4, 5
 MASK = 256
 VOCAB = 257
 
@@ -323,6 +324,29 @@ def blt_session_result(sess, b, cap):
 
 def blt_session_destroy(sess):
     _check("blt_session_destroy", lib().blt_session_destroy(sess))
+
+
+def decoder_params(n_layers, d_model, d_ffn, d_global, vocab=VOCAB):
+    """Parameters of the local decoder as configured here, the P_dec of the
+    bandwidth proxy: byte embedding and head (vocab x d each), latent
+    projection (d x d_global), per layer the cross-attention q/k/v/o and
+    self-attention q/k/v/o projections (8 d^2), the two FFN matrices (2 d F)
+    and two RMSNorm gains, and the final gain."""
+    d, F, L = d_model, d_ffn, n_layers
+    return 2 * vocab * d + d * d_global + L * (8 * d * d + 2 * d * F + 2 * d) + d
+
+
+def streamed_params(n_layers, d_model, d_ffn, vocab=VOCAB):
+    """Weights one decoder pass reads: per layer W_qkv, W_o, W1, W2, and the
+    byte head (the cross-attention products are applied once per latent)."""
+    d, F, L = d_model, d_ffn, n_layers
+    return L * (4 * d * d + 2 * d * F) + vocab * d
+
+
+def latent_params(n_layers, d_model, d_global):
+    """Weights one blt_latents_put batch reads: W_lat and the stacked
+    per-layer cross products W_o^c W_v^c."""
+    return d_model * d_global + n_layers * d_model * d_model
 
 
 class Decoder:

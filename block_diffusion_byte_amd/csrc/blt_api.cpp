@@ -168,6 +168,39 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
                           p.tokens_dev, c->h, s));
   KVGeom geo{L, g.n_heads, d / g.n_heads, kv_rows(g.max_ctx)};
   c->split.splits = 0;               // no sum left pending by an interrupted pass
+  // A projection, stamped with events when its kernel family is being timed:
+  // the GEMV families count algorithmic bytes (weights, activations read,
+  // outputs written, the residual read by a residual epilogue), the MFMA
+  // GEMM counts flops (2 N K R).
+  const size_t e = bf ? 2 : 4;
+  auto gemm = [&](const GemmArgs &a) -> blt_status {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    const int fam = c->prof_family;
+    if (fam == BLT_PROF_GEMV_MFMA || fam == BLT_PROF_GEMV || fam == BLT_PROF_GEMM) {
+      const GemmKind k = gemm_kind(bf, a);
+      if ((fam == BLT_PROF_GEMV_MFMA && k == GEMM_KIND_GEMV_MFMA) ||
+          (fam == BLT_PROF_GEMV && k == GEMM_KIND_GEMV) || (fam == BLT_PROF_GEMM && k == GEMM_KIND_MFMA)) {
+        double work;
+        if (k == GEMM_KIND_MFMA) {
+          work = 2.0 * a.N * a.K * a.R;
+        } else {
+          const double act = a.pro == PRO_NORM ? 4.0 : (double)e;
+          const double outb = (a.ep == EP_STORE_ACT || a.ep == EP_SILU_ACT) ? (double)e : 4.0;
+          work = (double)a.N * a.K * e + (double)a.R * a.K * act + (double)a.R * a.N * outb +
+                 (a.ep == EP_RESID ? 4.0 * a.R * a.N : 0.0);
+        }
+        blt_status pb = prof_next(c, work, &e0, &e1);
+        if (pb != BLT_OK) return pb;
+      }
+    }
+    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s, e0, e1));
+    return BLT_OK;
+  };
+#define BLT_GEMM_TRY(a)                 \
+  do {                                  \
+    const blt_status _g = gemm(a);      \
+    if (_g != BLT_OK) return _g;        \
+  } while (0)
   for (int l = 0; l < L; ++l) {
     const blt_layer_weights &lw = c->layers[l];
     GemmArgs a = base_args(c);
@@ -182,9 +215,9 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     if (gemv_path(bf, R) || geo.d_head <= 64) {
       a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
       a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = kv_rows(g.max_ctx); a.layer = l;
-      HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+      BLT_GEMM_TRY(a);
     } else {
-      HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+      BLT_GEMM_TRY(a);
       HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
     }
     hipEvent_t e0 = nullptr, e1 = nullptr;
@@ -202,27 +235,28 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     a.W = lw.wo; a.N = d; a.K = d;
     a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
     a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
-    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+    BLT_GEMM_TRY(a);
     // f = SiLU(W1 RMSNorm(h))
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.w1; a.N = F; a.K = d;
     a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_ffn;
     a.ep = EP_SILU_ACT; a.out_act = c->xa; a.ldo = F;
-    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+    BLT_GEMM_TRY(a);
     // h += W2 f (+ the next layer's cross-attention contribution)
     a = base_args(c); a.R = R; a.rows = c->rows_d;
     a.W = lw.w2; a.N = d; a.K = F;
     a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = F;
     a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
     if (l + 1 < L) { a.cross = cross; a.cross_layer = l + 1; }
-    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+    BLT_GEMM_TRY(a);
   }
   GemmArgs a = base_args(c);
   a.R = R; a.rows = c->rows_d;
   a.W = c->w.w_out; a.N = kVocab; a.K = d;
   a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
-  HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s));
+  BLT_GEMM_TRY(a);
+#undef BLT_GEMM_TRY
   if (c->split.splits) return fail(c, BLT_EHIP, "enqueue_pass: a split residual sum was left pending");
   const int rep_ent = p.unmask && p.mode == BLT_UNMASK_ENTROPY;
   if (p.unmask && !p.sample) {
@@ -725,7 +759,7 @@ blt_status blt_verify_sample(blt_ctx *c, int32_t batch, const int32_t *slot, int
 
 blt_status blt_profile_enable(blt_ctx *c, int32_t family) {
   if (!c) return BLT_EINVAL;
-  if (family != BLT_PROF_OFF && family != BLT_PROF_ATTENTION && family != BLT_PROF_ATTENTION_CAUSAL)
+  if (family < BLT_PROF_OFF || family > BLT_PROF_GEMM)
     return fail(c, BLT_EINVAL, "blt_profile_enable: unknown kernel family");
   if (family != BLT_PROF_OFF && c->prof_pool.empty()) {
     c->prof_pool.resize(4096);

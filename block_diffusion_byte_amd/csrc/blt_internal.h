@@ -128,7 +128,12 @@ struct SplitResid {
 // sr (nullable) allows residual products to split K and carries a pending
 // sum to the RMSNorm prologue that must take it; xnorm_ws holds the
 // normalised activations of the MFMA path.
-hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr, hipStream_t s);
+// ev0/ev1 (nullable): stamped by the dispatch of the product kernel itself
+// (not of the RMSNorm launch that precedes an MFMA GEMM with a norm prologue).
+hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr, hipStream_t s,
+                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+enum GemmKind { GEMM_KIND_GEMV_MFMA = 0, GEMM_KIND_GEMV = 1, GEMM_KIND_MFMA = 2 };
+GemmKind gemm_kind(bool bf16, const GemmArgs &a);
 hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
                         int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
                         const int32_t *tokens_dev, float *h, hipStream_t s);

@@ -1994,7 +1994,7 @@ __global__ void k_verify(int batch, const SeqDesc *seqs, int r, const int32_t *d
 }
 
 template <bool BF, int G, int NC, int RB, int PRO>
-hipError_t gemv_launch(const GemmArgs &a, hipStream_t s) {
+hipError_t gemv_launch(const GemmArgs &a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   constexpr int KC = 4 * NC * G;
   if (a.K != KC * Act<BF>::EPC) return hipErrorInvalidValue;
   const size_t lds = (size_t)RB * KC * 16;
@@ -2011,7 +2011,8 @@ hipError_t gemv_launch(const GemmArgs &a, hipStream_t s) {
     attr = true;
   }
   constexpr int RPW = 64 / G;
-  hipLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO>), dim3((a.N + RPW - 1) / RPW), dim3(256), lds, s, a);
+  hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO>), dim3((a.N + RPW - 1) / RPW), dim3(256), lds, s,
+                        ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
@@ -2022,27 +2023,27 @@ template <bool BF> int gemv_lanes(const GemmArgs &a) {
 }
 
 template <bool BF, int G, int NC>
-hipError_t gemv_rows(const GemmArgs &a, hipStream_t s) {
+hipError_t gemv_rows(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   // rows per block: 4, 8 or 16, the smallest that holds the pass (more rows
   // loop over blocks of 16); narrow-K matrices only, so the 16-row staging
   // fits the register budget
   constexpr bool wide16 = NC <= 8;
   if (a.pro == PRO_NORM) {
-    if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_NORM>(a, s);
-    if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_NORM>(a, s);
-    return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_NORM>(a, s);
+    if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_NORM>(a, s, e0, e1);
+    if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_NORM>(a, s, e0, e1);
+    return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_NORM>(a, s, e0, e1);
   }
-  if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_PLAIN>(a, s);
-  if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_PLAIN>(a, s);
-  return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_PLAIN>(a, s);
+  if (a.R <= 4) return gemv_launch<BF, G, NC, 4, PRO_PLAIN>(a, s, e0, e1);
+  if (a.R <= 8 || !wide16) return gemv_launch<BF, G, NC, 8, PRO_PLAIN>(a, s, e0, e1);
+  return gemv_launch<BF, G, NC, wide16 ? 16 : 8, PRO_PLAIN>(a, s, e0, e1);
 }
 
 template <bool BF>
-hipError_t gemv_dispatch(const GemmArgs &a, hipStream_t s) {
+hipError_t gemv_dispatch(const GemmArgs &a, hipStream_t s, hipEvent_t e0, hipEvent_t e1) {
   constexpr int EPC = Act<BF>::EPC;
   const int G = gemv_lanes<BF>(a), NC = a.K / (EPC * G * 4);
 #define BLT_GEMV_CASE(g, nc) \
-  if (G == g && NC == nc) return gemv_rows<BF, g, nc>(a, s);
+  if (G == g && NC == nc) return gemv_rows<BF, g, nc>(a, s, e0, e1);
   BLT_GEMV_CASE(8, 1) BLT_GEMV_CASE(8, 2) BLT_GEMV_CASE(8, 3) BLT_GEMV_CASE(8, 4)
   BLT_GEMV_CASE(8, 6) BLT_GEMV_CASE(8, 8) BLT_GEMV_CASE(8, 12) BLT_GEMV_CASE(8, 16)
   BLT_GEMV_CASE(16, 1) BLT_GEMV_CASE(16, 2) BLT_GEMV_CASE(16, 3) BLT_GEMV_CASE(16, 4)
@@ -2076,8 +2077,16 @@ static int resid_splits(const GemmArgs &a, int tiles, size_t cap) {
   return best;
 }
 
+// Which kernel launch_gemm runs for these arguments (the choice depends on
+// the matrix and, for the MFMA GEMM, on the row count only).
+GemmKind gemm_kind(bool bf16, const GemmArgs &a) {
+  if (!bf16 || a.R < kGemvRows)
+    return (bf16 && a.K <= 1536 && a.K % 128 == 0 && a.N >= 2048) ? GEMM_KIND_GEMV_MFMA : GEMM_KIND_GEMV;
+  return GEMM_KIND_MFMA;
+}
+
 hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
   if (a.R <= 0) return hipSuccess;
   const bool pending = sr && sr->splits > 0;
   // a pending sum is taken only by the RMSNorm prologue over its residual,
@@ -2097,8 +2106,9 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
       const int steps = a.K / 128;
       const dim3 g((a.N + 15) / 16);
 #define BLT_GEMV_MFMA(SB)                                                                        \
-  if (a.pro == PRO_NORM) hipLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB>), g, dim3(256), 0, s, a); \
-  else hipLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB>), g, dim3(256), 0, s, a);
+  if (a.pro == PRO_NORM)                                                                         \
+    hipExtLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB>), g, dim3(256), 0, s, ev0, ev1, 0, a);      \
+  else hipExtLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB>), g, dim3(256), 0, s, ev0, ev1, 0, a);
       if (steps % 8 == 0) { BLT_GEMV_MFMA(8) }
       else if (steps % 4 == 0) { BLT_GEMV_MFMA(4) }
       else if (steps % 2 == 0) { BLT_GEMV_MFMA(2) }
@@ -2106,7 +2116,7 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
 #undef BLT_GEMV_MFMA
       return hipGetLastError();
     }
-    return bf16 ? gemv_dispatch<true>(a, s) : gemv_dispatch<false>(a, s);
+    return bf16 ? gemv_dispatch<true>(a, s, ev0, ev1) : gemv_dispatch<false>(a, s, ev0, ev1);
   }
   GemmArgs b = a;
   if (a.pro == PRO_NORM) {
@@ -2149,11 +2159,11 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
   const int t128 = ((a.R + 127) / 128) * ((a.N + 127) / 128);
   const int t64w = ((a.R + 63) / 64) * ((a.N + 127) / 128);
   if (t128 * splits >= 176)
-    hipLaunchKernelGGL((k_gemm_mfma<128, 128, 2, 4, 1>), dim3(t128, splits), dim3(512), 0, s, b);
+    hipExtLaunchKernelGGL((k_gemm_mfma<128, 128, 2, 4, 1>), dim3(t128, splits), dim3(512), 0, s, ev0, ev1, 0, b);
   else if (t64w * splits >= 150)
-    hipLaunchKernelGGL((k_gemm_mfma<64, 128, 2, 4, 1>), dim3(t64w, splits), dim3(512), 0, s, b);
+    hipExtLaunchKernelGGL((k_gemm_mfma<64, 128, 2, 4, 1>), dim3(t64w, splits), dim3(512), 0, s, ev0, ev1, 0, b);
   else
-    hipLaunchKernelGGL((k_gemm_mfma<64, 64, 2, 2, 2>), dim3(t64, splits), dim3(512), 0, s, b);
+    hipExtLaunchKernelGGL((k_gemm_mfma<64, 64, 2, 2, 2>), dim3(t64, splits), dim3(512), 0, s, ev0, ev1, 0, b);
   return hipGetLastError();
 }
 

@@ -277,10 +277,25 @@ blt_status blt_verify_sample(blt_ctx *ctx, int32_t batch, const int32_t *slot, i
  *    count of the sequence's rows);
  *  - BLT_PROF_ATTENTION_CAUSAL, the causal (flash) self-attention kernel of
  *    long clean-row passes (prefill): floating-point operations, sum over its
- *    rows of 4 * d_model * kend (the multiply-adds of QK^T and PV).
- * reset != 0 clears the totals.  Enabling or disabling collects pending
- * events first. */
-typedef enum { BLT_PROF_OFF = 0, BLT_PROF_ATTENTION = 1, BLT_PROF_ATTENTION_CAUSAL = 2 } blt_prof_family;
+ *    rows of 4 * d_model * kend (the multiply-adds of QK^T and PV);
+ *  - BLT_PROF_GEMV_MFMA / BLT_PROF_GEMV, the projections of passes of fewer
+ *    than 16 rows on the MFMA GEMV (bfloat16, K <= 1536, N >= 2048: QKV, W1)
+ *    and on the dot-product GEMV (the others): bytes, N*K weights + R*K
+ *    activations (float32 when the RMSNorm prologue reads the residual) +
+ *    R*N outputs (+ R*N float32 residual reads of a residual epilogue), in the
+ *    context's element size;
+ *  - BLT_PROF_GEMM, the MFMA GEMM of passes of 16 or more rows: floating-point
+ *    operations, 2*N*K*R.
+ * Only decoder passes are timed (not blt_latents_put).  reset != 0 clears
+ * the totals.  Enabling or disabling collects pending events first. */
+typedef enum {
+  BLT_PROF_OFF = 0,
+  BLT_PROF_ATTENTION = 1,
+  BLT_PROF_ATTENTION_CAUSAL = 2,
+  BLT_PROF_GEMV_MFMA = 3,
+  BLT_PROF_GEMV = 4,
+  BLT_PROF_GEMM = 5
+} blt_prof_family;
 blt_status blt_profile_enable(blt_ctx *ctx, int32_t family);
 blt_status blt_profile_read(blt_ctx *ctx, uint64_t *launches, double *total_ms, double *bytes,
                             int32_t reset);
