@@ -35,7 +35,7 @@ EXPORTS = [
     "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_verify_sample", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
     "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
-    "blt_attention_chunks",
+    "blt_attention_chunks", "blt_kv_append_noalloc",
 ]
 
 
@@ -188,9 +188,12 @@ def _sampling(sampling, draw):
 
 def blt_kv_append(ctx, state, slot, start_pos, n_rows, n_max, lat_idx, bytes_=None,
                   tokens_dev=None, argmax_out=None, conf_out=None, logits_out=None, sampling=None,
-                  draw=None):
+                  draw=None, noalloc=False):
     """sampling: None (greedy) or (temperature, top_p, seed); draw: one draw
-    index per sequence (required with sampling)."""
+    index per sequence (required with sampling).  noalloc: call
+    blt_kv_append_noalloc (the pass works in the library's static scratch
+    array; at most 15 rows)."""
+    fn = "blt_kv_append_noalloc" if noalloc else "blt_kv_append"
     keep, smpp, drp = _sampling(sampling, draw)
     s, sp = _i32(slot)
     st, stp = _i32(start_pos)
@@ -200,7 +203,7 @@ def blt_kv_append(ctx, state, slot, start_pos, n_rows, n_max, lat_idx, bytes_=No
     bp = None
     if bytes_ is not None:
         b, bp = _u8(np.asarray(bytes_).reshape(-1))
-    _check("blt_kv_append", lib().blt_kv_append(
+    _check(fn, getattr(lib(), fn)(
         ctx, C.byref(state), len(s), sp, stp, np_, n_max, bp, _ptr(tokens_dev), lip,
         _ptr(argmax_out), _ptr(conf_out), _ptr(logits_out), smpp, drp), ctx)
 

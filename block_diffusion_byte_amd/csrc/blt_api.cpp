@@ -50,6 +50,12 @@ blt_status fail(blt_ctx *c, blt_status st, const std::string &m) {
   return st;
 }
 
+// Message without a temporary string: c->err keeps its reserved capacity.
+blt_status fail(blt_ctx *c, blt_status st, const char *m) {
+  if (c) c->err.assign(m);
+  return st;
+}
+
 blt_status hip_fail(blt_ctx *c, hipError_t e, const char *where) {
   if (c) c->err = std::string(where) + ": " + hipGetErrorString(e);
   return BLT_EHIP;
@@ -75,7 +81,8 @@ namespace blt {
 // carries the sequences and the rows.  Slots rotate; a slot is reused only
 // after its previous copy ended.
 blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
-                      const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs) {
+                      const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs,
+                      const PassWs *dst) {
   StageSlot &sl = c->ring[c->ring_next];
   c->ring_next = (c->ring_next + 1) % kRing;
   if (sl.pending) {
@@ -88,7 +95,12 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
   if (sb) memcpy(p, seqs.data(), sb);
   if (rb) memcpy(p + c->row_off, rows.data(), rb);
   if (ob) memcpy(p + c->off_off, offs->data(), ob);
-  if (rb)
+  if (dst) {
+    // another workspace's descriptor buffers: sequences and rows apart
+    if (ob) return fail(c, BLT_EINVAL, "stage_pass: offsets go to the context's buffer only");
+    if (sb) HIP_TRY(c, hipMemcpyAsync(dst->seqs, p, sb, hipMemcpyHostToDevice, c->stream));
+    if (rb) HIP_TRY(c, hipMemcpyAsync(dst->rows, p + c->row_off, rb, hipMemcpyHostToDevice, c->stream));
+  } else if (rb)
     HIP_TRY(c, hipMemcpyAsync(c->desc_d, p, c->row_off + rb, hipMemcpyHostToDevice, c->stream));
   else if (sb)
     HIP_TRY(c, hipMemcpyAsync(c->desc_d, p, sb, hipMemcpyHostToDevice, c->stream));
@@ -158,14 +170,14 @@ struct PassLaunch {
 };
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
-blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
+blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const PassWs &w) {
   const blt_config &g = c->cfg;
   const int R = p.R, S = p.S, d = g.d_model, F = g.d_ffn, L = g.n_layers;
   const bool bf = c->bf16;
   const blt_state *st = p.st;
   const float *cross = (const float *)st->cross;
-  HIP_TRY(c, launch_embed(bf, c->w.embed, cross, c->rows_d, R, d, L, g.max_latents, p.block_tok,
-                          p.tokens_dev, c->h, s));
+  HIP_TRY(c, launch_embed(bf, c->w.embed, cross, w.rows, R, d, L, g.max_latents, p.block_tok,
+                          p.tokens_dev, w.h, s));
   KVGeom geo{L, g.n_heads, d / g.n_heads, kv_rows(g.max_ctx)};
   c->split.splits = 0;               // no sum left pending by an interrupted pass
   // A projection, stamped with events when its kernel family is being timed:
@@ -193,7 +205,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
         if (pb != BLT_OK) return pb;
       }
     }
-    HIP_TRY(c, launch_gemm(bf, a, c->xb, &c->split, s, e0, e1));
+    HIP_TRY(c, launch_gemm(bf, a, w.xb, &c->split, s, e0, e1));
     return BLT_OK;
   };
 #define BLT_GEMM_TRY(a)                 \
@@ -205,20 +217,20 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
     const blt_layer_weights &lw = c->layers[l];
     GemmArgs a = base_args(c);
     a.R = R;
-    a.rows = c->rows_d;
+    a.rows = w.rows;
     // q, k, v = W_qkv RMSNorm(h)
     a.W = lw.wqkv; a.N = 3 * d; a.K = d;
-    a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_attn;
-    a.ep = EP_STORE_F32; a.out_f32 = c->qkv; a.ldo = 3 * d;
+    a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = lw.g_attn;
+    a.ep = EP_STORE_F32; a.out_f32 = w.qkv; a.ldo = 3 * d;
     // RoPE and the KV write happen in the projection's epilogue (on the
     // MFMA path when a 64-column tile holds whole heads)
     if (gemv_path(bf, R) || geo.d_head <= 64) {
-      a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = c->q; a.kv = st->kv;
+      a.qkv_rope = 1; a.rope_tab = c->rope_tab; a.q_out = w.q; a.kv = st->kv;
       a.n_heads = g.n_heads; a.d_head = d / g.n_heads; a.max_ctx = kv_rows(g.max_ctx); a.layer = l;
       BLT_GEMM_TRY(a);
     } else {
       BLT_GEMM_TRY(a);
-      HIP_TRY(c, launch_rope_kv(bf, c->qkv, R, c->rows_d, c->rope_tab, c->q, st->kv, geo, l, s));
+      HIP_TRY(c, launch_rope_kv(bf, w.qkv, R, w.rows, c->rope_tab, w.q, st->kv, geo, l, s));
     }
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool ev_flash = c->prof_family == BLT_PROF_ATTENTION_CAUSAL;
@@ -227,48 +239,48 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s) {
       blt_status pb = prof_next(c, ev_flash ? p.flash_flops : p.split_bytes, &e0, &e1);
       if (pb != BLT_OK) return pb;
     }
-    HIP_TRY(c, launch_attention(bf, c->q, st->kv, geo, l, c->seqs_d, S, p.seq1, p.grid_chunks,
+    HIP_TRY(c, launch_attention(bf, w.q, st->kv, geo, l, w.seqs, S, p.seq1, p.grid_chunks,
                                 p.attn_sub, p.attn_wg, c->max_chunks,
-                                p.flash_tiles, c->rows_d, R, c->part, c->xa, e0, e1, ev_flash, s));
+                                p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s));
     // h += W_o a
-    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.wo; a.N = d; a.K = d;
-    a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = d;
-    a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
+    a.pro = PRO_PLAIN; a.X = w.xa; a.ldx = d;
+    a.ep = EP_RESID; a.resid = w.h; a.ldo = d;
     BLT_GEMM_TRY(a);
     // f = SiLU(W1 RMSNorm(h))
-    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.w1; a.N = F; a.K = d;
-    a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = lw.g_ffn;
-    a.ep = EP_SILU_ACT; a.out_act = c->xa; a.ldo = F;
+    a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = lw.g_ffn;
+    a.ep = EP_SILU_ACT; a.out_act = w.xa; a.ldo = F;
     BLT_GEMM_TRY(a);
     // h += W2 f (+ the next layer's cross-attention contribution)
-    a = base_args(c); a.R = R; a.rows = c->rows_d;
+    a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.w2; a.N = d; a.K = F;
-    a.pro = PRO_PLAIN; a.X = c->xa; a.ldx = F;
-    a.ep = EP_RESID; a.resid = c->h; a.ldo = d;
+    a.pro = PRO_PLAIN; a.X = w.xa; a.ldx = F;
+    a.ep = EP_RESID; a.resid = w.h; a.ldo = d;
     if (l + 1 < L) { a.cross = cross; a.cross_layer = l + 1; }
     BLT_GEMM_TRY(a);
   }
   GemmArgs a = base_args(c);
-  a.R = R; a.rows = c->rows_d;
+  a.R = R; a.rows = w.rows;
   a.W = c->w.w_out; a.N = kVocab; a.K = d;
-  a.pro = PRO_NORM; a.H = c->h; a.ldh = d; a.gain = c->w.g_out;
-  a.ep = EP_STORE_F32; a.out_f32 = c->logits; a.ldo = kVocab;
+  a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = c->w.g_out;
+  a.ep = EP_STORE_F32; a.out_f32 = w.logits; a.ldo = kVocab;
   BLT_GEMM_TRY(a);
 #undef BLT_GEMM_TRY
   if (c->split.splits) return fail(c, BLT_EHIP, "enqueue_pass: a split residual sum was left pending");
   const int rep_ent = p.unmask && p.mode == BLT_UNMASK_ENTROPY;
   if (p.unmask && !p.sample) {
-    HIP_TRY(c, launch_decide_unmask(c->logits, S, c->seqs_d, c->rows_d, c->argmax_ws, c->conf_ws,
-                                    c->ent_ws, rep_ent, p.argmax_out, p.conf_out, p.logits_out,
+    HIP_TRY(c, launch_decide_unmask(w.logits, S, w.seqs, w.rows, w.argmax, w.conf,
+                                    w.ent, rep_ent, p.argmax_out, p.conf_out, p.logits_out,
                                     (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
     return BLT_OK;
   }
-  HIP_TRY(c, launch_decide(c->logits, R, c->rows_d, c->argmax_ws, c->conf_ws, c->ent_ws, rep_ent,
+  HIP_TRY(c, launch_decide(w.logits, R, w.rows, w.argmax, w.conf, w.ent, rep_ent,
                            p.argmax_out, p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s));
   if (p.unmask)
-    HIP_TRY(c, launch_unmask(c->seqs_d, S, c->argmax_ws, c->conf_ws, c->ent_ws,
+    HIP_TRY(c, launch_unmask(w.seqs, S, w.argmax, w.conf, w.ent,
                              (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
   return BLT_OK;
 }
@@ -287,7 +299,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                     std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
-                    float *logits_out, const blt_sampling *smp) {
+                    float *logits_out, const blt_sampling *smp, const PassWs *ws_static) {
   // Attention path per sequence, from its own rows only: a bf16 sequence
   // whose rows in the pass are all clean (no block) and number at least
   // kFlashMinRows takes the causal kernel; every other one the split-K kernel.
@@ -311,7 +323,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
       split_bytes += (double)sd.kmax * 2.0 * d * (c->bf16 ? 2 : 4);
     }
   }
-  blt_status bs = stage_pass(c, rows, seqs, nullptr);
+  blt_status bs = stage_pass(c, rows, seqs, nullptr, ws_static);
   if (bs != BLT_OK) return bs;
   PassLaunch p{(int)rows.size(), (int)seqs.size(), (kmax + kAttnChunk - 1) / kAttnChunk,
                flash_tiles, st, block_tok, tokens_dev, unmask, alpha, mode, masked_left,
@@ -347,10 +359,10 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
     const int wg = std::min(grid_chunks, std::max(1, (512 + units - 1) / units));
     p.attn_sub = (grid_chunks + wg - 1) / wg;
   };
-  if (!c->graphs || c->prof_family != BLT_PROF_OFF) {
+  if (ws_static || !c->graphs || c->prof_family != BLT_PROF_OFF) {
     attn_policy(p.grid_chunks);
     if (seqs.size() == 1) p.seq1 = &seqs[0];
-    return enqueue_pass(c, p, c->stream);
+    return enqueue_pass(c, p, c->stream, ws_static ? *ws_static : c->ws);
   }
   // chunk-grid buckets of 4 keep the number of distinct graphs small; the
   // chunks past a sequence's kmax leave at once
@@ -375,12 +387,12 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
     // first sighting: launch directly (also prepares every kernel's attributes)
     if (c->graph_cache.size() >= kMaxGraphs) drop_graphs(c);
     c->graph_cache.emplace(key, GraphEntry{});
-    return enqueue_pass(c, p, c->stream);
+    return enqueue_pass(c, p, c->stream, c->ws);
   }
   GraphEntry &ge = it->second;
   if (!ge.exec) {
     HIP_TRY(c, hipStreamBeginCapture(c->cap_stream, hipStreamCaptureModeThreadLocal));
-    const blt_status ls = enqueue_pass(c, p, c->cap_stream);
+    const blt_status ls = enqueue_pass(c, p, c->cap_stream, c->ws);
     hipGraph_t graph = nullptr;
     const hipError_t ee = hipStreamEndCapture(c->cap_stream, &graph);
     if (ls != BLT_OK || ee != hipSuccess) {
@@ -468,7 +480,14 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
     c->seqs_d = (SeqDesc *)c->desc_d;
     c->rows_d = (RowDesc *)((char *)c->desc_d + c->row_off);
     c->offs_d = (int64_t *)((char *)c->desc_d + c->off_off);
+    c->ws = PassWs{c->h, c->qkv, c->q, c->part, c->logits, c->conf_ws, c->ent_ws, c->argmax_ws,
+                   c->xa, c->xb, c->seqs_d, c->rows_d};
   }
+  for (auto &wr : c->written) wr.rows.assign(cfg->max_batch, 0);
+  c->rows_tmp.reserve(R);
+  c->seqs_tmp.reserve(cfg->max_batch);
+  c->seen_tmp.reserve(cfg->max_batch);
+  c->err.reserve(512);
   for (int i = 0; i < kRing && he == hipSuccess; ++i) {
     chk(hipHostMalloc(&c->ring[i].host, stage, hipHostMallocDefault));
     chk(hipEventCreateWithFlags(&c->ring[i].ev, hipEventDisableTiming));
@@ -575,11 +594,22 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
 
 static blt_status check_slots(blt_ctx *c, int32_t batch, const int32_t *slot, const char *fn) {
   const blt_config &g = c->cfg;
-  if (batch < 1 || batch > g.max_batch || !slot) return fail(c, BLT_EINVAL, std::string(fn) + ": bad batch or slot array");
-  std::vector<char> seen(g.max_batch, 0);
+  char msg[160];
+  if (batch < 1 || batch > g.max_batch || !slot) {
+    snprintf(msg, sizeof(msg), "%s: bad batch or slot array", fn);
+    return fail(c, BLT_EINVAL, (const char *)msg);
+  }
+  std::vector<char> &seen = c->seen_tmp;   // reserved at creation: no allocation here
+  seen.assign(g.max_batch, 0);
   for (int b = 0; b < batch; ++b) {
-    if (slot[b] < 0 || slot[b] >= g.max_batch) return fail(c, BLT_EINVAL, std::string(fn) + ": slot out of range");
-    if (seen[slot[b]]) return fail(c, BLT_EINVAL, std::string(fn) + ": a slot appears twice in one pass");
+    if (slot[b] < 0 || slot[b] >= g.max_batch) {
+      snprintf(msg, sizeof(msg), "%s: slot out of range", fn);
+      return fail(c, BLT_EINVAL, (const char *)msg);
+    }
+    if (seen[slot[b]]) {
+      snprintf(msg, sizeof(msg), "%s: a slot appears twice in one pass", fn);
+      return fail(c, BLT_EINVAL, (const char *)msg);
+    }
     seen[slot[b]] = 1;
   }
   return BLT_OK;
@@ -598,14 +628,16 @@ static blt_status check_sampling(blt_ctx *c, const blt_sampling *sampling, const
   return BLT_OK;
 }
 
-blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
-                         const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
-                         const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
-                         int32_t *argmax_out, float *conf_out, float *logits_out,
-                         const blt_sampling *sampling, const int32_t *draw) {
+// Rows of one blt_kv_append call; `noalloc` carves the pass workspace out of
+// the static scratch array instead of the context's workspace.
+static blt_status kv_append_impl(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
+                                 const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
+                                 const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
+                                 int32_t *argmax_out, float *conf_out, float *logits_out,
+                                 const blt_sampling *sampling, const int32_t *draw, bool noalloc) {
   if (!c) return BLT_EINVAL;
   const blt_config &g = c->cfg;
-  static const char *fn = "blt_kv_append";
+  const char *fn = noalloc ? "blt_kv_append_noalloc" : "blt_kv_append";
   if (!st || !st->kv || !st->cross) return fail(c, BLT_EINVAL, "blt_kv_append: state is NULL");
   blt_status bs = check_slots(c, batch, slot, fn);
   if (bs != BLT_OK) return bs;
@@ -615,9 +647,12 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
   if (bs != BLT_OK) return bs;
   if (sampling && n_max > kMaxBlock)
     return fail(c, BLT_EINVAL, "blt_kv_append: sampled passes take at most 64 rows per sequence");
-  std::vector<RowDesc> rows;
-  std::vector<SeqDesc> seqs;
+  std::vector<RowDesc> &rows = c->rows_tmp;   // reserved at creation (max_rows, max_batch)
+  std::vector<SeqDesc> &seqs = c->seqs_tmp;
+  rows.clear();
+  seqs.clear();
   int32_t *wr = c->written_rows(st);
+  if (!wr) return fail(c, BLT_ECAPACITY, "blt_kv_append: more decode states than one context tracks (16)");
   for (int b = 0; b < batch; ++b) {
     const int n = n_rows[b], s0 = start_pos[b];
     if (n < 0 || n > n_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_kv_append: bad n_rows or start_pos");
@@ -626,6 +661,8 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
       return fail(c, BLT_EINVAL, "blt_kv_append: start_pos beyond the rows already written for the slot");
     if (n == 0) continue;
     if ((int64_t)rows.size() + n > g.max_rows) return fail(c, BLT_ECAPACITY, "blt_kv_append: more rows than max_rows");
+    if (noalloc && (int64_t)rows.size() + n > kNoAllocRows)
+      return fail(c, BLT_ECAPACITY, "blt_kv_append_noalloc: more than 15 rows in one call");
     SeqDesc sd{slot[b], (int)rows.size(), n, s0 + n, -1, -1, 0, slot[b]};
     for (int j = 0; j < n; ++j) {
       const int li = lat_idx[(size_t)b * n_max + j];
@@ -638,11 +675,52 @@ blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const i
     seqs.push_back(sd);
   }
   if (rows.empty()) return BLT_OK;
+  PassWs sw{};
+  if (noalloc) {
+    // the pass workspace, carved out of the static scratch array in 256-byte
+    // aligned regions for this call's rows
+    const size_t R = rows.size(), d = g.d_model, H = g.n_heads, dh = d / H;
+    const size_t e = c->bf16 ? 2 : 4;
+    size_t off = 0;
+    auto take = [&](size_t bytes_) { const size_t o = off; off = (off + bytes_ + 255) & ~(size_t)255; return o; };
+    const size_t o_seqs = take((size_t)g.max_batch * sizeof(SeqDesc)), o_rows = take(R * sizeof(RowDesc));
+    const size_t o_h = take(R * d * 4), o_qkv = take(R * 3 * d * 4), o_q = take(R * d * 4);
+    const size_t o_part = take(R * H * c->max_chunks * (dh + 2) * 4), o_lg = take(R * kVocab * 4);
+    const size_t o_cf = take(R * 4), o_en = take(R * 4), o_am = take(R * 4);
+    const size_t o_xa = take(R * std::max<size_t>(d, g.d_ffn) * e);
+    const size_t o_xb = take(R * std::max<size_t>(d, g.d_global) * e);
+    if (off > kScratchBytes)
+      return fail(c, BLT_ECAPACITY, "blt_kv_append_noalloc: the pass needs more than the 32 MiB scratch array");
+    void *base = nullptr;
+    HIP_TRY(c, scratch_region(&base));
+    char *b8 = (char *)base;
+    sw = PassWs{(float *)(b8 + o_h), (float *)(b8 + o_qkv), (float *)(b8 + o_q), (float *)(b8 + o_part),
+                (float *)(b8 + o_lg), (float *)(b8 + o_cf), (float *)(b8 + o_en), (int32_t *)(b8 + o_am),
+                b8 + o_xa, b8 + o_xb, (SeqDesc *)(b8 + o_seqs), (RowDesc *)(b8 + o_rows)};
+  }
   bs = run_pass(c, st, rows, seqs, nullptr, tokens_dev, false, 0.f, 0, nullptr, argmax_out,
-                conf_out, logits_out, sampling);
+                conf_out, logits_out, sampling, noalloc ? &sw : nullptr);
   if (bs == BLT_OK)
     for (const SeqDesc &sd : seqs) wr[sd.slot] = rows[sd.row0].pos + sd.nrows;
   return bs;
+}
+
+blt_status blt_kv_append(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
+                         const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
+                         const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
+                         int32_t *argmax_out, float *conf_out, float *logits_out,
+                         const blt_sampling *sampling, const int32_t *draw) {
+  return kv_append_impl(c, st, batch, slot, start_pos, n_rows, n_max, bytes, tokens_dev, lat_idx,
+                        argmax_out, conf_out, logits_out, sampling, draw, false);
+}
+
+blt_status blt_kv_append_noalloc(blt_ctx *c, const blt_state *st, int32_t batch, const int32_t *slot,
+                                 const int32_t *start_pos, const int32_t *n_rows, int32_t n_max,
+                                 const uint8_t *bytes, const int32_t *tokens_dev, const int32_t *lat_idx,
+                                 int32_t *argmax_out, float *conf_out, float *logits_out,
+                                 const blt_sampling *sampling, const int32_t *draw) {
+  return kv_append_impl(c, st, batch, slot, start_pos, n_rows, n_max, bytes, tokens_dev, lat_idx,
+                        argmax_out, conf_out, logits_out, sampling, draw, true);
 }
 
 blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
@@ -675,6 +753,7 @@ blt_status blt_decode_block_step(blt_ctx *c, const blt_state *st, int32_t batch,
   std::vector<RowDesc> rows;
   std::vector<SeqDesc> seqs;
   int32_t *wr = c->written_rows(st);
+  if (!wr) return fail(c, BLT_ECAPACITY, "blt_decode_block_step: more decode states than one context tracks (16)");
   for (int b = 0; b < batch; ++b) {
     const int na = n_append_max > 0 ? n_append[b] : 0, s0 = start_pos[b];
     if (na < 0 || na > n_append_max || s0 < 0) return fail(c, BLT_EINVAL, "blt_decode_block_step: bad n_append or start_pos");

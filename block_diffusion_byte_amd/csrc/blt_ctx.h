@@ -3,6 +3,7 @@
 
 #include <string.h>
 
+#include <algorithm>
 #include <string>
 #include <unordered_map>
 #include <vector>
@@ -47,6 +48,7 @@ struct GraphEntry {
   hipGraphExec_t exec = nullptr;  // instantiated on the second sighting of a key
 };
 constexpr size_t kMaxGraphs = 256;
+constexpr int kMaxStates = 16;   // decode states whose written rows one context tracks
 
 }  // namespace blt
 
@@ -93,23 +95,44 @@ struct blt_ctx {
   double prof_ms = 0, prof_bytes = 0;
   // clean cache rows written so far per (state, slot), keyed by the state's
   // kv buffer: a pass may start at most at that count (rows past it were
-  // never written and would enter the softmax)
-  std::unordered_map<const void *, std::vector<int32_t>> written;
+  // never written and would enter the softmax).  A fixed table sized at
+  // creation, so no call allocates host memory for it.
+  struct Written {
+    const void *kv = nullptr;
+    std::vector<int32_t> rows;   // max_batch entries
+  };
+  Written written[blt::kMaxStates];
+  // nullptr when kMaxStates other states are already tracked
   int32_t *written_rows(const blt_state *st) {
-    std::vector<int32_t> &v = written[st->kv];
-    if (v.empty()) v.assign(cfg.max_batch, 0);
-    return v.data();
+    for (Written &wr : written)
+      if (wr.kv == st->kv) return wr.rows.data();
+    for (Written &wr : written)
+      if (!wr.kv) {
+        wr.kv = st->kv;
+        std::fill(wr.rows.begin(), wr.rows.end(), 0);
+        return wr.rows.data();
+      }
+    return nullptr;
   }
+  // the pass workspace above as one view; host descriptor lists reserved at
+  // creation (max_rows rows, max_batch sequences) for the allocation-free call
+  blt::PassWs ws{};
+  std::vector<blt::RowDesc> rows_tmp;
+  std::vector<blt::SeqDesc> seqs_tmp;
+  std::vector<char> seen_tmp;
 };
 
 namespace blt {
+// dst (nullable): the workspace whose descriptor buffers receive the rows and
+// sequences (default: the context's own descriptor buffer).
 blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
-                      const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs);
+                      const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs,
+                      const PassWs *dst = nullptr);
 blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1);
 blt_status prof_collect(blt_ctx *c);
 blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                     std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,
                     int32_t *masked_left, int32_t *argmax_out, float *conf_out,
-                    float *logits_out, const blt_sampling *smp);
+                    float *logits_out, const blt_sampling *smp, const PassWs *ws_static = nullptr);
 }  // namespace blt

@@ -56,6 +56,23 @@ struct SeqDesc {
   int32_t attn_flash;    // 1: self-attention by the causal kernel (clean rows only, >= kFlashMinRows)
 };
 
+// Device buffers one decoder pass works in (the context's workspace, or the
+// allocation-free entry point's static scratch array).
+struct PassWs {
+  float *h, *qkv, *q, *part, *logits, *conf, *ent;
+  int32_t *argmax;
+  void *xa, *xb;
+  SeqDesc *seqs;
+  RowDesc *rows;
+};
+
+// The allocation-free entry point's scratch: a file-scope device array of
+// kScratchBytes, one copy per GPU.  scratch_region returns its device address
+// on the current device (looked up once per device with hipGetSymbolAddress).
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+constexpr int kNoAllocRows = 15;    // rows per allocation-free call (the GEMV path)
+hipError_t scratch_region(void **ptr);
+
 // EP_PART (MFMA GEMM only): split y's partial product to out_f32[split][R][N]
 enum Epilogue { EP_STORE_F32 = 0, EP_RESID = 1, EP_SILU_ACT = 2, EP_STORE_ACT = 3, EP_ROWOFF_F32 = 4,
                 EP_PART = 5 };

@@ -22,6 +22,8 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <mutex>
+
 #include "blt_internal.h"
 
 namespace blt {
@@ -2334,6 +2336,31 @@ hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *d
   hipLaunchKernelGGL(k_verify, dim3((batch + 63) / 64), dim3(64), 0, s, batch, seqs, r, draft,
                      ld_draft, pred, ld_pred, accept_len, next_byte);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (blt_kv_append_noalloc): one
+// static device array per GPU.  Host code never passes the array's name to a
+// kernel (on the host it is only a stand-in symbol); it asks for the device
+// address, which differs per GPU, once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_region(void **ptr) {
+  static std::mutex mu;
+  static void *addr[64] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = p;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace blt

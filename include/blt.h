@@ -196,6 +196,30 @@ blt_status blt_kv_append(blt_ctx *ctx, const blt_state *st, int32_t batch, const
                          int32_t *argmax_out, float *conf_out, float *logits_out,
                          const blt_sampling *sampling, const int32_t *draw);
 
+/* blt_kv_append for callers that cannot allocate device memory at the time
+ * of the call (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same pass, with the same arguments, results
+ * and validation, but its working buffers (residual stream, queries,
+ * attention partials, activations, logits, decisions and the pass's row and
+ * sequence descriptors) live in one static device array of 32 MiB that the
+ * library holds on each GPU until the process ends, instead of the
+ * context's workspace.  The call allocates nothing (no hipMalloc, hipFree or
+ * allocating library routine) and never captures a graph; the context must
+ * already exist (blt_create allocates).  Limits, checked before anything is
+ * enqueued: at most 15 rows in the call (BLT_ECAPACITY), and the pass's
+ * buffers (about rows x (n_heads x ceil(max_ctx/128) x (d_model/n_heads+2) x
+ * 4 + 7 x d_model x 4 + 257 x 4 + max(d_model, d_ffn, d_global) x 4) bytes)
+ * within the 32 MiB (BLT_ECAPACITY).  Every call on one GPU, from any
+ * context, shares that GPU's array and nothing in it needs to start at zero:
+ * calls that overlap in time on one GPU (different streams or threads) race
+ * and must be serialised by the caller. */
+blt_status blt_kv_append_noalloc(blt_ctx *ctx, const blt_state *st, int32_t batch,
+                                 const int32_t *slot, const int32_t *start_pos,
+                                 const int32_t *n_rows, int32_t n_max, const uint8_t *bytes,
+                                 const int32_t *tokens_dev, const int32_t *lat_idx,
+                                 int32_t *argmax_out, float *conf_out, float *logits_out,
+                                 const blt_sampling *sampling, const int32_t *draw);
+
 /* One BLT-D decoder pass (pytorch.kr summary, "BLT-D inference" and
  * "BLT-D attention mask").  For sequence b: n_append[b] clean rows at
  * start_pos[b].. (tokens append_bytes[b*n_append_max+j], latents
