@@ -3,7 +3,8 @@
 For each full-size workload, the float64 CPU oracle (oracle/) runs the
 workload's decode policy on a few sampled sequences of the batch (seeded
 synthetic inputs from bltgen) just long enough to cover its first round,
-with pass tracing on, and the first passes of that trace are stored:
+with pass tracing on, and the first passes of that trace are stored (into
+the second block or round where the plan says so):
 rows, latent targets, logits, greedy choices, confidences, top-2 gaps and
 the block or acceptance decisions.  Nothing here calls the HIP path.
 
@@ -27,9 +28,10 @@ from oracle import loops, model  # noqa: E402
 
 # workload index -> (sampled sequences, bytes to generate, passes kept)
 PLAN = {
-    1: ([0], 4, 4),        # BLT-D-4, batch 1: the whole first block
+    1: ([0], 8, 5),        # BLT-D-4, batch 1: the first block and the second block's first
+                           # pass (rollback of the last prompt row, the block's bytes appended)
     2: ([0, 15], 16, 2),   # BLT-D-16, batch 16: the first two block passes
-    3: ([0], 1, 9),        # BLT-S k=8, batch 1: 8 draft passes and the verification
+    3: ([0], 10, 18),      # BLT-S k=8, batch 1: two rounds of 8 draft passes and a verification
     4: ([0, 63], 1, 2),    # BLT-DV-8 one-step, batch 64: draft pass and verification
 }
 KINDS = {"block": 0, "draft": 1, "verify": 2, "ar": 3}

@@ -21,8 +21,8 @@ import pytest
 
 import bltgen
 from oracle import patcher
-from tests.gpu_util import (check_block_pass, check_rows_pass, decoder_for, replay_and_compare,
-                            say)
+from tests.gpu_util import (assert_coverage, check_block_pass, check_rows_pass, decoder_for,
+                            replay_and_compare, say)
 
 pytestmark = pytest.mark.gpu
 GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -74,7 +74,7 @@ class FullBatch:
         import block_diffusion_byte_amd as blt
         self.torch, self.blt, self.wl = torch, blt, wl
         self.b, self.B = wl.batch, max(wl.block, 1)
-        self.max_rows = max(1024, wl.batch * (2 * wl.block + 2))      # as bench.py
+        self.max_rows = max(1024, wl.batch * (2 * wl.block + 2), wl.prompt_len)   # as bench.py
         self.dec = decoder_for(wl, bltgen.make_weights(wl), max_batch=self.b, max_rows=self.max_rows)
         dev = "cuda:0"
         inps = [bltgen.make_sequence_inputs(wl, s) for s in range(self.b)]
@@ -87,8 +87,9 @@ class FullBatch:
             self.x.append(x)
             self.seg.append((patch, ends, inp["prompt_patches"], inp["salt"]))
             # latents through a few patches past the prompt's last: verification
-            # rows over a draft may read patches the draft completes
-            m = min(patcher.last_target(patch) + self.B + 1, wl.n_latents - 1)
+            # rows over a draft may read patches the draft completes (two
+            # rounds of up to B + 1 bytes each)
+            m = min(patcher.last_target(patch) + 2 * (self.B + 1) + 1, wl.n_latents - 1)
             slots += [s] * (m + 1)
             idx += list(range(m + 1))
         blt.blt_latents_put(self.dec.ctx, self.dec.state, slots, idx, self.table, wl.n_latents)
@@ -143,6 +144,31 @@ class FullBatch:
         blk = self.block_tok.cpu().numpy().reshape(self.b, B)
         return z, am, cf, blk, self.masked.cpu().numpy()
 
+    def block_pass_rec(self, rec, alpha, one_step):
+        """One BLT-D pass of sequence 0 (batch 1) as the oracle's record has it:
+        its clean rows first (the pending prompt byte, or a rollback and the
+        previous block's bytes), then the block."""
+        blt, torch, B = self.blt, self.torch, self.B
+        assert self.b == 1
+        na = int(rec["n_append"])
+        self.block_tok[:B] = torch.tensor([int(t) for t in rec["block_before"]], dtype=torch.int32)
+        kw = {}
+        if na:
+            kw = dict(n_append=[na], n_append_max=na, append_bytes=[int(t) for t in rec["tokens"][:na]],
+                      append_lat=[int(t) for t in rec["targets"][:na]])
+        blt.blt_decode_block_step(
+            self.dec.ctx, self.dec.state, [0], [int(rec["start"])], self.block_tok, B,
+            [int(rec["targets"][na])], alpha,
+            mode=blt.BLT_UNMASK_ONE_STEP if one_step else blt.BLT_UNMASK_THRESHOLD,
+            mask=blt.BLT_BLOCK_BIDIR, argmax_out=self.argmax, conf_out=self.conf,
+            logits_out=self.logits, masked_left=self.masked, **kw)
+        torch.cuda.synchronize()
+        z = self.logits.view(-1, 257)[:B].cpu().numpy().reshape(1, B, 257)
+        am = self.argmax[:B].cpu().numpy().reshape(1, B)
+        cf = self.conf[:B].cpu().numpy().reshape(1, B)
+        blk = self.block_tok.cpu().numpy().reshape(1, B)
+        return z, am, cf, blk, self.masked.cpu().numpy()
+
     def rows_pass(self, forced, fallback):
         """Clean rows of every sequence in one cache append (draft rows or a
         verification).  forced: {slot: (start, tokens, targets)}; the other
@@ -171,21 +197,24 @@ class FullBatch:
 
 def _summary(name, worst, compared, skipped):
     say(f"{name}: worst logit err {worst:.3g}, {compared} decisions compared, {skipped} near-ties skipped")
-    assert compared > 0
+    assert_coverage(name, compared, skipped)
 
 
 def test_fullsize_bltd4_batch1_first_block():
     """BLT-D-4 at the 1B-class shape, batch 1, 4096-byte prompt: every pass
-    of the first block."""
+    of the first block and the second block's first pass (the last prompt
+    row rolled back to its causal latent and recomputed with the block's
+    committed bytes in front of the new block)."""
     wl = bltgen.WORKLOADS[1]
     gold = _gold(wl)
     fb = FullBatch(wl)
     worst, comp, skip = 0.0, 0, 0
     try:
+        assert len(gold[0]) >= 5 and int(gold[0][4]["n_append"]) > 1      # reaches block 2
         for k in range(len(gold[0])):
             rec = gold[0][k]
             assert int(rec["kind"]) == BLOCK
-            z, am, cf, blk, left = fb.block_pass(k == 0, {0: rec["block_before"]}, wl.alpha, False)
+            z, am, cf, blk, left = fb.block_pass_rec(rec, wl.alpha, False)
             err, c, sk = check_block_pass(k, rec, z[0], am[0], cf[0], blk[0], left[0], wl.alpha, False, "bf16")
             worst, comp, skip = max(worst, err), comp + c, skip + sk
     finally:
@@ -216,12 +245,14 @@ def test_fullsize_bltd16_batch16_first_passes():
 
 def test_fullsize_blts8_batch1_first_round():
     """BLT-S k=8, batch 1: the eight draft passes (stale latents past the
-    patch boundary) and the causal verification pass of the first round."""
+    patch boundary) and the causal verification pass of the first two
+    rounds (the second starts from the accepted bytes and the appended one)."""
     wl = bltgen.WORKLOADS[3]
     gold = _gold(wl)
     fb = FullBatch(wl)
     worst, comp, skip = 0.0, 0, 0
     try:
+        assert len(gold[0]) == 18 and int(gold[0][17]["kind"]) == VERIFY
         for k, rec in enumerate(gold[0]):
             assert int(rec["kind"]) in (DRAFT, VERIFY)
             z, am = fb.rows_pass({0: (rec["start"], rec["tokens"], rec["targets"])}, None)

@@ -13,7 +13,7 @@ import pytest
 
 import bltgen
 from oracle import loops
-from tests.gpu_util import decoder_for, oracle_inputs, replay_and_compare, say
+from tests.gpu_util import assert_coverage, decoder_for, oracle_inputs, replay_and_compare, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,7 +54,7 @@ def _replay(wl, policy, n_gen, gains="random", **kw):
         dec.close()
     say(f"{wl.name} {policy}: {len(run.passes)} passes, worst logit err {worst:.3g}, "
         f"{comp} decisions compared, {skip} near-ties skipped")
-    assert comp > 0
+    assert_coverage(f"{wl.name} {policy}", comp, skip)
     return worst
 
 
@@ -96,6 +96,16 @@ def test_mini_bf16_blt_s_teacher_forced():
 def test_mini_bf16_blt_dv_teacher_forced():
     wl = MINI_BF16.replace(block=8)
     _replay(wl, "blt_dv", 24, B=8, alpha=0.7, one_step=True)
+
+
+def test_mini_bf16_multi_commit_unscaled_head_teacher_forced():
+    """Passes that commit several block positions with the byte head as
+    stated (no scaling), so the logits are held to the plain 2e-2 bf16 bound:
+    the threshold rule at alpha 0.005 (every confidence of this decoder,
+    0.008-0.011, lies above it: four commits per pass) and entropy-bounded
+    unmasking with gamma 12 nats (entropies ~5.5: two of eight per pass)."""
+    _replay(MINI_BF16, "blt_d", 24, B=4, alpha=0.005)
+    _replay(MINI_BF16.replace(block=8), "blt_d", 24, B=8, alpha=12.0, unmask="entropy")
 
 
 def test_tiny_fp32_entropy_bounded_teacher_forced():
