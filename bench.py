@@ -78,6 +78,8 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times (the "
                          "reference kernel for scaling HBM traffic counters) and exit")
+    ap.add_argument("--device-blocks", action="store_true",
+                    help="time BLT-D with device-resident blocks (the host-driven blocks are timed beside them)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every decoder pass directly instead of replaying HIP graphs")
     return ap.parse_args()
@@ -102,9 +104,12 @@ FAMILIES = {
 }
 
 
-def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_report=False):
+def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_report=False,
+            device_blocks=False, compare=False):
     """Time `steps` generations of workload `wl` (after `warmup` untimed ones),
-    then one event-timed generation per kernel family."""
+    then one event-timed generation per kernel family.  device_blocks: BLT-D
+    blocks after the first run on the device (blt_session_device_blocks);
+    compare: also time the same steps with the other way of driving blocks."""
     import bltgen
     dev = "cuda:0"
     w = bltgen.make_weights(wl)
@@ -151,6 +156,8 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
         unmask = {"one_step": blt.BLT_UNMASK_ONE_STEP, "entropy": blt.BLT_UNMASK_ENTROPY}.get(
             wl.unmask, blt.BLT_UNMASK_THRESHOLD)
         pid = policy_id(blt, wl)
+        use_dev = device_blocks and wl.policy == "blt_d"
+        blt.blt_session_device_blocks(dec.ctx, sess, use_dev)
 
         def step():
             blt.blt_session_generate(dec.ctx, sess, pid, wl.block, wl.alpha, wl.n_gen, unmask)
@@ -166,6 +173,21 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
             times.append(time.perf_counter() - t0)
         elapsed = sum(times)
         res = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
+        if compare and wl.policy == "blt_d":
+            # the same steps with the blocks driven the other way
+            blt.blt_session_device_blocks(dec.ctx, sess, not use_dev)
+            step()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            th = (time.perf_counter() - t0) / steps
+            hres = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
+            out["host_driven_blocks" if use_dev else "device_resident_blocks"] = {
+                "value": sum(r["n"] for r in hres) / th, "ms_per_step": 1e3 * th,
+                "same_bytes_and_counts": all(h["out"] == r["out"] and h["n_dec"] == r["n_dec"] and
+                                             h["n_eg"] == r["n_eg"] for h, r in zip(hres, res))}
+            blt.blt_session_device_blocks(dec.ctx, sess, use_dev)
         n_bytes = sum(r["n"] for r in res)
         n_dec = sum(r["n_dec"] for r in res)
         n_eg = sum(r["n_eg"] for r in res)
@@ -234,6 +256,7 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
                                                                      wl.p_enc, wl.p_glob)[1],
                 "proxy_gb_per_seq_pages_params": blt.blt_bw_model(n_dec, n_eg, wl.batch, PAGES_P_DEC,
                                                                    wl.p_enc, wl.p_glob)[1]},
+            "device_blocks": use_dev,
             "config": {"workload": wl.name, "policy": wl.policy, "batch": wl.batch, "block": wl.block,
                        "alpha": wl.alpha, "unmask": wl.unmask, "layers": wl.n_layers,
                        "d_local": wl.d_model, "heads": wl.n_heads, "ffn": wl.d_ffn,
@@ -315,7 +338,8 @@ def main():
     wl = bltgen.WORKLOADS[args.workload]
     small = ["k_attn_mfma", "k_gemv_mfma", "k_gemv"]
     fams = [] if args.no_prof else (small if wl.batch * (wl.block + 1) < 16 else ["k_attn_mfma", "k_gemm_mfma"])
-    main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs, prefill_report=True)
+    main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs, prefill_report=True,
+                       device_blocks=args.device_blocks, compare=True)
     out = {
         "metric": "decoded bytes/sec",
         "value": main_leg["value"],
@@ -333,7 +357,8 @@ def main():
         "data": "synthetic (seeded N(0,0.02) decoder weights, N(0,1) latents, Zipf/uniform byte prompts)",
         "config": main_leg["config"],
     }
-    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill"):
+    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill", "device_blocks",
+              "host_driven_blocks", "device_resident_blocks"):
         if k in main_leg:
             out[k] = main_leg[k]
     if not args.no_legs and args.workload == 1:
@@ -341,7 +366,8 @@ def main():
         legs["batch64"] = run_leg(blt, torch, bltgen.WORKLOADS[4], 1, 1,
                                   [] if args.no_prof else ["k_attn_mfma", "k_gemm_mfma"], args.no_graphs)
         legs["peaked"] = run_leg(blt, torch, wl.replace(head_scale=12.0), max(1, args.steps // 2), 1,
-                                 [] if args.no_prof else ["k_attn_mfma"], args.no_graphs)
+                                 [] if args.no_prof else ["k_attn_mfma"], args.no_graphs,
+                                 device_blocks=args.device_blocks, compare=True)
         out["legs"] = legs
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_bytes, max(1, args.cpu_bytes // 2))

@@ -35,7 +35,7 @@ EXPORTS = [
     "blt_kv_append", "blt_decode_block_step", "blt_verify_accept", "blt_verify_sample", "blt_bw_model",
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
     "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
-    "blt_attention_chunks", "blt_kv_append_noalloc",
+    "blt_attention_chunks", "blt_kv_append_noalloc", "blt_session_device_blocks",
 ]
 
 
@@ -104,6 +104,7 @@ def lib():
             "blt_destroy": [P],
             "blt_latents_put": [P, P, I32, P, P, P, I64],
             "blt_kv_append": [P, P, I32, P, P, P, I32, P, P, P, P, P, P, P, P],
+            "blt_kv_append_noalloc": [P, P, I32, P, P, P, I32, P, P, P, P, P, P, P, P],
             "blt_decode_block_step": [P, P, I32, P, P, P, I32, P, P, P, I32, P, F, I32, I32,
                                       P, P, P, P, P, P],
             "blt_verify_accept": [P, I32, P, I32, P, I32, P, I32, P, P],
@@ -114,6 +115,7 @@ def lib():
             "blt_session_generate": [P, P],
             "blt_session_result": [P, I32, P, I32, P, P, P, P, P],
             "blt_session_destroy": [P],
+            "blt_session_device_blocks": [P, I32],
             "blt_profile_enable": [P, I32],
             "blt_profile_read": [P, P, P, P, I32],
             "blt_graphs_enable": [P, I32],
@@ -313,6 +315,11 @@ def blt_session_generate(ctx, sess, policy, block, alpha, n_gen, unmask=BLT_UNMA
                          block_mask=BLT_BLOCK_BIDIR, temperature=0.0, top_p=1.0, seed=0):
     a = blt_policy_args(policy, block, alpha, unmask, block_mask, n_gen, temperature, top_p, seed)
     _check("blt_session_generate", lib().blt_session_generate(sess, C.byref(a)), ctx)
+
+
+def blt_session_device_blocks(ctx, sess, enable=True):
+    """Run the BLT-D blocks after the first one on the device (see blt.h)."""
+    _check("blt_session_device_blocks", lib().blt_session_device_blocks(sess, 1 if enable else 0), ctx)
 
 
 def blt_session_result(sess, b, cap):

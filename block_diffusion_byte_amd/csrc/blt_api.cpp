@@ -167,7 +167,38 @@ struct PassLaunch {
   int attn_sub = 1;                  // kAttnChunk-key chunks per split-K attention workgroup
   int attn_wg = 1;                   // 2: eight-wave workgroups, one per (sequence, head)
   const SeqDesc *seq1 = nullptr;     // host copy of a one-sequence pass's descriptor (direct launches)
+  int32_t *gate = nullptr;           // device-resident passes: sequences with masks left (0: skip)
+  int32_t *pass_count = nullptr;     // device-resident passes: decoder passes per slot
 };
+
+// Split-K attention: a pass whose chunks number at most 1024 in all takes one
+// chunk per workgroup (small passes need the parallelism).  In larger ones,
+// when sequences times heads reach 256, one eight-wave workgroup per
+// (sequence, head) walks all of its chunks and writes the output (no
+// partials, no merge); below that the workgroups of a (sequence, head) share
+// its chunks evenly, as many as give about 512 in the pass: partials written
+// to memory slow the key stream far beyond their size, so they take many
+// chunks per workgroup.  Sequences of more than 16 split-K rows keep one
+// chunk, held in registers for every 16-row group.  The choice depends on the
+// pass's shape only (measured at the batch-1, batch-16 and batch-64 shapes).
+static void choose_attention(const blt_ctx *c, PassLaunch &p, int grid_chunks, int split_rows) {
+  p.attn_sub = 1;
+  p.attn_wg = 1;
+  if (!c->bf16 || c->cfg.d_model / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return;
+  if (c->attn_chunks) {
+    p.attn_sub = c->attn_chunks;
+    return;
+  }
+  const int units = c->cfg.n_heads * p.S;
+  if ((int64_t)units * grid_chunks <= 1024) return;
+  if (units >= 256) {
+    p.attn_sub = grid_chunks;
+    p.attn_wg = 2;
+    return;
+  }
+  const int wg = std::min(grid_chunks, std::max(1, (512 + units - 1) / units));
+  p.attn_sub = (grid_chunks + wg - 1) / wg;
+}
 
 // The kernel sequence of one decoder pass over the staged rows, on stream s.
 blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const PassWs &w) {
@@ -177,7 +208,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
   const blt_state *st = p.st;
   const float *cross = (const float *)st->cross;
   HIP_TRY(c, launch_embed(bf, c->w.embed, cross, w.rows, R, d, L, g.max_latents, p.block_tok,
-                          p.tokens_dev, w.h, s));
+                          p.tokens_dev, w.h, s, p.gate));
   KVGeom geo{L, g.n_heads, d / g.n_heads, kv_rows(g.max_ctx)};
   c->split.splits = 0;               // no sum left pending by an interrupted pass
   // A projection, stamped with events when its kernel family is being timed:
@@ -205,7 +236,9 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
         if (pb != BLT_OK) return pb;
       }
     }
-    HIP_TRY(c, launch_gemm(bf, a, w.xb, &c->split, s, e0, e1));
+    GemmArgs ag = a;
+    ag.gate = p.gate;
+    HIP_TRY(c, launch_gemm(bf, ag, w.xb, &c->split, s, e0, e1));
     return BLT_OK;
   };
 #define BLT_GEMM_TRY(a)                 \
@@ -230,7 +263,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
       BLT_GEMM_TRY(a);
     } else {
       BLT_GEMM_TRY(a);
-      HIP_TRY(c, launch_rope_kv(bf, w.qkv, R, w.rows, c->rope_tab, w.q, st->kv, geo, l, s));
+      HIP_TRY(c, launch_rope_kv(bf, w.qkv, R, w.rows, c->rope_tab, w.q, st->kv, geo, l, s, p.gate));
     }
     hipEvent_t e0 = nullptr, e1 = nullptr;
     const bool ev_flash = c->prof_family == BLT_PROF_ATTENTION_CAUSAL;
@@ -241,7 +274,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
     }
     HIP_TRY(c, launch_attention(bf, w.q, st->kv, geo, l, w.seqs, S, p.seq1, p.grid_chunks,
                                 p.attn_sub, p.attn_wg, c->max_chunks,
-                                p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s));
+                                p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s, p.gate));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.wo; a.N = d; a.K = d;
@@ -274,14 +307,17 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
   if (p.unmask && !p.sample) {
     HIP_TRY(c, launch_decide_unmask(w.logits, S, w.seqs, w.rows, w.argmax, w.conf,
                                     w.ent, rep_ent, p.argmax_out, p.conf_out, p.logits_out,
-                                    (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
+                                    (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s,
+                                    p.gate, p.pass_count));
     return BLT_OK;
   }
   HIP_TRY(c, launch_decide(w.logits, R, w.rows, w.argmax, w.conf, w.ent, rep_ent,
-                           p.argmax_out, p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s));
+                           p.argmax_out, p.conf_out, p.logits_out, p.sample ? &p.smp : nullptr, s,
+                           p.gate));
   if (p.unmask)
     HIP_TRY(c, launch_unmask(w.seqs, S, w.argmax, w.conf, w.ent,
-                             (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s));
+                             (int32_t *)p.block_tok, p.alpha, p.mode, p.masked_left, s, p.gate,
+                             p.pass_count));
   return BLT_OK;
 }
 
@@ -330,35 +366,7 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                argmax_out, conf_out, logits_out, split_bytes, flash_flops, smp != nullptr,
                SampleArgs{smp ? smp->temperature : 0.f, smp ? smp->top_p : 0.f,
                           smp ? smp->seed : 0}};
-  // Split-K attention: a pass whose chunks number at most 1024 in all takes
-  // one chunk per workgroup (small passes need the parallelism).  In larger
-  // ones, when sequences times heads reach 256, one eight-wave workgroup per
-  // (sequence, head) walks all of its chunks and writes the output (no
-  // partials, no merge); below that the workgroups of a (sequence, head)
-  // share its chunks evenly, as many as give about 512 in the pass: partials
-  // written to memory slow the key stream far beyond their size, so they
-  // take many chunks per workgroup.  Sequences of more than 16 split-K rows
-  // keep one chunk, held in registers for every 16-row group.  The choice
-  // depends on the pass's shape only (measured at the batch-1, batch-16 and
-  // batch-64 shapes).
-  auto attn_policy = [&](int grid_chunks) {
-    p.attn_sub = 1;
-    p.attn_wg = 1;
-    if (!c->bf16 || d / c->cfg.n_heads > 64 || split_rows > 16 || grid_chunks <= 0) return;
-    if (c->attn_chunks) {
-      p.attn_sub = c->attn_chunks;
-      return;
-    }
-    const int units = c->cfg.n_heads * p.S;
-    if ((int64_t)units * grid_chunks <= 1024) return;
-    if (units >= 256) {
-      p.attn_sub = grid_chunks;
-      p.attn_wg = 2;
-      return;
-    }
-    const int wg = std::min(grid_chunks, std::max(1, (512 + units - 1) / units));
-    p.attn_sub = (grid_chunks + wg - 1) / wg;
-  };
+  auto attn_policy = [&](int grid_chunks) { choose_attention(c, p, grid_chunks, split_rows); };
   if (ws_static || !c->graphs || c->prof_family != BLT_PROF_OFF) {
     attn_policy(p.grid_chunks);
     if (seqs.size() == 1) p.seq1 = &seqs[0];
@@ -407,6 +415,48 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
     }
   }
   HIP_TRY(c, hipGraphLaunch(ge.exec, c->stream));
+  return BLT_OK;
+}
+
+// A BLT-D block pass whose descriptors were written on the device (by the
+// block plan kernel): R rows of S sequences, attention over at most
+// grid_chunks chunks, every kernel gated by *gate, decoder passes counted in
+// pass_count.  Nothing is staged from the host and no host copy of a
+// descriptor is handed to a kernel, so the launches can be captured once and
+// replayed.
+blt_status enqueue_device_pass(blt_ctx *c, const blt_state *st, int R, int S, int grid_chunks,
+                               RowDesc *rows, SeqDesc *seqs, int32_t *block_tok, float alpha,
+                               int mode, int32_t *masked_left, int32_t *gate, int32_t *pass_count,
+                               int rows_per_seq, hipStream_t s) {
+  PassLaunch p{R, S, grid_chunks, 0, st, block_tok, nullptr, true, alpha, mode, masked_left,
+               nullptr, nullptr, nullptr, 0.0, 0.0, false, SampleArgs{0.f, 0.f, 0}};
+  p.gate = gate;
+  p.pass_count = pass_count;
+  choose_attention(c, p, grid_chunks, rows_per_seq);
+  PassWs w = c->ws;
+  w.rows = rows;
+  w.seqs = seqs;
+  return enqueue_pass(c, p, s, w);
+}
+
+// The latent projections of m latents whose table rows and cross rows the
+// device wrote into offs[0..m) and offs[m..2m) (an encoder/global pass
+// planned on the device): o~ = W_lat o, then cross = C o~ for every layer.
+blt_status latents_from_device(blt_ctx *c, const blt_state *st, int m, const int64_t *offs,
+                               const void *table, hipStream_t s) {
+  const blt_config &g = c->cfg;
+  if (m > g.max_rows) return fail(c, BLT_ECAPACITY, "latents_from_device: more latents than max_rows");
+  const int d = g.d_model, L = g.n_layers;
+  GemmArgs a = base_args(c);
+  a.R = m; a.W = c->w.w_lat; a.N = d; a.K = g.d_global;
+  a.pro = PRO_PLAIN; a.X = table; a.x_row_off = offs;
+  a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
+  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s));
+  a = base_args(c);
+  a.R = m; a.W = c->cross_w; a.N = L * d; a.K = d;
+  a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
+  a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = offs + m;
+  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s));
   return BLT_OK;
 }
 

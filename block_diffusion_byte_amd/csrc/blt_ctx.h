@@ -130,6 +130,12 @@ blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
                       const PassWs *dst = nullptr);
 blt_status prof_next(blt_ctx *c, double bytes, hipEvent_t *ev0, hipEvent_t *ev1);
 blt_status prof_collect(blt_ctx *c);
+blt_status enqueue_device_pass(blt_ctx *c, const blt_state *st, int R, int S, int grid_chunks,
+                               RowDesc *rows, SeqDesc *seqs, int32_t *block_tok, float alpha,
+                               int mode, int32_t *masked_left, int32_t *gate, int32_t *pass_count,
+                               int rows_per_seq, hipStream_t s);
+blt_status latents_from_device(blt_ctx *c, const blt_state *st, int m, const int64_t *offs,
+                               const void *table, hipStream_t s);
 blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
                     std::vector<SeqDesc> &seqs, const int32_t *block_tok,
                     const int32_t *tokens_dev, bool unmask, float alpha, int mode,

@@ -36,6 +36,8 @@ struct RowDesc {
   int32_t oidx;   // index into the caller's per-row outputs, -1 for none
   int32_t attn_flash;  // 1: its sequence takes the causal kernel (no partials to merge)
   int32_t ctr;    // sampled passes: the row's draw number (block rows), -1: no draw
+  int32_t keep_kv;  // 1: the cache already holds this row's keys and values (a
+                    // recomputation with an unchanged latent): they are not written
 };
 
 // Temperature / top-p sampling of a pass's block rows (temperature > 0).
@@ -109,6 +111,9 @@ struct GemmArgs {
   float *q_out;
   void *kv;
   int n_heads, d_head, max_ctx, layer;   // max_ctx: cache rows, kv_rows(cfg.max_ctx)
+  // device-resident passes: the number of sequences that still have masked
+  // positions; when it reads 0 the kernel returns at once (nullptr: always run)
+  const int32_t *gate;
 };
 
 // Cache rows per sequence and head: max_ctx rounded up to whole attention
@@ -132,6 +137,38 @@ __host__ __device__ inline int64_t v_off(int key, int dim, int d_head) {
   return ((int64_t)(key / kVTile) * d_head + dim) * kVTile + key % kVTile;
 }
 
+// Device-side state of one sequence for device-resident BLT-D blocks: the
+// committed bytes live in a device array next to it, the stand-in patcher
+// runs on the device after each block, and each block's encoder/global pass
+// (the latents it makes available) and first decoder pass are planned there.
+struct DevSeq {
+  int32_t n;           // committed bytes (prompt + generated)
+  int32_t patch_last;  // patch index of byte n-1
+  int32_t cur_len;     // bytes of that patch so far
+  int32_t ends_last;   // a patch boundary follows byte n-1
+  int32_t lat_ready;   // latents 0..lat_ready-1 have cross vectors
+  int32_t err;         // nonzero: a latent index or byte out of range
+  uint64_t salt;
+  int32_t win_patch[kMaxBlock + 1], win_ends[kMaxBlock + 1];   // bytes n-B-1 .. n-1
+};
+
+struct DevBlockArgs {
+  DevSeq *st;                 // [S]
+  int32_t *x;                 // committed bytes, x[b * x_stride + i]
+  int x_stride;
+  int S, B, causal;           // sequences (slots 0..S-1), block size, block mask
+  RowDesc *rows0;             // first pass: B+1 clean rows, then B block rows, per sequence
+  SeqDesc *seqs0;
+  RowDesc *rows1;             // later passes: the B block rows per sequence
+  SeqDesc *seqs1;
+  int64_t *lat_offs;          // [2][S*(B+1)]: latent table rows, cross rows of the latents to make
+  int32_t *block_tok, *masked_left, *gate, *n_eg;
+  int max_latents, n_lat, d_global, n_layers, d_model;
+  int64_t seq_stride;         // latent table rows per sequence
+};
+hipError_t launch_block_plan(const DevBlockArgs &a, hipStream_t s);
+hipError_t launch_block_commit(const DevBlockArgs &a, hipStream_t s);
+
 // Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.
 // A residual product (EP_RESID) on the MFMA path whose K was split: its
 // partial products wait in ws[splits][R][N], and the next RMSNorm prologue
@@ -151,12 +188,14 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
                        hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
 enum GemmKind { GEMM_KIND_GEMV_MFMA = 0, GEMM_KIND_GEMV = 1, GEMM_KIND_MFMA = 2 };
 GemmKind gemm_kind(bool bf16, const GemmArgs &a);
+// gate (nullable, every launcher below): see GemmArgs::gate.
 hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
                         int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
-                        const int32_t *tokens_dev, float *h, hipStream_t s);
+                        const int32_t *tokens_dev, float *h, hipStream_t s,
+                        const int32_t *gate = nullptr);
 hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
-                          hipStream_t s);
+                          hipStream_t s, const int32_t *gate = nullptr);
 // ev0/ev1 (nullable) are stamped by the dispatch of the split-K partials
 // kernel, or of the causal kernel when ev_flash is set.  grid_chunks = 0
 // skips the split-K kernel and its merge (every sequence on the causal
@@ -174,25 +213,31 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
                             int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
-                            hipStream_t s);
+                            hipStream_t s, const int32_t *gate = nullptr);
 bool gemv_supported(bool bf16, int K);
 // report_entropy: conf_out receives each row's entropy instead of its confidence.
 // smp (nullable): rows with ctr >= 0 draw their byte by temperature / top-p
 // sampling; confidence and entropy stay those of the model's distribution.
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
-                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s);
+                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s,
+                         const int32_t *gate = nullptr);
 // mode: a blt_unmask value; alpha: the confidence threshold or the entropy bound.
+// gate (nullable): decremented when a sequence's last [MASK] is committed;
+// pass_count (nullable): pass_count[slot] += 1 for each sequence that still
+// had a [MASK] when the pass began (device-resident decoder pass counter).
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok,
-                         float alpha, int mode, int32_t *masked_left, hipStream_t s);
+                         float alpha, int mode, int32_t *masked_left, hipStream_t s,
+                         int32_t *gate = nullptr, int32_t *pass_count = nullptr);
 // Greedy decisions of every row and the unmasking of every sequence's block
 // in one launch (block passes without sampling): one workgroup per sequence.
 hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *seqs,
                                 const RowDesc *rows, int32_t *argmax_ws, float *conf_ws,
                                 float *ent_ws, int report_entropy, int32_t *argmax_out,
                                 float *conf_out, float *logits_out, int32_t *block_tok,
-                                float alpha, int mode, int32_t *masked_left, hipStream_t s);
+                                float alpha, int mode, int32_t *masked_left, hipStream_t s,
+                                int32_t *gate = nullptr, int32_t *pass_count = nullptr);
 // Rejection-sampling verification: draws[b] = the verify pass's draw index d of
 // sequence b (uniforms d*64 + j and d*64 + r of the stream seed + slot).
 hipError_t launch_verify_sample(int batch, const SeqDesc *seqs, const int64_t *draws, int r,

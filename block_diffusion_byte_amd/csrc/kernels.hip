@@ -197,6 +197,7 @@ __device__ __forceinline__ int qkv_rope_row(const GemmArgs &a, int i) {
 struct QkvEpi {
   int pos, slot;
   float2 cs;
+  int keep_kv;   // the row's keys and values stay as cached
 };
 
 // Column j (within its head half) of the pair whose first output is i0.
@@ -221,6 +222,7 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
     a.q_out[(int64_t)r * a.d + lo + half] = y1 * cs.x + y0 * cs.y;
     return;
   }
+  if (e.keep_kv) return;
   const int64_t plane = (int64_t)a.max_ctx * a.d_head;
   const int64_t head = (((int64_t)e.slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
   T *kv = (T *)a.kv;
@@ -239,7 +241,8 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
 // its outputs: q kept in f32 (RoPE), k (RoPE) and v written to the cache.
 template <bool BF>
 __device__ __forceinline__ void qkv_rope_store_col(const GemmArgs &a, int r, int n, float y0,
-                                                   float y1, int pos, int slot, float2 cs) {
+                                                   float y1, int pos, int slot, float2 cs,
+                                                   int keep_kv) {
   using T = typename Act<BF>::T;
   const int half = a.d_head >> 1, sec = n / a.d, c = n - sec * a.d;
   const int hh = c / a.d_head, j = c - hh * a.d_head;
@@ -248,6 +251,7 @@ __device__ __forceinline__ void qkv_rope_store_col(const GemmArgs &a, int r, int
     a.q_out[(int64_t)r * a.d + c + half] = y1 * cs.x + y0 * cs.y;
     return;
   }
+  if (keep_kv) return;
   const int64_t plane = (int64_t)a.max_ctx * a.d_head;
   const int64_t head = (((int64_t)slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
   T *kv = (T *)a.kv;
@@ -314,6 +318,7 @@ __device__ __forceinline__ uint4 stage_value(const StageRaw<BF, PRO> &st, uint4 
 
 template <bool BF, int G, int NC, int RB, int PRO>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
+  if (a.gate && *a.gate == 0) return;
   constexpr int EPC = Act<BF>::EPC;
   constexpr int RPW = 64 / G;
   constexpr int Q = NC * G, KC = 4 * Q;      // chunks per wave quarter, per row
@@ -355,14 +360,16 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
   // in for unused operands), so no branch forces an early wait.
   const bool need_row = a.qkv_rope || (a.ep == EP_RESID && a.cross);
   const int4 *rowp = need_row ? (const int4 *)(a.rows + erc) : (const int4 *)a.W;
-  const int4 rlo = rowp[0], rhi = rowp[1];        // slot pos tok blk | lat kend oidx pad
+  const int4 rlo = rowp[0], rhi = rowp[1];        // slot pos tok blk | lat kend oidx attn_flash
+  const int2 *rxp = need_row ? (const int2 *)((const int *)(a.rows + erc) + 8) : (const int2 *)a.W;
+  const int2 rx = rxp[0];                         // ctr keep_kv
   const float *resp = a.ep == EP_RESID ? a.resid + (int64_t)erc * a.ldo + eoc : (const float *)a.W;
   ResidEpi re{*resp, 0.f};
 #pragma unroll
   for (int u = 0; u < NC; ++u) wv[u] = wrow[u * G];
   // keep every use of the loaded descriptors below the weight loads
   __builtin_amdgcn_sched_barrier(0);
-  QkvEpi qe{rlo.y, rlo.x, make_float2(1.f, 0.f)};
+  QkvEpi qe{rlo.y, rlo.x, make_float2(1.f, 0.f), a.qkv_rope ? rx.y : 0};
   {
     const int64_t ci = (((int64_t)rlo.x * a.max_lat + rhi.x) * a.n_layers + a.cross_layer) * a.d + eoc;
     const int64_t ti = (int64_t)rlo.y * (a.d_head >> 1) + qkv_pair_j(a, min(ep0, a.N - 2));
@@ -437,6 +444,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
           const RowDesc rd = a.rows[rb + r];
           qe.pos = rd.pos;
           qe.slot = rd.slot;
+          qe.keep_kv = rd.keep_kv;
           qe.cs = a.rope_tab[(int64_t)rd.pos * (a.d_head >> 1) + qkv_pair_j(a, i0)];
         }
         qkv_rope_store<BF>(a, rb + r, i0, y0, y1, qe);
@@ -495,6 +503,7 @@ __device__ __forceinline__ void static_for(F &&f) {
 
 template <int BM, int BN, int WM, int WN, int KH>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
+  if (a.gate && *a.gate == 0) return;
   constexpr int NT = 512, P = 2;                    // threads; register slots of prefetched steps
   constexpr int CH = kGemmBK / 8;                   // 16-byte chunks per tile row
   constexpr int LA = BM * CH / NT, LB = BN * CH / NT;  // chunks per thread per step
@@ -638,7 +647,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
       if (m >= a.R || n >= a.N) continue;
       const RowDesc rd = a.rows[m];
       qkv_rope_store_col<true>(a, m, n, ct[rr * BN + c], ct[rr * BN + c + half], rd.pos, rd.slot,
-                               a.rope_tab[(int64_t)rd.pos * half + (n % a.d_head)]);
+                               a.rope_tab[(int64_t)rd.pos * half + (n % a.d_head)], rd.keep_kv);
     }
     return;
   }
@@ -669,6 +678,7 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 template <bool BF, int SPLITS>
 __global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, const void *gain,
                                                      int K, float eps, void *out, GemmArgs p) {
+  if (p.gate && *p.gate == 0) return;
   using T = typename Act<BF>::T;
   constexpr int E = 8;                       // elements per thread and block
   constexpr int NS = SPLITS > 0 ? SPLITS : 1;
@@ -734,7 +744,9 @@ template <bool BF>
 __global__ __launch_bounds__(256) void k_embed(const void *embed, const float *cross,
                                                const RowDesc *rows, int d, int n_layers,
                                                int max_lat, const int32_t *block_tok,
-                                               const int32_t *tokens_dev, float *h) {
+                                               const int32_t *tokens_dev, float *h,
+                                               const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   const int r = blockIdx.x;
   const RowDesc rd = rows[r];
@@ -753,7 +765,8 @@ __global__ __launch_bounds__(256) void k_embed(const void *embed, const float *c
 template <bool BF>
 __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc *rows,
                                                  const float2 *rope_tab, float *q_out, void *kvp,
-                                                 KVGeom g, int layer) {
+                                                 KVGeom g, int layer, const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   const int r = blockIdx.x;
   const RowDesc rd = rows[r];
@@ -768,6 +781,7 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
     const float q1 = src[lo], q2 = src[hi];
     q_out[(int64_t)r * d + lo] = q1 * cs.x - q2 * cs.y;
     q_out[(int64_t)r * d + hi] = q2 * cs.x + q1 * cs.y;
+    if (rd.keep_kv) continue;
     const float k1 = src[d + lo], k2 = src[d + hi];
     const int64_t kb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + hh) * plane +
                        (int64_t)rd.pos * dh;
@@ -830,6 +844,7 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // 1B-class shapes runs in the time of a plain read of the weights).
 template <int PRO, int SB>
 __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
+  if (a.gate && *a.gate == 0) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l & 15, lq = l >> 4;
   const int n0 = blockIdx.x * 16;
   const int kq = a.K / 4, steps = kq / 32;  // this wave's K range in 32-wide steps (a multiple of SB)
@@ -854,11 +869,12 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
   // rotation's cos/sin right after the first weight loads, so that neither
   // dependent load is waited for after the products
   const int erow = min(t >> 4, a.R - 1);
-  int epos = 0, eslot = 0;
+  int epos = 0, eslot = 0, ekeep = 0;
   float2 ecs = make_float2(1.f, 0.f);
   if (a.qkv_rope) {
     epos = a.rows[erow].pos;
     eslot = a.rows[erow].slot;
+    ekeep = a.rows[erow].keep_kv;
   }
   __builtin_amdgcn_sched_barrier(0);
   __shared__ float red[4][16][17];
@@ -924,7 +940,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
     // outputs (n0+c, n0+c+1), c even: the (j, j + d_h/2) pair of one head
     const int i0 = n0 + c;
     if ((c & 1) || i0 + 1 >= a.N) return;
-    qkv_rope_store<true>(a, r, i0, out(c), out(c + 1), QkvEpi{epos, eslot, ecs});
+    qkv_rope_store<true>(a, r, i0, out(c), out(c + 1), QkvEpi{epos, eslot, ecs, ekeep});
     return;
   }
   const int n = n0 + c;
@@ -962,7 +978,8 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
                                                         const RowDesc *rows, float *part,
                                                         int max_chunks, int chunks_per_wg,
                                                         int direct, void *a_out, SeqDesc sd_arg,
-                                                        int use_sd_arg) {
+                                                        int use_sd_arg, const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
   constexpr int NWV = 4 * WG;                 // waves
   constexpr int KS = DH / 32;                 // k-steps of the score product
@@ -1189,7 +1206,9 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
                                                     int layer, const SeqDesc *seqs,
-                                                    const RowDesc *rows, void *a_out) {
+                                                    const RowDesc *rows, void *a_out,
+                                                    const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   constexpr int KS = DH / 32;                 // k-steps of the score product
   constexpr int DT = DH / 16;                 // 16-dim output tiles
   constexpr int KT = DH <= 64 ? 64 : 32;      // keys per LDS tile
@@ -1418,7 +1437,8 @@ template <int DH>
 __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kvp, KVGeom g,
                                                   int layer, const SeqDesc *seqs,
                                                   const RowDesc *rows, float *part,
-                                                  int max_chunks) {
+                                                  int max_chunks, const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   constexpr int RG = 16;                              // rows per row group
   constexpr int ROWB = DH * 4;                        // bytes of one key row
   constexpr int LDB = ROWB + 16;                      // padded LDS row stride (bytes)
@@ -1589,7 +1609,8 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 template <bool BF, int DH, int PRE>
 __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
                                                    int n_heads, int max_chunks, int gc, int ck,
-                                                   void *a_out) {
+                                                   void *a_out, const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   static_assert(PRE % 32 == 0 || PRE < 32, "later chunks go 32 at a time");
   constexpr int EPL = (DH + 63) / 64;       // output dims per lane
@@ -1705,7 +1726,9 @@ __device__ __forceinline__ void decide_row(int r, const float *logits, const Row
 __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDesc *rows,
                                                int32_t *argmax_ws, float *conf_ws, float *ent_ws,
                                                int report_entropy, int32_t *argmax_out,
-                                               float *conf_out, float *logits_out) {
+                                               float *conf_out, float *logits_out,
+                                               const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   decide_row(blockIdx.x, logits, rows, argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out,
              conf_out, logits_out);
 }
@@ -1749,7 +1772,9 @@ __global__ __launch_bounds__(256) void k_decide_sample(const float *logits, cons
                                                       int32_t *argmax_ws, float *conf_ws,
                                                       float *ent_ws, int report_entropy,
                                                       int32_t *argmax_out, float *conf_out,
-                                                      float *logits_out, SampleArgs smp) {
+                                                      float *logits_out, SampleArgs smp,
+                                                      const int32_t *gate) {
+  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
   __shared__ float ew[256];
   __shared__ float red[4];
   __shared__ float pick_e;
@@ -1822,7 +1847,8 @@ __global__ __launch_bounds__(256) void k_transpose(const T *src, T *dst, int n) 
 __device__ __forceinline__ void unmask_seq(const SeqDesc &sd, const int32_t *argmax_ws,
                                            const float *conf_ws, const float *ent_ws,
                                            int32_t *block_tok, float alpha, int mode,
-                                           int32_t *masked_left) {
+                                           int32_t *masked_left, int32_t *gate,
+                                           int32_t *pass_count) {
   if (sd.nblk <= 0) return;
   const int j = threadIdx.x & 63;
   const bool active = j < sd.nblk;
@@ -1855,14 +1881,24 @@ __device__ __forceinline__ void unmask_seq(const SeqDesc &sd, const int32_t *arg
     }
   }
   if ((cm >> j) & 1ull) block_tok[sd.blk0 + j] = argmax_ws[sd.blk_row0 + j];
-  if (j == 0) masked_left[sd.out_b] = __popcll(mm) - __popcll(cm);
+  const int left = __popcll(mm) - __popcll(cm);
+  if (j == 0) {
+    masked_left[sd.out_b] = left;
+    // device-resident blocks: a pass counts for a sequence that still had a
+    // [MASK]; the gate drops when its last one is committed
+    if (pass_count && mm != 0ull) pass_count[sd.slot] += 1;
+    if (gate && mm != 0ull && left == 0) atomicSub(gate, 1);
+  }
 }
 
 __global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_t *argmax_ws,
                                                const float *conf_ws, const float *ent_ws,
                                                int32_t *block_tok, float alpha, int mode,
-                                               int32_t *masked_left) {
-  unmask_seq(seqs[blockIdx.x], argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left);
+                                               int32_t *masked_left, int32_t *gate,
+                                               int32_t *pass_count) {
+  if (gate && *gate == 0) return;
+  unmask_seq(seqs[blockIdx.x], argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left,
+             gate, pass_count);
 }
 
 // Decisions and unmasking of a block pass in one launch: workgroup b takes
@@ -1874,14 +1910,17 @@ __global__ __launch_bounds__(256) void k_decide_unmask(const float *logits, cons
                                                       int report_entropy, int32_t *argmax_out,
                                                       float *conf_out, float *logits_out,
                                                       int32_t *block_tok, float alpha, int mode,
-                                                      int32_t *masked_left) {
+                                                      int32_t *masked_left, int32_t *gate,
+                                                      int32_t *pass_count) {
+  if (gate && *gate == 0) return;
   const SeqDesc sd = seqs[blockIdx.x];
   const int w = threadIdx.x >> 6;
   for (int r = sd.row0 + w; r < sd.row0 + sd.nrows; r += 4)
     decide_row(r, logits, rows, argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out, conf_out,
                logits_out);
   __syncthreads();                            // the rows' decisions are visible to wave 0
-  if (w == 0) unmask_seq(sd, argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left);
+  if (w == 0) unmask_seq(sd, argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left, gate,
+                         pass_count);
 }
 
 // Probability of byte t (this thread's) under the distribution the top-p
@@ -2171,25 +2210,25 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
 
 hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
                         int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
-                        const int32_t *tokens_dev, float *h, hipStream_t s) {
+                        const int32_t *tokens_dev, float *h, hipStream_t s, const int32_t *gate) {
   if (bf16)
     hipLaunchKernelGGL((k_embed<true>), dim3(R), dim3(256), 0, s, embed, cross, rows, d, n_layers,
-                       max_lat, block_tok, tokens_dev, h);
+                       max_lat, block_tok, tokens_dev, h, gate);
   else
     hipLaunchKernelGGL((k_embed<false>), dim3(R), dim3(256), 0, s, embed, cross, rows, d, n_layers,
-                       max_lat, block_tok, tokens_dev, h);
+                       max_lat, block_tok, tokens_dev, h, gate);
   return hipGetLastError();
 }
 
 hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
-                          hipStream_t s) {
+                          hipStream_t s, const int32_t *gate) {
   if (bf16)
     hipLaunchKernelGGL((k_rope_kv<true>), dim3(R), dim3(256), 0, s, qkv, rows, rope_tab, q_out, kv,
-                       g, layer);
+                       g, layer, gate);
   else
     hipLaunchKernelGGL((k_rope_kv<false>), dim3(R), dim3(256), 0, s, qkv, rows, rope_tab, q_out, kv,
-                       g, layer);
+                       g, layer, gate);
   return hipGetLastError();
 }
 
@@ -2198,16 +2237,16 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                         int n_seq, const SeqDesc *sd_host, int grid_chunks, int nsub, int wg,
                         int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
-                        hipEvent_t ev1, bool ev_flash, hipStream_t s) {
+                        hipEvent_t ev1, bool ev_flash, hipStream_t s, const int32_t *gate) {
   if constexpr (BF) {
     if (flash_tiles > 0) {
       const dim3 fg((flash_tiles + 1) / 2, g.n_heads, n_seq);   // pairs of row tiles
       if (ev0 && ev_flash)
         hipExtLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
-                              seqs, rows, a_out);
+                              seqs, rows, a_out, gate);
       else
         hipLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
-                           a_out);
+                           a_out, gate);
     }
   }
   if (ev_flash) ev0 = ev1 = nullptr;
@@ -2227,10 +2266,11 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   if (ev0)                                                                                        \
     hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, ev0, ev1, 0,   \
                           q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out,     \
-                          sd_arg, use_sd_arg);                                                    \
+                          sd_arg, use_sd_arg, gate);                                              \
   else                                                                                            \
     hipLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, q, kv, g, layer,  \
-                       seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg, use_sd_arg);
+                       seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg, use_sd_arg,     \
+                       gate);
     if constexpr (DH <= 64) {
       if (wg == 2) { BLT_SPLITK(true, 2) }
       else if (nsub > 1) { BLT_SPLITK(true, 1) }
@@ -2242,33 +2282,34 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   } else {
     if (ev0)
       hipExtLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
-                            seqs, rows, part, max_chunks);
+                            seqs, rows, part, max_chunks, gate);
     else
       hipLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
-                         part, max_chunks);
+                         part, max_chunks, gate);
   }
   if (BF && direct) return;                 // no partials to merge
   // the merge takes its first 16 (or 64) chunks in one round of loads
   if (gc <= 16)
     hipLaunchKernelGGL((k_attn_merge<BF, DH, 16>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
-                       g.n_heads, max_chunks, gc, kCK * nsub, a_out);
+                       g.n_heads, max_chunks, gc, kCK * nsub, a_out, gate);
   else
     hipLaunchKernelGGL((k_attn_merge<BF, DH, (DH > 64 ? 32 : 64)>), dim3(R, g.n_heads), dim3(64), 0,
-                       s, part, rows, g.n_heads, max_chunks, gc, kCK * nsub, a_out);
+                       s, part, rows, g.n_heads, max_chunks, gc, kCK * nsub, a_out, gate);
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
                             const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
                             int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
-                            hipStream_t s) {
+                            hipStream_t s, const int32_t *gate) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
   if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,   \
                                   max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1,        \
-                                  ev_flash, s);                                                   \
+                                  ev_flash, s, gate);                                             \
   else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,       \
-                              max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s);
+                              max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s, \
+                              gate);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;
@@ -2281,13 +2322,14 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
 
 hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_t *argmax_ws,
                          float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
-                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s) {
+                         float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s,
+                         const int32_t *gate) {
   if (smp)
     hipLaunchKernelGGL(k_decide_sample, dim3(R), dim3(256), 0, s, logits, rows, argmax_ws, conf_ws,
-                       ent_ws, report_entropy, argmax_out, conf_out, logits_out, *smp);
+                       ent_ws, report_entropy, argmax_out, conf_out, logits_out, *smp, gate);
   else
     hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
-                       report_entropy, argmax_out, conf_out, logits_out);
+                       report_entropy, argmax_out, conf_out, logits_out, gate);
   return hipGetLastError();
 }
 
@@ -2295,10 +2337,11 @@ hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *s
                                 const RowDesc *rows, int32_t *argmax_ws, float *conf_ws,
                                 float *ent_ws, int report_entropy, int32_t *argmax_out,
                                 float *conf_out, float *logits_out, int32_t *block_tok,
-                                float alpha, int mode, int32_t *masked_left, hipStream_t s) {
+                                float alpha, int mode, int32_t *masked_left, hipStream_t s,
+                                int32_t *gate, int32_t *pass_count) {
   hipLaunchKernelGGL(k_decide_unmask, dim3(n_seq), dim3(256), 0, s, logits, seqs, rows, argmax_ws,
                      conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, block_tok,
-                     alpha, mode, masked_left);
+                     alpha, mode, masked_left, gate, pass_count);
   return hipGetLastError();
 }
 
@@ -2324,9 +2367,10 @@ hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStr
 
 hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_ws,
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok, float alpha,
-                         int mode, int32_t *masked_left, hipStream_t s) {
+                         int mode, int32_t *masked_left, hipStream_t s, int32_t *gate,
+                         int32_t *pass_count) {
   hipLaunchKernelGGL(k_unmask, dim3(n_seq), dim3(64), 0, s, seqs, argmax_ws, conf_ws, ent_ws,
-                     block_tok, alpha, mode, masked_left);
+                     block_tok, alpha, mode, masked_left, gate, pass_count);
   return hipGetLastError();
 }
 
@@ -2335,6 +2379,103 @@ hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *d
                          int32_t *next_byte, hipStream_t s) {
   hipLaunchKernelGGL(k_verify, dim3((batch + 63) / 64), dim3(64), 0, s, batch, seqs, r, draft,
                      ld_draft, pred, ld_pred, accept_len, next_byte);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Device-resident BLT-D blocks (pytorch.kr summary, "BLT-D inference": per
+// block one encoder/global pass, then decoder passes until the block is
+// filled; "BLT-D attention mask" for the latent each row reads).  One thread
+// per sequence; sequence b sits in state slot b.
+
+// Plan of a block: its encoder/global pass (latents lat_ready .. M of the
+// last, possibly truncated, patch M; the remaining of the B+1 requests repeat
+// M, which recomputes the same values), the first pass's rows (the last B+1
+// committed bytes as clean rows with their causal latents -- the newest byte
+// reads o_M as the last byte of the truncated patch, the one before it is
+// recomputed with its now final latent -- and the B [MASK] rows reading o_M)
+// and the later passes' rows (the block rows alone).
+__global__ void k_block_plan(DevBlockArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b == 0) *a.gate = a.S;                 // every sequence starts with B masks
+  if (b >= a.S) return;
+  DevSeq &q = a.st[b];
+  const int B = a.B, n = q.n, M = q.patch_last;
+  const int r0 = b * (2 * B + 1);
+  const int32_t *xs = a.x + (int64_t)b * a.x_stride;
+  for (int j = 0; j <= B; ++j) {
+    const int i = n - B - 1 + j;
+    const int tgt = j == B ? M : (q.win_ends[j] ? q.win_patch[j] : q.win_patch[j] - 1);
+    // the oldest of them read its patch's latent as the last prefix byte of
+    // the previous block: unchanged when a boundary follows it, and then its
+    // cached keys and values stay (as a host-driven block leaves them)
+    a.rows0[r0 + j] = RowDesc{b, i, xs[i], 0, tgt, i + 1, -1, 0, -1, j == 0 && q.win_ends[0] ? 1 : 0};
+  }
+  for (int j = 0; j < B; ++j) {
+    const int pos = n + j;
+    const RowDesc rd{b, pos, kTokFromBlock, b * B + j, M, a.causal ? pos + 1 : n + B, b * B + j, 0, -1, 0};
+    a.rows0[r0 + B + 1 + j] = rd;
+    a.rows1[b * B + j] = rd;
+    a.block_tok[b * B + j] = kMask;
+  }
+  a.seqs0[b] = SeqDesc{b, r0, 2 * B + 1, n + B, b * B, r0 + B + 1, B, b, 0};
+  a.seqs1[b] = SeqDesc{b, b * B, B, n + B, b * B, b * B, B, b, 0};
+  a.masked_left[b] = B;
+  const int m0 = q.lat_ready;
+  if (M - m0 + 1 > B + 1) q.err = 2;
+  for (int e = 0; e <= B; ++e) {
+    int idx = min(m0 + e, M);
+    if (idx < 0 || idx >= a.n_lat || idx >= a.max_latents) {
+      q.err = 1;
+      idx = 0;
+    }
+    a.lat_offs[b * (B + 1) + e] = ((int64_t)b * a.seq_stride + idx) * a.d_global;
+    a.lat_offs[(int64_t)a.S * (B + 1) + b * (B + 1) + e] =
+        ((int64_t)b * a.max_latents + idx) * a.n_layers * a.d_model;
+  }
+  q.lat_ready = max(m0, M + 1);
+  a.n_eg[b] += 1;
+}
+
+// Commit of a filled block: its bytes join the sequence and the stand-in
+// patcher decides, byte by byte, where patches end (a new patch starts after
+// byte x_i iff the current one holds 8 bytes or the (1 + 256 x_{i-1} +
+// x_i)-th SplitMix64 output from the sequence's salt is 0 modulo 4).
+__global__ void k_block_commit(DevBlockArgs a) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= a.S) return;
+  DevSeq &q = a.st[b];
+  const int B = a.B;
+  int32_t *xs = a.x + (int64_t)b * a.x_stride;
+  q.win_patch[0] = q.patch_last;
+  q.win_ends[0] = q.ends_last;
+  for (int j = 0; j < B; ++j) {
+    int byte = a.block_tok[b * B + j];
+    if (byte < 0 || byte > 255) {
+      q.err = 3;
+      byte = 0;
+    }
+    const int prev = xs[q.n - 1 + j];
+    const bool fresh = q.ends_last != 0;
+    const int p = q.patch_last + (fresh ? 1 : 0);
+    q.cur_len = fresh ? 1 : q.cur_len + 1;
+    const bool e = q.cur_len >= 8 || (splitmix64_nth(q.salt, 1 + 256ull * prev + byte) & 3ull) == 0;
+    xs[q.n + j] = byte;
+    q.patch_last = p;
+    q.ends_last = e;
+    q.win_patch[j + 1] = p;
+    q.win_ends[j + 1] = e;
+  }
+  q.n += B;
+}
+
+hipError_t launch_block_plan(const DevBlockArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_block_plan, dim3((a.S + 63) / 64), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_commit(const DevBlockArgs &a, hipStream_t s) {
+  hipLaunchKernelGGL(k_block_commit, dim3((a.S + 63) / 64), dim3(64), 0, s, a);
   return hipGetLastError();
 }
 

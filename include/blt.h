@@ -424,6 +424,23 @@ blt_status blt_session_generate(blt_session *s, const blt_policy_args *args);
 blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int32_t cap,
                               int32_t *n_out, uint64_t *n_dec, uint64_t *n_encglob,
                               uint64_t *n_rounds, uint64_t *n_accepted);
+/* Device-resident BLT-D blocks (pytorch.kr summary, "BLT-D inference"):
+ * with enable != 0, a BLT-D generation (greedy, any unmask rule, either block
+ * mask) runs its first block as above and every later block with no host
+ * round trip.  On the device, per block: the stand-in patcher's state and
+ * the committed bytes decide the block's encoder/global pass (the latents of
+ * patches up to the last, possibly truncated, one get their cross vectors;
+ * the pass is counted) and its first decoder pass (the last B+1 committed
+ * bytes as clean rows with their latents, the one before the newest
+ * recomputed with its final latent, then the B [MASK] rows); B decoder
+ * passes follow, each counted for a sequence only while its block still has
+ * a [MASK] (a pass in which no sequence has one does no work); the filled
+ * block is committed and the patcher runs over its bytes.  The block's
+ * launches are captured once as a HIP graph (when graphs are enabled) and
+ * replayed; the bytes and counters are read back at the end.  Results and
+ * counts equal the host-driven path's.  Sampled generation and the other
+ * policies are unaffected.  Default off. */
+blt_status blt_session_device_blocks(blt_session *s, int32_t enable);
 blt_status blt_session_destroy(blt_session *s);
 
 #ifdef __cplusplus

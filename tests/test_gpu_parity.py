@@ -123,7 +123,7 @@ def test_mini_bf16_entropy_bounded_block16_teacher_forced():
 
 # ---------------------------------------------------------------- sessions
 def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_rows=64,
-             graphs=True, repeats=1, between=None):
+             graphs=True, repeats=1, between=None, device=False):
     """Run a native decode session; with repeats > 1 the generation is rerun
     from the same prefill (calling `between` in between) and every run's
     results are returned."""
@@ -137,6 +137,8 @@ def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_row
                                   table, wl.n_latents)
     runs = []
     try:
+        if device:
+            blt.blt_session_device_blocks(dec.ctx, sess, True)
         blt.blt_session_prefill(dec.ctx, sess)
         for k in range(repeats):
             if k and between:
@@ -204,6 +206,58 @@ def test_tiny_fp32_sessions_match_oracle_exactly(policy):
         if r.accept:
             assert g["rounds"] == len(r.accept) and g["accepted"] == sum(r.accept)
     say(f"{policy}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
+
+
+@pytest.mark.parametrize("case", ["threshold", "peaked", "entropy", "one_step", "causal"])
+def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
+    """BLT-D with every block after the first planned, decoded, committed and
+    patched on the device (one captured graph per block, one readback at the
+    end): 3 sequences, bytes and decoder / encoder-global pass counts equal
+    to the oracle's, for the threshold rule (one commit per pass), the peaked
+    head (several commits per pass, so later passes of a block do no work),
+    entropy-bounded and one-step unmasking, and the causal block mask."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    B, alpha, unmask, mode, causal = 4, 0.7, None, blt.BLT_UNMASK_THRESHOLD, False
+    if case in ("peaked", "entropy"):
+        wl = wl.replace(head_scale=12.0)
+    if case == "entropy":
+        B, alpha, unmask, mode = 8, 4.0, "entropy", blt.BLT_UNMASK_ENTROPY
+    if case == "one_step":
+        unmask, mode = "one_step", blt.BLT_UNMASK_ONE_STEP
+    if case == "causal":
+        causal = True
+    w = bltgen.make_weights(wl, gains="random")
+    n_gen = 40
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        refs.append(loops.blt_d(W, wl, inp64, n_gen, B, alpha, block_causal=causal, unmask=unmask))
+    got = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, n_gen, B, alpha, mode,
+                   blt.BLT_BLOCK_CAUSAL if causal else blt.BLT_BLOCK_BIDIR, device=True)
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
+    say(f"device blocks ({case}): 3 x {n_gen} bytes identical to the oracle; n_dec {[g['n_dec'] for g in got]}")
+
+
+@pytest.mark.parametrize("graphs", [True, False])
+def test_bf16_device_blocks_equal_host_blocks(graphs):
+    """bfloat16 decoder, 2 sequences: the device-resident blocks give exactly
+    the bytes and counts of the host-driven blocks (the recomputed prefix row
+    reads the same latent through the same kernels, and a row's result does
+    not depend on the rows beside it)."""
+    import block_diffusion_byte_amd as blt
+    wl = MINI_BF16.replace(head_scale=12.0)
+    w = bltgen.make_weights(wl)
+    inps = [bltgen.make_sequence_inputs(wl, b) for b in range(2)]
+    host = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 4, 0.5, graphs=graphs)
+    dev = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 4, 0.5, graphs=graphs, device=True)
+    for b in range(2):
+        assert dev[b]["out"] == host[b]["out"], f"seq {b}: bytes differ"
+        assert (dev[b]["n_dec"], dev[b]["n_eg"]) == (host[b]["n_dec"], host[b]["n_eg"])
+    say(f"bf16 device blocks (graphs {graphs}) equal host blocks; n_dec {[r['n_dec'] for r in dev]}")
 
 
 def test_tiny_fp32_entropy_bounded_session_exact():
