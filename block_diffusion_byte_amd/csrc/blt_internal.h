@@ -167,6 +167,10 @@ struct DevBlockArgs {
   int64_t seq_stride;         // latent table rows per sequence
 };
 hipError_t launch_block_plan(const DevBlockArgs &a, hipStream_t s);
+// kept[i] = logits[i] (rows of 257) for every block position i = slot*B + j
+// of slots 0..n_slots-1 that was [MASK] in `before` and holds a byte in `after`.
+hipError_t launch_keep_drawn(const int32_t *before, const int32_t *after, const float *logits,
+                             float *kept, int n_slots, int B, hipStream_t s);
 hipError_t launch_block_commit(const DevBlockArgs &a, hipStream_t s);
 
 // Kernel launchers (kernels.hip).  `bf16` selects the bfloat16 instantiations.

@@ -2383,6 +2383,25 @@ hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *d
 }
 
 // ---------------------------------------------------------------------------
+// Draft distributions of sampled BLT-DV blocks: after each pass, a position
+// committed by it (masked before, a byte after) keeps the logits of that
+// pass, the distribution its byte was drawn from.  Block (slot, j) per
+// workgroup; logits and kept rows both at (slot * B + j) * 257.
+__global__ __launch_bounds__(64) void k_keep_drawn(const int32_t *before, const int32_t *after,
+                                                   const float *logits, float *kept, int B) {
+  const int i = blockIdx.x;                  // slot * B + j
+  if (before[i] != kMask || after[i] == kMask) return;
+  for (int v = threadIdx.x; v < kVocab; v += 64) kept[(int64_t)i * kVocab + v] = logits[(int64_t)i * kVocab + v];
+}
+
+hipError_t launch_keep_drawn(const int32_t *before, const int32_t *after, const float *logits,
+                             float *kept, int n_slots, int B, hipStream_t s) {
+  if (n_slots * B <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_keep_drawn, dim3(n_slots * B), dim3(64), 0, s, before, after, logits, kept, B);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Device-resident BLT-D blocks (pytorch.kr summary, "BLT-D inference": per
 // block one encoder/global pass, then decoder passes until the block is
 // filled; "BLT-D attention mask" for the latent each row reads).  One thread

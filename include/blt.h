@@ -392,8 +392,9 @@ typedef struct {
    * sequence's generation (its decoder passes so far) drawing n = d*64 + j.
    * Greedy BLT: each pass draws the next byte.  BLT-D: block positions draw
    * their bytes.  BLT-S: draft bytes are drawn and the draft is verified by
-   * blt_verify_sample (the verify pass is pass d).  BLT-DV: one-step drafts
-   * only (unmask ONE_STEP, else BLT_ENOTIMPL), verified the same way. */
+   * blt_verify_sample (the verify pass is pass d).  BLT-DV: the block draft
+   * (any unmask rule) is verified the same way, each draft byte against the
+   * distribution of the pass that committed it. */
   float temperature;
   float top_p;
   uint64_t seed;

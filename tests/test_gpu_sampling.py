@@ -119,7 +119,7 @@ def test_mini_bf16_sampled_blt_d_entropy_teacher_forced():
     _replay_sampled(wl, "entropy", 3.0, (1.0, 0.8, 77), n_gen=24)
 
 
-def _replay_verify(wl, policy, r, sampling, n_gen=24):
+def _replay_verify(wl, policy, r, sampling, n_gen=24, unmask="one_step", alpha=0.0):
     """Teacher-forced replay of a sampled BLT-S (drafts of r bytes) or
     one-step BLT-DV (blocks of r) oracle trace: draft passes draw on the GPU,
     the verify pass runs the causal rows, then blt_verify_sample decides
@@ -136,7 +136,8 @@ def _replay_verify(wl, policy, r, sampling, n_gen=24):
     if policy == "blt_s":
         run = loops.blt_s(W, wl, inp64, n_gen, r, trace=True, sampling=sampling)
     else:
-        run = loops.blt_dv(W, wl, inp64, n_gen, r, 0.0, one_step=True, trace=True, sampling=sampling)
+        run = loops.blt_dv(W, wl, inp64, n_gen, r, alpha, one_step=unmask == "one_step", unmask=unmask,
+                           trace=True, sampling=sampling)
     dec = decoder_for(wl.replace(block=r), w, max_batch=1, max_rows=256)
     dev = "cuda:0"
     zq_d = torch.zeros((r, 257), dtype=torch.float32, device=dev)
@@ -157,8 +158,13 @@ def _replay_verify(wl, policy, r, sampling, n_gen=24):
                     assert am[0] == rec["choice"][0], f"pass {d}: drew {am[0]}, oracle {rec['choice'][0]}"
                 continue
             if rec["kind"] == "block":
-                z, am, _, after, _ = rp.block(rec, 0.0, "one_step", sampling=sampling, draw=d)
-                zq = [z[j] for j in range(r)]
+                # each position's draft distribution: the logits of the pass that committed it
+                z, am, _, after, _ = rp.block(rec, alpha, unmask, sampling=sampling, draw=d)
+                if not zq:
+                    zq = [None] * r
+                for j in range(r):
+                    if rec["block_before"][j] == decide.MASK and rec["block_after"][j] != decide.MASK:
+                        zq[j] = z[j]
                 continue
             # verify pass: rows l..l+r, then the rejection-sampling decision
             z, _ = rp.rows(rec)
@@ -188,7 +194,7 @@ def _replay_verify(wl, policy, r, sampling, n_gen=24):
             zq = []
     finally:
         dec.close()
-    say(f"sampled {policy} (r={r}, T={temp}, top_p={top_p}): {stats['rounds']} verifications, worst logit "
+    say(f"sampled {policy} {unmask} (r={r}, T={temp}, top_p={top_p}): {stats['rounds']} verifications, worst logit "
         f"err {stats['worst']:.3g}, {stats['vs_rule']} decisions vs the rule on GPU logits, "
         f"{stats['vs_oracle']} vs the oracle's")
     assert stats["vs_rule"] > 0 and stats["vs_oracle"] > 0
@@ -198,6 +204,16 @@ def _replay_verify(wl, policy, r, sampling, n_gen=24):
 def test_tiny_fp32_rejection_sampling_verify_teacher_forced(policy, r):
     wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
     _replay_verify(wl, policy, r, (0.8, 0.9, 4321))
+
+
+@pytest.mark.parametrize("unmask,alpha", [("threshold", 0.3), ("entropy", 3.0)])
+def test_tiny_fp32_sampled_blt_dv_multi_pass_drafts_teacher_forced(unmask, alpha):
+    """Sampled BLT-DV whose block draft takes several passes (threshold or
+    entropy-bounded unmasking): every draft byte is verified against the
+    distribution of the pass that committed it (the oracle's blt_dv with
+    sampling), by blt_verify_sample from the GPU's own logits."""
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    _replay_verify(wl, "blt_dv", 4, (0.8, 0.9, 4321), unmask=unmask, alpha=alpha)
 
 
 def _session(wl, w, inps, n_gen, block, alpha, unmask, temp, top_p, seed, policy=None):
@@ -240,30 +256,61 @@ def test_sampled_sessions_are_seeded_and_reach_the_greedy_limit():
     say(f"sampled sessions: seeded, n_dec {[r['n_dec'] for r in a]}; top_p -> 0 equals greedy")
 
 
-@pytest.mark.parametrize("policy", ["greedy", "blt_s", "blt_dv"])
+@pytest.mark.parametrize("policy", ["greedy", "blt_s", "blt_dv", "blt_dv_threshold", "blt_dv_entropy"])
 def test_sampled_verified_sessions_are_seeded_and_reach_the_greedy_limit(policy):
-    """Sampled greedy BLT, BLT-S and one-step BLT-DV sessions (rejection-
-    sampling verification): a seed reproduces its bytes, another seed gives
-    others, and a vanishing top_p gives the greedy session exactly."""
+    """Sampled greedy BLT, BLT-S and BLT-DV sessions (one-step, threshold and
+    entropy-bounded drafts; rejection-sampling verification): a seed
+    reproduces its bytes, another seed gives others, and a vanishing top_p
+    gives the greedy session exactly."""
     import block_diffusion_byte_amd as blt
     wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
     w = bltgen.make_weights(wl, gains="random")
     inps = [bltgen.make_sequence_inputs(wl, b) for b in range(3)]
-    pid = {"greedy": blt.BLT_POLICY_GREEDY, "blt_s": blt.BLT_POLICY_BLT_S,
-           "blt_dv": blt.BLT_POLICY_BLT_DV}[policy]
-    block = {"greedy": 1, "blt_s": 4, "blt_dv": 4}[policy]
-    O = blt.BLT_UNMASK_ONE_STEP
-    a = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 5, policy=pid)
-    b = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 5, policy=pid)
-    c = _session(wl, w, inps, 32, block, 0.0, O, 0.8, 0.9, 6, policy=pid)
+    pid = {"greedy": blt.BLT_POLICY_GREEDY, "blt_s": blt.BLT_POLICY_BLT_S}.get(policy, blt.BLT_POLICY_BLT_DV)
+    block = {"greedy": 1, "blt_s": 4}.get(policy, 4)
+    O, alpha = blt.BLT_UNMASK_ONE_STEP, 0.0
+    if policy == "blt_dv_threshold":
+        O, alpha = blt.BLT_UNMASK_THRESHOLD, 0.3
+    if policy == "blt_dv_entropy":
+        O, alpha = blt.BLT_UNMASK_ENTROPY, 3.0
+    a = _session(wl, w, inps, 32, block, alpha, O, 0.8, 0.9, 5, policy=pid)
+    b = _session(wl, w, inps, 32, block, alpha, O, 0.8, 0.9, 5, policy=pid)
+    c = _session(wl, w, inps, 32, block, alpha, O, 0.8, 0.9, 6, policy=pid)
     assert [r["out"] for r in a] == [r["out"] for r in b]
     assert [r["out"] for r in a] != [r["out"] for r in c]
     assert all(r["n"] == 32 for r in a)
-    g = _session(wl, w, inps, 32, block, 0.0, O, 0.0, 1.0, 0, policy=pid)
-    lim = _session(wl, w, inps, 32, block, 0.0, O, 1.0, 1e-7, 5, policy=pid)
+    g = _session(wl, w, inps, 32, block, alpha, O, 0.0, 1.0, 0, policy=pid)
+    lim = _session(wl, w, inps, 32, block, alpha, O, 1.0, 1e-7, 5, policy=pid)
     assert [(r["out"], r["n_dec"], r["accepted"]) for r in lim] == \
         [(r["out"], r["n_dec"], r["accepted"]) for r in g]
     say(f"sampled {policy} sessions: seeded; top_p -> 0 equals greedy; n_dec {[r['n_dec'] for r in a]}")
+
+
+@pytest.mark.parametrize("unmask,alpha", [("threshold", 0.3), ("entropy", 3.0)])
+def test_tiny_fp32_sampled_blt_dv_session_matches_oracle(unmask, alpha):
+    """The native driver's sampled BLT-DV with multi-pass drafts (each draft
+    byte verified against the distribution of the pass that committed it, as
+    kept on the device) reproduces the oracle's sampled blt_dv: bytes,
+    decoder / encoder-global passes and accepted draft bytes (float32: the
+    sampler's and the acceptance test's margins lie far outside the path's
+    rounding for these draws)."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0].replace(head_scale=12.0)
+    w = bltgen.make_weights(wl, gains="random")
+    smp = (0.8, 0.9, 5)
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        refs.append(loops.blt_dv(W, wl, inp64, 32, 4, alpha, one_step=False, unmask=unmask,
+                                 sampling=(smp[0], smp[1], smp[2] + seq)))
+    mode = blt.BLT_UNMASK_ENTROPY if unmask == "entropy" else blt.BLT_UNMASK_THRESHOLD
+    got = _session(wl, w, inps, 32, 4, alpha, mode, smp[0], smp[1], smp[2], policy=blt.BLT_POLICY_BLT_DV)
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"], g["accepted"]) == (r.n_dec, r.n_eg, sum(r.accept)), f"seq {b}"
+    say(f"sampled BLT-DV {unmask} sessions equal the oracle: n_dec {[g['n_dec'] for g in got]}, "
+        f"accepted {[g['accepted'] for g in got]}")
 
 
 def test_sampling_argument_errors():
@@ -271,9 +318,6 @@ def test_sampling_argument_errors():
     wl = bltgen.WORKLOADS[0]
     w = bltgen.make_weights(wl)
     inps = [bltgen.make_sequence_inputs(wl, 0)]
-    with pytest.raises(blt.BltError) as ei:       # threshold BLT-DV drafts are not verifiable here
-        _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.9, 1, policy=blt.BLT_POLICY_BLT_DV)
-    assert ei.value.status == blt.BLT_ENOTIMPL
     with pytest.raises(blt.BltError) as ei:
         _session(wl, w, inps, 8, 4, 0.7, 0, 1.0, 0.0, 1)
     assert ei.value.status == blt.BLT_EINVAL
