@@ -80,6 +80,10 @@ def parse():
                          "reference kernel for scaling HBM traffic counters) and exit")
     ap.add_argument("--device-blocks", action="store_true",
                     help="time BLT-D with device-resident blocks (the host-driven blocks are timed beside them)")
+    ap.add_argument("--plain", action="store_true",
+                    help="only the timed generations of the main workload: no prefill timing, no "
+                         "comparison with the other block driver, no event-timed passes, no legs, "
+                         "no CPU baseline (the program that hardware-counter runs profile)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every decoder pass directly instead of replaying HIP graphs")
     return ap.parse_args()
@@ -336,10 +340,13 @@ def main():
     import block_diffusion_byte_amd as blt
 
     wl = bltgen.WORKLOADS[args.workload]
+    if args.plain:
+        args.no_prof = args.no_legs = args.no_cpu = True
     small = ["k_attn_mfma", "k_gemv_mfma", "k_gemv"]
     fams = [] if args.no_prof else (small if wl.batch * (wl.block + 1) < 16 else ["k_attn_mfma", "k_gemm_mfma"])
-    main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs, prefill_report=True,
-                       device_blocks=args.device_blocks, compare=True)
+    main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs,
+                       prefill_report=not args.plain, device_blocks=args.device_blocks,
+                       compare=not args.plain)
     out = {
         "metric": "decoded bytes/sec",
         "value": main_leg["value"],

@@ -18,7 +18,13 @@ from typing import Dict, List, Optional, Sequence
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libblt.so")
+# BLT_LIB=debug loads the bounds-checking build (libblt_debug.so), BLT_LIB=asan
+# the host-sanitized one (libblt_asan.so; the process must preload the
+# sanitizer runtime); unset: the release build.
+_VARIANT = os.environ.get("BLT_LIB", "")
+if _VARIANT not in ("", "release", "debug", "asan"):
+    raise ImportError(f"BLT_LIB={_VARIANT!r}: expected release, debug or asan")
+LIB_PATH = os.path.join(_HERE, "libblt.so" if _VARIANT in ("", "release") else f"libblt_{_VARIANT}.so")
 
 BLT_OK, BLT_EINVAL, BLT_ECAPACITY, BLT_EDTYPE, BLT_EHIP, BLT_ENOTIMPL = 0, -1, -2, -3, -4, -5
 BLT_F32, BLT_BF16 = 0, 1
@@ -95,7 +101,8 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise ImportError(f"{LIB_PATH} is missing: build it with "
-                              "`python -m block_diffusion_byte_amd.build`")
+                              "`python -m block_diffusion_byte_amd.build"
+                              f"{' --variant ' + _VARIANT if _VARIANT not in ('', 'release') else ''}`")
         L = C.CDLL(LIB_PATH)
         P, I32, I64, F = C.c_void_p, C.c_int32, C.c_int64, C.c_float
         sig = {

@@ -10,6 +10,7 @@
 #include <vector>
 
 #include "blt_ctx.h"
+#include "host_checks.h"
 
 using namespace blt;
 
@@ -83,6 +84,17 @@ namespace blt {
 blt_status stage_pass(blt_ctx *c, const std::vector<RowDesc> &rows,
                       const std::vector<SeqDesc> &seqs, const std::vector<int64_t> *offs,
                       const PassWs *dst) {
+#ifdef BLT_DEBUG_BOUNDS
+  {
+    const blt_config &g = c->cfg;
+    const DescLimits lim{g.max_batch, g.max_ctx, g.max_latents, g.max_rows,
+                         (int64_t)g.max_batch * g.max_block};
+    char msg[160];
+    if (const char *why = check_pass_descs(rows.data(), (int)rows.size(), seqs.data(),
+                                           (int)seqs.size(), lim, msg, sizeof msg))
+      return fail(c, BLT_EINVAL, why);
+  }
+#endif
   StageSlot &sl = c->ring[c->ring_next];
   c->ring_next = (c->ring_next + 1) % kRing;
   if (sl.pending) {

@@ -27,63 +27,11 @@
 #include <vector>
 
 #include "blt_ctx.h"
+#include "host_patcher.h"
 
 using namespace blt;
 
 namespace {
-
-// Stand-in patcher: after a generated byte a new patch starts iff the patch
-// already holds 8 bytes or the (1 + 256*prev + byte)-th SplitMix64 output
-// (Steele, Lea, Flood 2014) from the sequence's salt is 0 modulo 4.
-uint64_t splitmix64_nth(uint64_t seed, uint64_t n) {
-  uint64_t z = seed + 0x9E3779B97F4A7C15ull * n;
-  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
-  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
-  return z ^ (z >> 31);
-}
-
-struct Seg {
-  std::vector<int32_t> patch;   // patch index of every byte
-  std::vector<uint8_t> ends;    // a boundary follows the byte
-  int cur_len = 0;
-  int last_complete = -1;       // index of the newest complete patch
-
-  void init_prompt(const std::vector<int32_t> &lens) {
-    patch.clear();
-    ends.clear();
-    for (size_t p = 0; p < lens.size(); ++p)
-      for (int j = 0; j < lens[p]; ++j) {
-        patch.push_back((int32_t)p);
-        ends.push_back(j == lens[p] - 1);
-      }
-    cur_len = lens.empty() ? 0 : lens.back();
-    last_complete = (int)lens.size() - 1;
-  }
-  void push(uint64_t salt, uint8_t prev, uint8_t byte) {
-    const bool fresh = ends.empty() || ends.back();
-    const int p = patch.empty() ? 0 : patch.back() + (fresh ? 1 : 0);
-    cur_len = fresh ? 1 : cur_len + 1;
-    const bool e = cur_len >= 8 || (splitmix64_nth(salt, 1 + 256ull * prev + byte) & 3ull) == 0;
-    patch.push_back(p);
-    ends.push_back(e);
-    if (e) last_complete = p;
-  }
-  void truncate(size_t n) {
-    patch.resize(n);
-    ends.resize(n);
-    // recompute the running state from the kept bytes
-    cur_len = 0;
-    last_complete = -1;
-    for (size_t i = 0; i < n; ++i) {
-      cur_len = (i == 0 || ends[i - 1]) ? 1 : cur_len + 1;
-      if (ends[i]) last_complete = patch[i];
-    }
-  }
-  // clean byte i reads o_{p(i)-1}, or o_{p(i)} when it ends its patch
-  int causal_target(size_t i) const { return ends[i] ? patch[i] : patch[i] - 1; }
-  // the last prefix byte and the block read the last (possibly truncated) patch's latent
-  int last_target() const { return patch.back(); }
-};
 
 struct SeqState {
   std::vector<uint8_t> prompt;
