@@ -1179,19 +1179,22 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
 // Causal attention for long runs of clean rows (prompt prefill, KV rebuild):
 // the keys of every row are a prefix [0, kend) of its sequence's cache, so
 // one pass over the keys serves a whole tile of rows with an online softmax
-// (running max and sum per row, the accumulator rescaled when the max grows)
-// and the normalised output is written straight to the activations, with no
-// partials and no merge.
+// (a reference max and a running sum per row, the accumulator rescaled when
+// the max outgrows the reference by 2^8) and the normalised output is written
+// straight to the activations, with no partials and no merge.
 //
 // Row tiles hold kFlashRows = 128 consecutive rows of a sequence in the pass,
 // 32 per wave in two groups of 16.  Under the causal mask tile i reads about
 // i + 1 key tiles, so workgroup (p, head h, sequence b) takes the pair of row
-// tiles n-1-p and p, which balances the work of the workgroups.  For each row
+// tiles n-1-p and p, which balances the work of the workgroups; the
+// workgroups of one XCD take consecutive (pair, head) items, so they share
+// their heads' keys and values in that XCD's L2.  For each row
 // tile it walks the keys below the tile's largest kend in tiles of KT keys
 // staged through LDS (double-buffered: the next tile's loads are in flight
 // during the current tile's products).  Same MFMA formulation as the split-K
-// kernel: S^T = K Q^T leaves each lane with scores of one row, which are
-// already the B operand of O^T += V^T P^T (P rounded to bf16 for the
+// kernel: S^T = K Q^T, with the K rows fed permuted, leaves each lane with
+// the scores of one row for 8 consecutive keys of each 32, which are already
+// the B operand of O^T += V^T P^T (P rounded to bf16 for the
 // product, its sum kept in f32: the kernel is bound by its MFMA and softmax
 // work, and the hi + lo split of the split-K kernel would double the P.V
 // products), and the lane's O^T entries belong to that same row, so the softmax
@@ -1222,11 +1225,21 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
   __shared__ __align__(16) uint16_t kt_s[2][KT * KST];
   __shared__ __align__(16) uint16_t vt_s[2][DH * VST];
   __shared__ int kend_s[kFlashRows];
-  const int h = blockIdx.y, b = blockIdx.z;
+  // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
+  // L2: workgroup i (linear index) runs on XCD i % 8, which takes a
+  // contiguous run of the (pair, head, sequence) items, so the workgroups of
+  // one XCD share a few heads' keys and values in its L2 instead of every
+  // XCD streaming all of them.
+  const int gx = (int)gridDim.x, gy = (int)gridDim.y;
+  const int total = gx * gy * (int)gridDim.z;
+  const int lin = (int)blockIdx.x + gx * ((int)blockIdx.y + gy * (int)blockIdx.z);
+  const int xcd = lin & 7;
+  const int item = xcd * (total >> 3) + min(xcd, total & 7) + (lin >> 3);
+  const int h = (item / gx) % gy, b = item / (gx * gy);
   const SeqDesc sd = seqs[b];
   if (!sd.attn_flash) return;
   const int ntile = (sd.nrows + kFlashRows - 1) / kFlashRows;
-  const int pr = (int)blockIdx.x;
+  const int pr = item % gx;
   if (pr >= (ntile + 1) / 2) return;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int d = g.n_heads * DH;
@@ -1236,6 +1249,12 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
   const uint16_t *Vt = Kp + (int64_t)g.n_heads * plane;
   const int kmax = sd.kmax;
   const float c2 = 1.4426950408889634f / sqrtf((float)DH);   // log2(e) / sqrt(d_h)
+  // Keys of the score tiles: row m of 16-key tile k16 is key 32 (k16/2) +
+  // 8 (m/4) + 4 (k16%2) + m%4 of the LDS tile, so that after S^T = K Q^T
+  // lane group q holds keys 8q..8q+7 of each 32-key group for its row: the
+  // B-operand layout of O^T += V^T P^T with k-slot 8q+i = key 8q+i, and the V
+  // operand of a lane is one 16-byte piece.
+  auto kperm = [](int k16, int m) { return 32 * (k16 >> 1) + 8 * (m >> 2) + 4 * (k16 & 1) + (m & 3); };
 
   // staging: thread t moves NK 16-byte pieces of K ([key][dim]) and of V^T
   // ([dim][key]) per tile; pieces past kmax become zeros.  V piece i is
@@ -1342,7 +1361,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
           bf16x8_t ka[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            ka[ks] = *(const bf16x8_t *)(&kt_s[buf][(16 * k16 + lr) * KST + 32 * ks + 8 * lq]);
+            ka[ks] = *(const bf16x8_t *)(&kt_s[buf][kperm(k16, lr) * KST + 32 * ks + 8 * lq]);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
             acc[gi][k16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1362,44 +1381,51 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
             for (int k16 = 0; k16 < N16; ++k16)
 #pragma unroll
               for (int v = 0; v < 4; ++v)
-                if (key0 + 16 * k16 + 4 * lq + v >= my_kend[gi]) acc[gi][k16][v] = -INFINITY;
+                if (key0 + kperm(k16, 4 * lq + v) >= my_kend[gi]) acc[gi][k16][v] = -INFINITY;
         }
         u32x4_t ph[2][NJ];
 #pragma unroll
         for (int gi = 0; gi < 2; ++gi) {
-          float mt = -INFINITY;
+          float sv[KT / 4];                   // the lane's scores, read once from the accumulators
 #pragma unroll
           for (int k16 = 0; k16 < N16; ++k16)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) mt = fmaxf(mt, acc[gi][k16][v]);
-          // key 0 lies in the first tile and every row has kend >= 1, so the
-          // running max is finite from the first tile on; exp2(-inf) = 0
-          const float m_new = fmaxf(m_run[gi], max_lane_groups(mt) * c2);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[gi] - m_new);
+            for (int v = 0; v < 4; ++v) sv[4 * k16 + v] = acc[gi][k16][v];
+          float mt = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < KT / 4; ++i) mt = fmaxf(mt, sv[i]);
+          // The reference max m moves only when a row's max exceeds it by 8
+          // (base-2 units): the probabilities exp2(s c - m) stay <= 256, exact
+          // in f32 and as bf16 operands, the numerator and the denominator
+          // share the scale, and the output is rescaled rarely.  Key 0 lies
+          // in the first tile and every row has kend >= 1, so m is finite
+          // from the first tile on; exp2(-inf) = 0.
+          const float m_tile = max_lane_groups(mt) * c2;
+          const bool grow = m_tile > m_run[gi] + 8.f;
+          const float m_new = grow ? m_tile : m_run[gi];
+          const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[gi] - m_new) : 1.f;
           m_run[gi] = m_new;
           float ps = 0.f;
 #pragma unroll
           for (int i = 0; i < KT / 4; i += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4], c2, -m_new));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(acc[gi][i / 4][i % 4 + 1], c2, -m_new));
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -m_new));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i + 1], c2, -m_new));
             ps += p0 + p1;
             ph[gi][i / 8][(i % 8) / 2] = f2bf2(p0, p1);
           }
           l_run[gi] = l_run[gi] * alpha + ps;
-          if (__ballot(alpha != 1.f)) {       // the running max moved for some row of the wave
+          if (__ballot(grow)) {               // the reference max moved for some row of the wave
 #pragma unroll
             for (int dt = 0; dt < DT; ++dt) o[gi][dt] = o[gi][dt] * alpha;
           }
         }
         // O^T += V^T P^T: slot group j holds k-slots 8 lq + i <-> keys
-        // 32 j + 4 lq + i (i < 4) and 32 j + 16 + 4 lq + i - 4; every V operand read once
+        // 32 j + 8 lq + i, one 16-byte piece of the V^T tile; every V operand read once
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const uint16_t *vrow = &vt_s[buf][(16 * dt + lr) * VST + 32 * j];
-            const uint2 v0 = *(const uint2 *)(vrow + 4 * lq), v1 = *(const uint2 *)(vrow + 16 + 4 * lq);
-            const bf16x8_t va = __builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y));
+            const bf16x8_t va = *(const bf16x8_t *)(&vt_s[buf][(16 * dt + lr) * VST + 32 * j + 8 * lq]);
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
               o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
