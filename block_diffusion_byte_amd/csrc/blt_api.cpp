@@ -286,7 +286,8 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
     }
     HIP_TRY(c, launch_attention(bf, w.q, st->kv, geo, l, w.seqs, S, p.seq1, p.grid_chunks,
                                 p.attn_sub, p.attn_wg, c->max_chunks,
-                                p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s, p.gate));
+                                p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s, p.gate,
+                                c->flash_kg));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.wo; a.N = d; a.K = d;
@@ -925,6 +926,13 @@ blt_status blt_attention_chunks(blt_ctx *c, int32_t chunks) {
   if (!c) return BLT_EINVAL;
   if (chunks < 0) return fail(c, BLT_EINVAL, "blt_attention_chunks: chunks must be >= 0");
   c->attn_chunks = chunks;
+  return BLT_OK;
+}
+
+blt_status blt_flash_key_groups(blt_ctx *c, int32_t groups) {
+  if (!c) return BLT_EINVAL;
+  if (groups < 0 || groups > 2) return fail(c, BLT_EINVAL, "blt_flash_key_groups: groups must be 0, 1 or 2");
+  c->flash_kg = groups;
   return BLT_OK;
 }
 

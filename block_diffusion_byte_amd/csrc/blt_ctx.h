@@ -85,6 +85,8 @@ struct blt_ctx {
   bool graphs = false;
   // split-K attention chunks per workgroup forced by blt_attention_chunks (0: per pass)
   int attn_chunks = 0;
+  // key groups of the causal attention kernel forced by blt_flash_key_groups (0: per pass)
+  int flash_kg = 0;
   hipStream_t cap_stream = nullptr;
   std::unordered_map<blt::PassKey, blt::GraphEntry, blt::PassKeyHash> graph_cache;
   // profiling: family being timed, event pool, pending and accumulated figures

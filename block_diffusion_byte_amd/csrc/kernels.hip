@@ -1206,8 +1206,8 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
 // the row's statistics unchanged, whatever the other rows of the tile read.
 // Cache rows at or past the sequence's kmax are never written and are staged
 // as zeros.
-template <int DH>
-__global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
+template <int DH, int KG>
+__global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
                                                     int layer, const SeqDesc *seqs,
                                                     const RowDesc *rows, void *a_out,
                                                     const int32_t *gate) {
@@ -1222,8 +1222,13 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
   constexpr int NK = KT * DH / 8 / 256;       // 16-byte pieces per thread per tile, K and V each
   static_assert(NK >= 1 && KT * DH / 8 == NK * 256, "tile must split evenly over 256 threads");
   static_assert(kFlashRows == 128, "4 waves x 2 groups x 16 rows");
-  __shared__ __align__(16) uint16_t kt_s[2][KT * KST];
-  __shared__ __align__(16) uint16_t vt_s[2][DH * VST];
+  static_assert(KG == 1 || KG == 2, "one or two key groups");
+  // key group kg (KG = 2: eight waves) walks the key tiles kg, kg + KG, ...
+  // through its own two LDS buffers
+  constexpr int BUF = KT * KST + DH * VST;    // one buffer: a K tile, then a V^T tile
+  __shared__ __align__(16) uint16_t smem[KG * 2 * BUF];
+  auto kt_s = [&](int grp, int buf) { return smem + (grp * 2 + buf) * BUF; };
+  auto vt_s = [&](int grp, int buf) { return smem + (grp * 2 + buf) * BUF + KT * KST; };
   __shared__ int kend_s[kFlashRows];
   // Workgroups are dispatched round-robin over the 8 XCDs, each with its own
   // L2: workgroup i (linear index) runs on XCD i % 8, which takes a
@@ -1241,7 +1246,8 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
   const int ntile = (sd.nrows + kFlashRows - 1) / kFlashRows;
   const int pr = item % gx;
   if (pr >= (ntile + 1) / 2) return;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
+  const int kg = (int)threadIdx.x >> 8, t = (int)threadIdx.x & 255;   // key group, thread in it
+  const int lane = t & 63, w = t >> 6, lr = lane & 15, lq = lane >> 4;
   const int d = g.n_heads * DH;
   const int64_t plane = (int64_t)g.max_ctx * DH;
   const uint16_t *Kp =
@@ -1283,7 +1289,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
       const int kk = i / (DH / 8), kp = i % (DH / 8);
       u32x4_t kv = kr[j];
       if (key0 + kk >= kmax) kv = u32x4_t{0u, 0u, 0u, 0u};
-      *(u32x4_t *)(&kt_s[buf][kk * KST + 8 * kp]) = kv;
+      *(u32x4_t *)(kt_s(kg, buf) + kk * KST + 8 * kp) = kv;
       const int dd = vdim(i), vp = vpiece(i);
       u32x4_t vv = vr[j];
       const int k0 = key0 + 8 * vp;
@@ -1295,7 +1301,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
           vv[e] = lo | hi;
         }
       }
-      *(u32x4_t *)(&vt_s[buf][dd * VST + 8 * vp]) = vv;
+      *(u32x4_t *)(vt_s(kg, buf) + dd * VST + 8 * vp) = vv;
     }
   };
 
@@ -1305,7 +1311,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
     const int r0 = tile * kFlashRows;
     const int nr = min(kFlashRows, sd.nrows - r0);
     if (half) __syncthreads();                   // LDS of the first row tile fully read
-    if (t < kFlashRows) kend_s[t] = rows[sd.row0 + r0 + min(t, nr - 1)].kend;
+    if (kg == 0 && t < kFlashRows) kend_s[t] = rows[sd.row0 + r0 + min(t, nr - 1)].kend;
     // the lane's rows: 32 w + 16 g + lr of the tile (clamped into the tile's rows)
     bf16x8_t qb[2][KS];
 #pragma unroll
@@ -1344,16 +1350,19 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
       for (int dt = 0; dt < DT; ++dt) o[gi][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
 
-    if (ntk > 0) {
-      load(0);
-      store(0, 0);
+    if (kg < ntk) {
+      load(kg);
+      store(kg, 0);
     }
     __syncthreads();
-    for (int tk = 0; tk < ntk; ++tk) {
-      const int buf = tk & 1;
+    // every key group runs the same number of steps (barriers line up); a
+    // group whose tile lies past the last one idles in that step
+    for (int it = 0; it * KG < ntk; ++it) {
+      const int tk = it * KG + kg;
+      const int buf = it & 1;
       const int key0 = tk * KT;
-      if (tk + 1 < ntk) load(tk + 1);
-      if (key0 < kend_hi) {                   // wave-uniform: some row of the wave reads these keys
+      if (tk + KG < ntk) load(tk + KG);
+      if (tk < ntk && key0 < kend_hi) {       // wave-uniform: some row of the wave reads these keys
         // S^T for both row groups; every K operand read once
         f32x4_t acc[2][N16];
 #pragma unroll
@@ -1361,7 +1370,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
           bf16x8_t ka[KS];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks)
-            ka[ks] = *(const bf16x8_t *)(&kt_s[buf][kperm(k16, lr) * KST + 32 * ks + 8 * lq]);
+            ka[ks] = *(const bf16x8_t *)(kt_s(kg, buf) + kperm(k16, lr) * KST + 32 * ks + 8 * lq);
 #pragma unroll
           for (int gi = 0; gi < 2; ++gi) {
             acc[gi][k16] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -1425,7 +1434,7 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int dt = 0; dt < DT; ++dt) {
-            const bf16x8_t va = *(const bf16x8_t *)(&vt_s[buf][(16 * dt + lr) * VST + 32 * j + 8 * lq]);
+            const bf16x8_t va = *(const bf16x8_t *)(vt_s(kg, buf) + (16 * dt + lr) * VST + 32 * j + 8 * lq);
 #pragma unroll
             for (int gi = 0; gi < 2; ++gi) {
               o[gi][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
@@ -1433,12 +1442,48 @@ __global__ __launch_bounds__(256) void k_attn_flash(const float *q, const void *
             }
           }
       }
-      if (tk + 1 < ntk) store(tk + 1, buf ^ 1);
+      if (tk + KG < ntk) store(tk + KG, buf ^ 1);
       __syncthreads();
+    }
+    if constexpr (KG == 2) {
+      // the second key group's (o, m, l) join the first's through LDS (the
+      // operand buffers are free after the last barrier): o = o0 a0 + o1 a1,
+      // l = l0 a0 + l1 a1 with a_i = exp2(m_i - max(m0, m1)); m0 is finite
+      // (key 0 is the first group's), a group without keys has m = -inf, a = 0
+      float *xs = reinterpret_cast<float *>(smem);
+      constexpr int NV = 2 * DT * 4 + 4;     // floats per lane
+      static_assert(256 * NV * 4 <= (int)sizeof(smem), "exchange fits the operand buffers");
+      float *mine = xs + (size_t)t * NV;
+      if (kg == 1) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mine[(gi * DT + dt) * 4 + v] = o[gi][dt][v];
+          mine[2 * DT * 4 + gi] = m_run[gi];
+          mine[2 * DT * 4 + 2 + gi] = l_run[gi];
+        }
+      }
+      __syncthreads();
+      if (kg == 0) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const float m1 = mine[2 * DT * 4 + gi], l1 = mine[2 * DT * 4 + 2 + gi];
+          const float mx = fmaxf(m_run[gi], m1);
+          const float a0 = __builtin_amdgcn_exp2f(m_run[gi] - mx), a1 = __builtin_amdgcn_exp2f(m1 - mx);
+          l_run[gi] = l_run[gi] * a0 + l1 * a1;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[gi][dt][v] = o[gi][dt][v] * a0 + mine[(gi * DT + dt) * 4 + v] * a1;
+        }
+      }
     }
     // o[g][dt][v]: unnormalised output of the lane's row of group g, dim 16 dt + 4 lq + v
 #pragma unroll
     for (int gi = 0; gi < 2; ++gi) {
+      if (kg != 0) break;
       const float L = sum_lane_groups(l_run[gi]);
       const int wr = 32 * w + 16 * gi + lr;
       if (wr < nr) {
@@ -2263,16 +2308,24 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                         int n_seq, const SeqDesc *sd_host, int grid_chunks, int nsub, int wg,
                         int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
-                        hipEvent_t ev1, bool ev_flash, hipStream_t s, const int32_t *gate) {
+                        hipEvent_t ev1, bool ev_flash, hipStream_t s, const int32_t *gate,
+                        int flash_kg) {
   if constexpr (BF) {
     if (flash_tiles > 0) {
       const dim3 fg((flash_tiles + 1) / 2, g.n_heads, n_seq);   // pairs of row tiles
-      if (ev0 && ev_flash)
-        hipExtLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
+      // up to 2048 workgroups: eight waves in two key groups (two waves per
+      // SIMD with one workgroup per CU); measured 8-25% faster from 128 to
+      // 1024 workgroups, equal at 512-3072, 6% slower at 49152 (64 prompts
+      // of 8192 rows).  The choice depends on the grid only (flash_kg > 0
+      // forces a form).
+      const bool two = flash_kg ? flash_kg == 2 : (int64_t)fg.x * fg.y * fg.z <= 2048;
+      hipEvent_t e0 = ev_flash ? ev0 : nullptr, e1 = ev_flash ? ev1 : nullptr;
+      if (two)
+        hipExtLaunchKernelGGL((k_attn_flash<DH, 2>), fg, dim3(512), 0, s, e0, e1, 0, q, kv, g, layer,
                               seqs, rows, a_out, gate);
       else
-        hipLaunchKernelGGL((k_attn_flash<DH>), fg, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
-                           a_out, gate);
+        hipExtLaunchKernelGGL((k_attn_flash<DH, 1>), fg, dim3(256), 0, s, e0, e1, 0, q, kv, g, layer,
+                              seqs, rows, a_out, gate);
     }
   }
   if (ev_flash) ev0 = ev1 = nullptr;
@@ -2327,15 +2380,15 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
                             int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
-                            hipStream_t s, const int32_t *gate) {
+                            hipStream_t s, const int32_t *gate, int flash_kg) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
   if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,   \
                                   max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1,        \
-                                  ev_flash, s, gate);                                             \
+                                  ev_flash, s, gate, flash_kg);                                   \
   else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,       \
                               max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s, \
-                              gate);
+                              gate, flash_kg);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;

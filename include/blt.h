@@ -352,6 +352,17 @@ blt_status blt_graphs_enable(blt_ctx *ctx, int32_t enable);
  * negative count. */
 blt_status blt_attention_chunks(blt_ctx *ctx, int32_t chunks);
 
+/* Form of the causal (prefill) self-attention kernel, which takes a bf16
+ * sequence's clean rows of a pass once it has at least 64 of them.  Its
+ * workgroups each take a pair of 128-row tiles of one (sequence, head);
+ * groups = 0 (the default) lets each pass choose from its grid: with up to
+ * 2048 workgroups, eight waves in two key groups that walk alternate key
+ * tiles and join their softmax states at the end; with more, four waves
+ * that walk every key tile.  groups = 1 or 2 forces that form.  The form
+ * changes the rounding of the softmax sums, not what is computed.
+ * BLT_EINVAL for other values. */
+blt_status blt_flash_key_groups(blt_ctx *ctx, int32_t groups);
+
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
  * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),
  * gb_per_seq = bytes_total / 1e9 / n_seq.  Host-only, exact integers;

@@ -32,7 +32,7 @@ PLAN = {
                            # pass (rollback of the last prompt row, the block's bytes appended)
     2: ([0, 15], 16, 2),   # BLT-D-16, batch 16: the first two block passes
     3: ([0], 10, 18),      # BLT-S k=8, batch 1: two rounds of 8 draft passes and a verification
-    4: ([0, 63], 1, 2),    # BLT-DV-8 one-step, batch 64: draft pass and verification
+    4: ([0, 21, 42, 63], 1, 2),   # BLT-DV-8 one-step, batch 64: draft pass and verification
 }
 KINDS = {"block": 0, "draft": 1, "verify": 2, "ar": 3}
 

@@ -266,7 +266,7 @@ def test_fullsize_blts8_batch1_first_round():
 def test_fullsize_bltdv8_batch64_first_round():
     """BLT-DV-8 one-step at the larger decoder (d 1536, 24 heads), batch 64,
     8192-byte prompts: the one-step draft pass and the verification pass of
-    all 64 sequences, sequences 0 and 63 against the oracle."""
+    all 64 sequences, sequences 0, 21, 42 and 63 against the oracle."""
     wl = bltgen.WORKLOADS[4]
     gold = _gold(wl)
     fb = FullBatch(wl)

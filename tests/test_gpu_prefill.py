@@ -6,7 +6,9 @@ A bf16 sequence with at least 64 clean rows in a pass takes the causal
 (flash) attention kernel; shorter ones and block passes take the split-K
 kernel.  These tests append ragged runs of rows (tiles of 64 with a partial
 last tile, a cached prefix before the run, two sequences of different lengths
-in one pass, and a pass that mixes both kernels) and compare every row's
+in one pass, and a pass that mixes both kernels), with the causal kernel in
+each of its forms (four waves, or two key groups whose softmax states join
+at the end), and compare every row's
 logits with the float64 oracle's cached decoder (bf16 tolerance: 2e-2
 absolute), and every greedy byte whose oracle top-2 gap is outside the
 rounding band.
@@ -90,7 +92,10 @@ def _append(blt, torch, dec, seqs, plan, z):
     return out
 
 
-def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes():
+@pytest.mark.parametrize("groups", [0, 1, 2])
+def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes(groups):
+    """groups: the causal kernel's form (0: chosen per pass, 1: four waves
+    over every key tile, 2: two key groups of four waves)."""
     import torch
     import block_diffusion_byte_amd as blt
     wl = MINI
@@ -98,6 +103,7 @@ def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes():
     seqs = [_Seq(wl, w, s) for s in range(2)]
     dec = decoder_for(wl, w, max_batch=2, max_rows=512)
     try:
+        blt.blt_flash_key_groups(dec.ctx, groups)
         for s in range(2):
             table = torch.from_numpy(seqs[s].inp["latents"]).to("cuda:0", dec.torch_dtype)
             blt.blt_latents_put(dec.ctx, dec.state, [s] * wl.n_latents, list(range(wl.n_latents)),
@@ -119,6 +125,8 @@ def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes():
         seqs[0].oracle.truncate(300)
         got = _append(blt, torch, dec, seqs, [(0, 300, 299)], z)
         _check(got[0], seqs[0].expect(300, 299), "seq 0 rows 300..598 after truncation to 300")
+        with pytest.raises(blt.BltError):
+            blt.blt_flash_key_groups(dec.ctx, 3)
     finally:
         dec.close()
 
