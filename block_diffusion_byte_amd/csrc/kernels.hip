@@ -1283,6 +1283,16 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
   };
   auto store = [&](int tk, int buf) {
     const int key0 = tk * KT;
+    if (key0 + KT <= kmax) {                   // uniform: the whole tile lies below kmax
+#pragma unroll
+      for (int j = 0; j < NK; ++j) {
+        const int i = t + 256 * j;
+        const int kk = i / (DH / 8), kp = i % (DH / 8);
+        *(u32x4_t *)(kt_s(kg, buf) + kk * KST + 8 * kp) = kr[j];
+        *(u32x4_t *)(vt_s(kg, buf) + vdim(i) * VST + 8 * vpiece(i)) = vr[j];
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int i = t + 256 * j;
