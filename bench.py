@@ -308,7 +308,17 @@ def cpu_baseline(wl, n_all, n_one):
     t_all, p_all = decode(n_all)
     with threadpool_limits(limits=1):
         t_one, p_one = decode(n_one)
+    cpu_model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": n_all / t_all, "unit": "bytes/s", "cores": int(cores), "kind": "oracle",
+            "host": {"cpu_model": cpu_model, "nproc": os.cpu_count(),
+                     "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None},
             "sample": f"sequence 0 of {wl.name} with its full {len(x0)}-byte prompt (prefill {t_pre:.1f} s, "
                       f"untimed): {n_all} bytes ({p_all} decoder passes) in {t_all:.1f} s on {cores} threads",
             "single_thread": {"value": n_one / t_one, "unit": "bytes/s", "cores": 1,
