@@ -208,6 +208,60 @@ def test_tiny_fp32_sessions_match_oracle_exactly(policy):
     say(f"{policy}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
 
 
+# (policy, block or draft window, alpha or entropy bound, unmask, causal block mask, head scale)
+EDGE_BLOCKS = {
+    "blt_d_b1": ("blt_d", 1, 0.7, "threshold", False, 1.0),
+    "blt_d_b1_causal": ("blt_d", 1, 0.7, "threshold", True, 1.0),
+    "blt_d_b64": ("blt_d", 64, 0.7, "threshold", False, 1.0),
+    "blt_d_b64_causal_one_step": ("blt_d", 64, 0.7, "one_step", True, 1.0),
+    "blt_d_b64_entropy_peaked": ("blt_d", 64, 10.0, "entropy", False, 12.0),
+    "blt_s_k1": ("blt_s", 1, 0.0, "threshold", False, 1.0),
+    "blt_dv_b1": ("blt_dv", 1, 0.7, "one_step", False, 1.0),
+    "blt_dv_b64": ("blt_dv", 64, 0.7, "one_step", False, 1.0),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE_BLOCKS))
+def test_tiny_fp32_degenerate_and_largest_blocks_match_oracle(case):
+    """The smallest and the largest block / draft window (1 and 64 positions,
+    the most one unmask wave takes) in native sessions: bytes, decoder and
+    encoder/global passes, rounds and accepted bytes equal the oracle's
+    (pytorch.kr summary, "BLT-D inference", "BLT-S and BLT-DV").  With 40
+    bytes to generate, a 64-position block over-fills the generation and is
+    truncated after its passes are counted; with B = 1 every pass commits
+    its one position.  The entropy-bounded case takes the peaked head
+    (x12), whose entropies are spread far beyond float32 rounding, so every
+    ranking of the 64 positions is decided.  The latent tables and caches
+    are sized for 40 + 2 x 64 bytes, as a drafted block past the 40 bytes
+    completes patches of its own."""
+    import block_diffusion_byte_amd as blt
+    policy, B, alpha, unmask, causal, scale = EDGE_BLOCKS[case]
+    n_gen = 40
+    wl = bltgen.WORKLOADS[0].replace(block=B, n_gen=n_gen + 2 * B, head_scale=scale)
+    w = bltgen.make_weights(wl, gains="random")
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        if policy == "blt_d":
+            refs.append(loops.blt_d(W, wl, inp64, n_gen, B, alpha, block_causal=causal, unmask=unmask))
+        elif policy == "blt_s":
+            refs.append(loops.blt_s(W, wl, inp64, n_gen, B))
+        else:
+            refs.append(loops.blt_dv(W, wl, inp64, n_gen, B, alpha, unmask=unmask))
+    pid = {"blt_d": blt.BLT_POLICY_BLT_D, "blt_s": blt.BLT_POLICY_BLT_S, "blt_dv": blt.BLT_POLICY_BLT_DV}[policy]
+    um = {"threshold": blt.BLT_UNMASK_THRESHOLD, "one_step": blt.BLT_UNMASK_ONE_STEP,
+          "entropy": blt.BLT_UNMASK_ENTROPY}[unmask]
+    mask = blt.BLT_BLOCK_CAUSAL if causal else blt.BLT_BLOCK_BIDIR
+    got = _session(wl, w, inps, pid, n_gen, B, alpha, um, mask, max_rows=3 * (2 * B + 2))
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
+        if r.accept:
+            assert g["rounds"] == len(r.accept) and g["accepted"] == sum(r.accept)
+    say(f"{case}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
+
+
 @pytest.mark.parametrize("case", ["threshold", "peaked", "entropy", "one_step", "causal"])
 def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
     """BLT-D with every block after the first planned, decoded, committed and
