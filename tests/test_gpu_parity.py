@@ -463,6 +463,17 @@ def test_argument_errors_enqueue_nothing():
             with pytest.raises(blt.BltError) as ei:
                 blt.blt_kv_append(dec.ctx, dec.state, [1], [bad], [1], 1, [0], bytes_=[7])
             assert ei.value.status == blt.BLT_EINVAL
+        # empty inputs: an append of no rows and a latent upload of no
+        # entries are accepted and do nothing (slot 0 still has no rows, so
+        # start 1 stays rejected); a pass over no sequences is refused
+        blt.blt_kv_append(dec.ctx, dec.state, [0, 1], [0, 0], [0, 0], 1, [0, 0], bytes_=[0, 0])
+        blt.blt_latents_put(dec.ctx, dec.state, [], [], torch.zeros(1, device="cuda:0"), 0)
+        with pytest.raises(blt.BltError) as ei:
+            blt.blt_kv_append(dec.ctx, dec.state, [0], [1], [1], 1, [0], bytes_=[7])
+        assert ei.value.status == blt.BLT_EINVAL
+        with pytest.raises(blt.BltError) as ei:
+            blt.blt_decode_block_step(dec.ctx, dec.state, [], [], bt, 4, [], 0.7, masked_left=ml)
+        assert ei.value.status == blt.BLT_EINVAL
         torch.cuda.synchronize()
     finally:
         dec.close()
