@@ -1416,19 +1416,21 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
           // The reference max m moves only when a row's max exceeds it by 8
           // (base-2 units): the probabilities exp2(s c - m) stay <= 256, exact
           // in f32 and as bf16 operands, the numerator and the denominator
-          // share the scale, and the output is rescaled rarely.  Key 0 lies
-          // in the first tile and every row has kend >= 1, so m is finite
-          // from the first tile on; exp2(-inf) = 0.
+          // share the scale, and the output is rescaled rarely.  A row whose
+          // keys all lie past its kend so far (m = -inf: the second key
+          // group's first tiles) takes m = 0 in the exponent, so its masked
+          // scores give exp2(-inf) = 0 and not exp2(-inf + inf).
           const float m_tile = max_lane_groups(mt) * c2;
           const bool grow = m_tile > m_run[gi] + 8.f;
           const float m_new = grow ? m_tile : m_run[gi];
           const float alpha = grow ? __builtin_amdgcn_exp2f(m_run[gi] - m_new) : 1.f;
           m_run[gi] = m_new;
+          const float m_exp = m_new == -INFINITY ? 0.f : m_new;
           float ps = 0.f;
 #pragma unroll
           for (int i = 0; i < KT / 4; i += 2) {
-            const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -m_new));
-            const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i + 1], c2, -m_new));
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(sv[i], c2, -m_exp));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(sv[i + 1], c2, -m_exp));
             ps += p0 + p1;
             ph[gi][i / 8][(i % 8) / 2] = f2bf2(p0, p1);
           }

@@ -125,6 +125,12 @@ def test_causal_kernel_ragged_tiles_prefix_and_mixed_passes(groups):
         seqs[0].oracle.truncate(300)
         got = _append(blt, torch, dec, seqs, [(0, 300, 299)], z)
         _check(got[0], seqs[0].expect(300, 299), "seq 0 rows 300..598 after truncation to 300")
+        # pass 5: 100 rows after a 40-row prefix: the first wave's rows read
+        # 41..72 keys, so the second key group's first tile (keys 64..127)
+        # lies wholly past the kend of some of them
+        seqs[1].oracle.truncate(40)
+        got = _append(blt, torch, dec, seqs, [(1, 40, 100)], z)
+        _check(got[1], seqs[1].expect(40, 100), "seq 1 rows 40..139 after truncation to 40")
         with pytest.raises(blt.BltError):
             blt.blt_flash_key_groups(dec.ctx, 3)
     finally:
