@@ -932,6 +932,7 @@ blt_status blt_attention_chunks(blt_ctx *c, int32_t chunks) {
 blt_status blt_flash_key_groups(blt_ctx *c, int32_t groups) {
   if (!c) return BLT_EINVAL;
   if (groups < 0 || groups > 2) return fail(c, BLT_EINVAL, "blt_flash_key_groups: groups must be 0, 1 or 2");
+  if (groups != c->flash_kg) drop_graphs(c);   // captured passes keep the form they were captured with
   c->flash_kg = groups;
   return BLT_OK;
 }
