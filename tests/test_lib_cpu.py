@@ -81,3 +81,10 @@ def test_null_context_and_weights():
     ctx = C.c_void_p()
     assert L.blt_create(C.byref(_cfg()), None, None, C.byref(ctx)) == blt.BLT_EINVAL
     assert L.blt_last_error(None) == b"NULL context"
+    # the tuning controls and the session switches refuse a NULL context or session
+    assert L.blt_attention_chunks(None, 1) == blt.BLT_EINVAL
+    assert L.blt_flash_key_groups(None, 2) == blt.BLT_EINVAL
+    assert L.blt_graphs_enable(None, 1) == blt.BLT_EINVAL
+    assert L.blt_profile_enable(None, 1) == blt.BLT_EINVAL
+    assert L.blt_session_device_blocks(None, 1) == blt.BLT_EINVAL
+    assert L.blt_session_destroy(None) == blt.BLT_EINVAL
