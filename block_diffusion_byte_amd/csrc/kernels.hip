@@ -35,6 +35,16 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
+// Device-resident passes gate every kernel on a count of sequences with
+// masks left (0: the kernel returns at once).  Each gated kernel has two
+// instantiations: GT launches with the gate pointer; the ungated one, for
+// host-driven passes, does not load it, so its first kernel-argument loads
+// are not held behind that pointer's (about 0.25 us per launch measured).
+template <bool GT> __device__ __forceinline__ bool gate_closed(const int32_t *gate) {
+  if constexpr (GT) return *gate == 0;
+  else return false;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -316,9 +326,9 @@ __device__ __forceinline__ uint4 stage_value(const StageRaw<BF, PRO> &st, uint4 
   }
 }
 
-template <bool BF, int G, int NC, int RB, int PRO>
+template <bool BF, int G, int NC, int RB, int PRO, bool GT>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
-  if (a.gate && *a.gate == 0) return;
+  if (gate_closed<GT>(a.gate)) return;
   constexpr int EPC = Act<BF>::EPC;
   constexpr int RPW = 64 / G;
   constexpr int Q = NC * G, KC = 4 * Q;      // chunks per wave quarter, per row
@@ -501,9 +511,9 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-template <int BM, int BN, int WM, int WN, int KH>
+template <int BM, int BN, int WM, int WN, int KH, bool GT>
 __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
-  if (a.gate && *a.gate == 0) return;
+  if (gate_closed<GT>(a.gate)) return;
   constexpr int NT = 512, P = 2;                    // threads; register slots of prefetched steps
   constexpr int CH = kGemmBK / 8;                   // 16-byte chunks per tile row
   constexpr int LA = BM * CH / NT, LB = BN * CH / NT;  // chunks per thread per step
@@ -675,10 +685,10 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
 // partials added in split order, as the product's own epilogue would.  Each
 // thread takes elements t + 256 i of blocks of 2048, every load of a block
 // issued before the first is used.
-template <bool BF, int SPLITS>
+template <bool BF, int SPLITS, bool GT>
 __global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, const void *gain,
                                                      int K, float eps, void *out, GemmArgs p) {
-  if (p.gate && *p.gate == 0) return;
+  if (gate_closed<GT>(p.gate)) return;
   using T = typename Act<BF>::T;
   constexpr int E = 8;                       // elements per thread and block
   constexpr int NS = SPLITS > 0 ? SPLITS : 1;
@@ -740,13 +750,13 @@ __global__ __launch_bounds__(256) void k_rmsnorm_act(float *H, int64_t ldh, cons
 
 // ---------------------------------------------------------------------------
 // h[r] = E[tok_r] + cross contribution of layer 0 for the row's latent.
-template <bool BF>
+template <bool BF, bool GT>
 __global__ __launch_bounds__(256) void k_embed(const void *embed, const float *cross,
                                                const RowDesc *rows, int d, int n_layers,
                                                int max_lat, const int32_t *block_tok,
                                                const int32_t *tokens_dev, float *h,
                                                const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   const int r = blockIdx.x;
   const RowDesc rd = rows[r];
@@ -762,11 +772,11 @@ __global__ __launch_bounds__(256) void k_embed(const void *embed, const float *c
 // RoPE on q and k at the row's absolute position (rotate-half pairs (j, j+dh/2),
 // angles from a float2 (cos, sin) table), q kept in f32, k and v written to the
 // cache row `pos` of the row's sequence.
-template <bool BF>
+template <bool BF, bool GT>
 __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc *rows,
                                                  const float2 *rope_tab, float *q_out, void *kvp,
                                                  KVGeom g, int layer, const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   const int r = blockIdx.x;
   const RowDesc rd = rows[r];
@@ -842,9 +852,9 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // the pass: the MFMA keeps rows apart and no order depends on the row count.
 // Its cost hardly grows with the row count (a cold pass of 1 to 9 rows at the
 // 1B-class shapes runs in the time of a plain read of the weights).
-template <int PRO, int SB>
+template <int PRO, int SB, bool GT>
 __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
-  if (a.gate && *a.gate == 0) return;
+  if (gate_closed<GT>(a.gate)) return;
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l & 15, lq = l >> 4;
   const int n0 = blockIdx.x * 16;
   const int kq = a.K / 4, steps = kq / 32;  // this wave's K range in 32-wide steps (a multiple of SB)
@@ -972,14 +982,14 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
 // eight waves in two groups that take alternate chunks (group 0 the even
 // ones), so one workgroup covers a (sequence, head) with twice the loads in
 // flight; their eight (o, m, l) are combined the same way.
-template <int DH, bool PIPE, int WG>
+template <int DH, bool PIPE, int WG, bool GT>
 __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
                                                         int layer, const SeqDesc *seqs,
                                                         const RowDesc *rows, float *part,
                                                         int max_chunks, int chunks_per_wg,
                                                         int direct, void *a_out, SeqDesc sd_arg,
                                                         int use_sd_arg, const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
   constexpr int NWV = 4 * WG;                 // waves
   constexpr int KS = DH / 32;                 // k-steps of the score product
@@ -1206,12 +1216,12 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
 // the row's statistics unchanged, whatever the other rows of the tile read.
 // Cache rows at or past the sequence's kmax are never written and are staged
 // as zeros.
-template <int DH, int KG>
+template <int DH, int KG, bool GT>
 __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const void *kvp, KVGeom g,
                                                     int layer, const SeqDesc *seqs,
                                                     const RowDesc *rows, void *a_out,
                                                     const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   constexpr int KS = DH / 32;                 // k-steps of the score product
   constexpr int DT = DH / 16;                 // 16-dim output tiles
   constexpr int KT = DH <= 64 ? 64 : 32;      // keys per LDS tile
@@ -1516,12 +1526,12 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
 // exchange), softmax statistics by 16-lane groups, P.V by (dim, key
 // partition) threads with the thread's V column (a row of the transposed V)
 // in registers.
-template <int DH>
+template <int DH, bool GT>
 __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kvp, KVGeom g,
                                                   int layer, const SeqDesc *seqs,
                                                   const RowDesc *rows, float *part,
                                                   int max_chunks, const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   constexpr int RG = 16;                              // rows per row group
   constexpr int ROWB = DH * 4;                        // bytes of one key row
   constexpr int LDB = ROWB + 16;                      // padded LDS row stride (bytes)
@@ -1689,11 +1699,11 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 // weighted by an exact 0), so the partial outputs of the first PRE chunks,
 // the statistics and the row descriptor are all in flight at once; chunks
 // past PRE follow 32 at a time.
-template <bool BF, int DH, int PRE>
+template <bool BF, int DH, int PRE, bool GT>
 __global__ __launch_bounds__(64) void k_attn_merge(const float *part, const RowDesc *rows,
                                                    int n_heads, int max_chunks, int gc, int ck,
                                                    void *a_out, const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   using T = typename Act<BF>::T;
   static_assert(PRE % 32 == 0 || PRE < 32, "later chunks go 32 at a time");
   constexpr int EPL = (DH + 63) / 64;       // output dims per lane
@@ -1806,12 +1816,13 @@ __device__ __forceinline__ void decide_row(int r, const float *logits, const Row
     for (int j = l; j < kVocab; j += 64) logits_out[(int64_t)oidx * kVocab + j] = z[j];
 }
 
+template <bool GT>
 __global__ __launch_bounds__(64) void k_decide(const float *logits, const RowDesc *rows,
                                                int32_t *argmax_ws, float *conf_ws, float *ent_ws,
                                                int report_entropy, int32_t *argmax_out,
                                                float *conf_out, float *logits_out,
                                                const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   decide_row(blockIdx.x, logits, rows, argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out,
              conf_out, logits_out);
 }
@@ -1851,13 +1862,14 @@ __device__ __forceinline__ float block_max256(float v, float *red) {
   return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
+template <bool GT>
 __global__ __launch_bounds__(256) void k_decide_sample(const float *logits, const RowDesc *rows,
                                                       int32_t *argmax_ws, float *conf_ws,
                                                       float *ent_ws, int report_entropy,
                                                       int32_t *argmax_out, float *conf_out,
                                                       float *logits_out, SampleArgs smp,
                                                       const int32_t *gate) {
-  if (gate && *gate == 0) return;   // device-resident pass with nothing left to do
+  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
   __shared__ float ew[256];
   __shared__ float red[4];
   __shared__ float pick_e;
@@ -1974,12 +1986,13 @@ __device__ __forceinline__ void unmask_seq(const SeqDesc &sd, const int32_t *arg
   }
 }
 
+template <bool GT>
 __global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_t *argmax_ws,
                                                const float *conf_ws, const float *ent_ws,
                                                int32_t *block_tok, float alpha, int mode,
                                                int32_t *masked_left, int32_t *gate,
                                                int32_t *pass_count) {
-  if (gate && *gate == 0) return;
+  if (gate_closed<GT>(gate)) return;
   unmask_seq(seqs[blockIdx.x], argmax_ws, conf_ws, ent_ws, block_tok, alpha, mode, masked_left,
              gate, pass_count);
 }
@@ -1987,6 +2000,7 @@ __global__ __launch_bounds__(64) void k_unmask(const SeqDesc *seqs, const int32_
 // Decisions and unmasking of a block pass in one launch: workgroup b takes
 // sequence b, its four waves decide the sequence's rows (row0 + w, + 4, ...)
 // exactly as k_decide does, then wave 0 unmasks its block.
+template <bool GT>
 __global__ __launch_bounds__(256) void k_decide_unmask(const float *logits, const SeqDesc *seqs,
                                                       const RowDesc *rows, int32_t *argmax_ws,
                                                       float *conf_ws, float *ent_ws,
@@ -1995,7 +2009,7 @@ __global__ __launch_bounds__(256) void k_decide_unmask(const float *logits, cons
                                                       int32_t *block_tok, float alpha, int mode,
                                                       int32_t *masked_left, int32_t *gate,
                                                       int32_t *pass_count) {
-  if (gate && *gate == 0) return;
+  if (gate_closed<GT>(gate)) return;
   const SeqDesc sd = seqs[blockIdx.x];
   const int w = threadIdx.x >> 6;
   for (int r = sd.row0 + w; r < sd.row0 + sd.nrows; r += 4)
@@ -2122,21 +2136,26 @@ hipError_t gemv_launch(const GemmArgs &a, hipStream_t s, hipEvent_t ev0, hipEven
   constexpr int KC = 4 * NC * G;
   if (a.K != KC * Act<BF>::EPC) return hipErrorInvalidValue;
   const size_t lds = (size_t)RB * KC * 16;
-  static bool attr = false;
-  if (!attr) {
+  const bool gt = a.gate != nullptr;
+  const void *fn = gt ? (const void *)k_gemv<BF, G, NC, RB, PRO, true>
+                      : (const void *)k_gemv<BF, G, NC, RB, PRO, false>;
+  static bool attr[2] = {false, false};
+  if (!attr[gt]) {
     // allow dynamic LDS up to the 160 KB of a gfx950 CU, less the static part
     hipFuncAttributes fa;
-    hipError_t e = hipFuncGetAttributes(&fa, (const void *)k_gemv<BF, G, NC, RB, PRO>);
+    hipError_t e = hipFuncGetAttributes(&fa, fn);
     if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute((const void *)k_gemv<BF, G, NC, RB, PRO>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize,
                             160 * 1024 - (int)fa.sharedSizeBytes);
     if (e != hipSuccess) return e;
-    attr = true;
+    attr[gt] = true;
   }
   constexpr int RPW = 64 / G;
-  hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO>), dim3((a.N + RPW - 1) / RPW), dim3(256), lds, s,
-                        ev0, ev1, 0, a);
+  const dim3 grid((a.N + RPW - 1) / RPW);
+  if (gt)
+    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, true>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
+  else
+    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, false>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
@@ -2229,15 +2248,18 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     if (bf16 && a.K <= 1536 && a.K % 128 == 0 && a.N >= 2048) {
       const int steps = a.K / 128;
       const dim3 g((a.N + 15) / 16);
-#define BLT_GEMV_MFMA(SB)                                                                        \
+#define BLT_GEMV_MFMA_GT(SB, GT)                                                                 \
   if (a.pro == PRO_NORM)                                                                         \
-    hipExtLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB>), g, dim3(256), 0, s, ev0, ev1, 0, a);      \
-  else hipExtLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB>), g, dim3(256), 0, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB, GT>), g, dim3(256), 0, s, ev0, ev1, 0, a);  \
+  else hipExtLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB, GT>), g, dim3(256), 0, s, ev0, ev1, 0, a);
+#define BLT_GEMV_MFMA(SB)                                                                        \
+  if (a.gate) { BLT_GEMV_MFMA_GT(SB, true) } else { BLT_GEMV_MFMA_GT(SB, false) }
       if (steps % 8 == 0) { BLT_GEMV_MFMA(8) }
       else if (steps % 4 == 0) { BLT_GEMV_MFMA(4) }
       else if (steps % 2 == 0) { BLT_GEMV_MFMA(2) }
       else { BLT_GEMV_MFMA(1) }
 #undef BLT_GEMV_MFMA
+#undef BLT_GEMV_MFMA_GT
       return hipGetLastError();
     }
     return bf16 ? gemv_dispatch<true>(a, s, ev0, ev1) : gemv_dispatch<false>(a, s, ev0, ev1);
@@ -2247,8 +2269,12 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     float *H = const_cast<float *>(a.H);
     const GemmArgs &pa = pending ? sr->a : a;
 #define BLT_NORM(SP)                                                                             \
-  hipLaunchKernelGGL((k_rmsnorm_act<true, SP>), dim3(a.R), dim3(256), 0, s, H, a.ldh, a.gain, a.K, \
-                     a.eps, xnorm_ws, pa);
+  if (pa.gate)                                                                                   \
+    hipLaunchKernelGGL((k_rmsnorm_act<true, SP, true>), dim3(a.R), dim3(256), 0, s, H, a.ldh,    \
+                       a.gain, a.K, a.eps, xnorm_ws, pa);                                        \
+  else                                                                                           \
+    hipLaunchKernelGGL((k_rmsnorm_act<true, SP, false>), dim3(a.R), dim3(256), 0, s, H, a.ldh,   \
+                       a.gain, a.K, a.eps, xnorm_ws, pa);
     switch (pending ? sr->splits : 0) {
       case 0: BLT_NORM(0) break;
       case 2: BLT_NORM(2) break;
@@ -2282,36 +2308,47 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
   // the batch-16, batch-64 and prefill shapes)
   const int t128 = ((a.R + 127) / 128) * ((a.N + 127) / 128);
   const int t64w = ((a.R + 63) / 64) * ((a.N + 127) / 128);
-  if (t128 * splits >= 176)
-    hipExtLaunchKernelGGL((k_gemm_mfma<128, 128, 2, 4, 1>), dim3(t128, splits), dim3(512), 0, s, ev0, ev1, 0, b);
-  else if (t64w * splits >= 150)
-    hipExtLaunchKernelGGL((k_gemm_mfma<64, 128, 2, 4, 1>), dim3(t64w, splits), dim3(512), 0, s, ev0, ev1, 0, b);
-  else
-    hipExtLaunchKernelGGL((k_gemm_mfma<64, 64, 2, 2, 2>), dim3(t64, splits), dim3(512), 0, s, ev0, ev1, 0, b);
+#define BLT_GEMM(BM, BN, WM, WN, KH, T)                                                           \
+  if (b.gate)                                                                                     \
+    hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, KH, true>), dim3(T, splits), dim3(512), 0, \
+                          s, ev0, ev1, 0, b);                                                     \
+  else                                                                                            \
+    hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, KH, false>), dim3(T, splits), dim3(512), 0, \
+                          s, ev0, ev1, 0, b);
+  if (t128 * splits >= 176) { BLT_GEMM(128, 128, 2, 4, 1, t128) }
+  else if (t64w * splits >= 150) { BLT_GEMM(64, 128, 2, 4, 1, t64w) }
+  else { BLT_GEMM(64, 64, 2, 2, 2, t64) }
+#undef BLT_GEMM
   return hipGetLastError();
 }
 
 hipError_t launch_embed(bool bf16, const void *embed, const float *cross, const RowDesc *rows,
                         int R, int d, int n_layers, int max_lat, const int32_t *block_tok,
                         const int32_t *tokens_dev, float *h, hipStream_t s, const int32_t *gate) {
-  if (bf16)
-    hipLaunchKernelGGL((k_embed<true>), dim3(R), dim3(256), 0, s, embed, cross, rows, d, n_layers,
-                       max_lat, block_tok, tokens_dev, h, gate);
-  else
-    hipLaunchKernelGGL((k_embed<false>), dim3(R), dim3(256), 0, s, embed, cross, rows, d, n_layers,
-                       max_lat, block_tok, tokens_dev, h, gate);
+#define BLT_EMBED(BF, GT)                                                                        \
+  hipLaunchKernelGGL((k_embed<BF, GT>), dim3(R), dim3(256), 0, s, embed, cross, rows, d, n_layers, \
+                     max_lat, block_tok, tokens_dev, h, gate);
+  if (bf16) {
+    if (gate) { BLT_EMBED(true, true) } else { BLT_EMBED(true, false) }
+  } else {
+    if (gate) { BLT_EMBED(false, true) } else { BLT_EMBED(false, false) }
+  }
+#undef BLT_EMBED
   return hipGetLastError();
 }
 
 hipError_t launch_rope_kv(bool bf16, const float *qkv, int R, const RowDesc *rows,
                           const float2 *rope_tab, float *q_out, void *kv, KVGeom g, int layer,
                           hipStream_t s, const int32_t *gate) {
-  if (bf16)
-    hipLaunchKernelGGL((k_rope_kv<true>), dim3(R), dim3(256), 0, s, qkv, rows, rope_tab, q_out, kv,
-                       g, layer, gate);
-  else
-    hipLaunchKernelGGL((k_rope_kv<false>), dim3(R), dim3(256), 0, s, qkv, rows, rope_tab, q_out, kv,
-                       g, layer, gate);
+#define BLT_ROPE(BF, GT)                                                                         \
+  hipLaunchKernelGGL((k_rope_kv<BF, GT>), dim3(R), dim3(256), 0, s, qkv, rows, rope_tab, q_out, kv, \
+                     g, layer, gate);
+  if (bf16) {
+    if (gate) { BLT_ROPE(true, true) } else { BLT_ROPE(true, false) }
+  } else {
+    if (gate) { BLT_ROPE(false, true) } else { BLT_ROPE(false, false) }
+  }
+#undef BLT_ROPE
   return hipGetLastError();
 }
 
@@ -2332,12 +2369,15 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
       // forces a form).
       const bool two = flash_kg ? flash_kg == 2 : (int64_t)fg.x * fg.y * fg.z <= 2048;
       hipEvent_t e0 = ev_flash ? ev0 : nullptr, e1 = ev_flash ? ev1 : nullptr;
-      if (two)
-        hipExtLaunchKernelGGL((k_attn_flash<DH, 2>), fg, dim3(512), 0, s, e0, e1, 0, q, kv, g, layer,
-                              seqs, rows, a_out, gate);
-      else
-        hipExtLaunchKernelGGL((k_attn_flash<DH, 1>), fg, dim3(256), 0, s, e0, e1, 0, q, kv, g, layer,
-                              seqs, rows, a_out, gate);
+#define BLT_FLASH(KG, GT)                                                                         \
+  hipExtLaunchKernelGGL((k_attn_flash<DH, KG, GT>), fg, dim3(256 * KG), 0, s, e0, e1, 0, q, kv, g, \
+                        layer, seqs, rows, a_out, gate);
+      if (two) {
+        if (gate) { BLT_FLASH(2, true) } else { BLT_FLASH(2, false) }
+      } else {
+        if (gate) { BLT_FLASH(1, true) } else { BLT_FLASH(1, false) }
+      }
+#undef BLT_FLASH
     }
   }
   if (ev_flash) ev0 = ev1 = nullptr;
@@ -2353,15 +2393,17 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
   const int use_sd_arg = sd_host && n_seq == 1;
   // with events: stamped by the dispatch itself at the kernel's start and end
   if constexpr (BF) {
-#define BLT_SPLITK(PIPE, WG)                                                                      \
+#define BLT_SPLITK_GT(PIPE, WG, GT)                                                               \
   if (ev0)                                                                                        \
-    hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, ev0, ev1, 0,   \
-                          q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out,     \
+    hipExtLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG, GT>), grid, dim3(256 * WG), 0, s, ev0, ev1, \
+                          0, q, kv, g, layer, seqs, rows, part, max_chunks, nsub, direct, a_out,  \
                           sd_arg, use_sd_arg, gate);                                              \
   else                                                                                            \
-    hipLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG>), grid, dim3(256 * WG), 0, s, q, kv, g, layer,  \
-                       seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg, use_sd_arg,     \
-                       gate);
+    hipLaunchKernelGGL((k_attn_mfma<DH, PIPE, WG, GT>), grid, dim3(256 * WG), 0, s, q, kv, g,     \
+                       layer, seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg,          \
+                       use_sd_arg, gate);
+#define BLT_SPLITK(PIPE, WG)                                                                      \
+  if (gate) { BLT_SPLITK_GT(PIPE, WG, true) } else { BLT_SPLITK_GT(PIPE, WG, false) }
     if constexpr (DH <= 64) {
       if (wg == 2) { BLT_SPLITK(true, 2) }
       else if (nsub > 1) { BLT_SPLITK(true, 1) }
@@ -2370,22 +2412,30 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
       BLT_SPLITK(false, 1)
     }
 #undef BLT_SPLITK
+#undef BLT_SPLITK_GT
   } else {
-    if (ev0)
-      hipExtLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g, layer,
-                            seqs, rows, part, max_chunks, gate);
-    else
-      hipLaunchKernelGGL((k_attn_f32<DH>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,
-                         part, max_chunks, gate);
+#define BLT_F32(GT)                                                                               \
+  if (ev0)                                                                                        \
+    hipExtLaunchKernelGGL((k_attn_f32<DH, GT>), grid, dim3(256), 0, s, ev0, ev1, 0, q, kv, g,     \
+                          layer, seqs, rows, part, max_chunks, gate);                             \
+  else                                                                                            \
+    hipLaunchKernelGGL((k_attn_f32<DH, GT>), grid, dim3(256), 0, s, q, kv, g, layer, seqs, rows,  \
+                       part, max_chunks, gate);
+    if (gate) { BLT_F32(true) } else { BLT_F32(false) }
+#undef BLT_F32
   }
   if (BF && direct) return;                 // no partials to merge
   // the merge takes its first 16 (or 64) chunks in one round of loads
-  if (gc <= 16)
-    hipLaunchKernelGGL((k_attn_merge<BF, DH, 16>), dim3(R, g.n_heads), dim3(64), 0, s, part, rows,
-                       g.n_heads, max_chunks, gc, kCK * nsub, a_out, gate);
-  else
-    hipLaunchKernelGGL((k_attn_merge<BF, DH, (DH > 64 ? 32 : 64)>), dim3(R, g.n_heads), dim3(64), 0,
-                       s, part, rows, g.n_heads, max_chunks, gc, kCK * nsub, a_out, gate);
+#define BLT_MERGE(PRE, GT)                                                                        \
+  hipLaunchKernelGGL((k_attn_merge<BF, DH, PRE, GT>), dim3(R, g.n_heads), dim3(64), 0, s, part,  \
+                     rows, g.n_heads, max_chunks, gc, kCK * nsub, a_out, gate);
+  constexpr int PRE_WIDE = DH > 64 ? 32 : 64;
+  if (gc <= 16) {
+    if (gate) { BLT_MERGE(16, true) } else { BLT_MERGE(16, false) }
+  } else {
+    if (gate) { BLT_MERGE(PRE_WIDE, true) } else { BLT_MERGE(PRE_WIDE, false) }
+  }
+#undef BLT_MERGE
 }
 
 hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g, int layer,
@@ -2415,12 +2465,19 @@ hipError_t launch_decide(const float *logits, int R, const RowDesc *rows, int32_
                          float *conf_ws, float *ent_ws, int report_entropy, int32_t *argmax_out,
                          float *conf_out, float *logits_out, const SampleArgs *smp, hipStream_t s,
                          const int32_t *gate) {
-  if (smp)
-    hipLaunchKernelGGL(k_decide_sample, dim3(R), dim3(256), 0, s, logits, rows, argmax_ws, conf_ws,
-                       ent_ws, report_entropy, argmax_out, conf_out, logits_out, *smp, gate);
-  else
-    hipLaunchKernelGGL(k_decide, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws, ent_ws,
-                       report_entropy, argmax_out, conf_out, logits_out, gate);
+#define BLT_DECIDE_SAMPLE(GT)                                                                     \
+  hipLaunchKernelGGL(k_decide_sample<GT>, dim3(R), dim3(256), 0, s, logits, rows, argmax_ws,      \
+                     conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, *smp, gate);
+#define BLT_DECIDE(GT)                                                                            \
+  hipLaunchKernelGGL(k_decide<GT>, dim3(R), dim3(64), 0, s, logits, rows, argmax_ws, conf_ws,     \
+                     ent_ws, report_entropy, argmax_out, conf_out, logits_out, gate);
+  if (smp) {
+    if (gate) { BLT_DECIDE_SAMPLE(true) } else { BLT_DECIDE_SAMPLE(false) }
+  } else {
+    if (gate) { BLT_DECIDE(true) } else { BLT_DECIDE(false) }
+  }
+#undef BLT_DECIDE_SAMPLE
+#undef BLT_DECIDE
   return hipGetLastError();
 }
 
@@ -2430,9 +2487,12 @@ hipError_t launch_decide_unmask(const float *logits, int n_seq, const SeqDesc *s
                                 float *conf_out, float *logits_out, int32_t *block_tok,
                                 float alpha, int mode, int32_t *masked_left, hipStream_t s,
                                 int32_t *gate, int32_t *pass_count) {
-  hipLaunchKernelGGL(k_decide_unmask, dim3(n_seq), dim3(256), 0, s, logits, seqs, rows, argmax_ws,
-                     conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, block_tok,
-                     alpha, mode, masked_left, gate, pass_count);
+#define BLT_DECIDE_UNMASK(GT)                                                                     \
+  hipLaunchKernelGGL(k_decide_unmask<GT>, dim3(n_seq), dim3(256), 0, s, logits, seqs, rows,       \
+                     argmax_ws, conf_ws, ent_ws, report_entropy, argmax_out, conf_out, logits_out, \
+                     block_tok, alpha, mode, masked_left, gate, pass_count);
+  if (gate) { BLT_DECIDE_UNMASK(true) } else { BLT_DECIDE_UNMASK(false) }
+#undef BLT_DECIDE_UNMASK
   return hipGetLastError();
 }
 
@@ -2460,8 +2520,11 @@ hipError_t launch_unmask(const SeqDesc *seqs, int n_seq, const int32_t *argmax_w
                          const float *conf_ws, const float *ent_ws, int32_t *block_tok, float alpha,
                          int mode, int32_t *masked_left, hipStream_t s, int32_t *gate,
                          int32_t *pass_count) {
-  hipLaunchKernelGGL(k_unmask, dim3(n_seq), dim3(64), 0, s, seqs, argmax_ws, conf_ws, ent_ws,
+#define BLT_UNMASK(GT)                                                                            \
+  hipLaunchKernelGGL(k_unmask<GT>, dim3(n_seq), dim3(64), 0, s, seqs, argmax_ws, conf_ws, ent_ws, \
                      block_tok, alpha, mode, masked_left, gate, pass_count);
+  if (gate) { BLT_UNMASK(true) } else { BLT_UNMASK(false) }
+#undef BLT_UNMASK
   return hipGetLastError();
 }
 
