@@ -82,6 +82,18 @@ struct KVGeom {
   int n_layers, n_heads, d_head, max_ctx;  // max_ctx: cache rows, kv_rows(cfg.max_ctx)
 };
 
+// Element offset of (key, dim) in a head's K plane.  The plane is cut into
+// tiles of kKTile keys, each stored [d_h / 32][kKTile][32]: one 32-dimension
+// slice of every key of the tile, then the next slice.  A bf16 128-byte line
+// then holds one slice of two consecutive keys, so the 16-byte pieces that
+// one attention load instruction takes (16 keys, one slice, four pieces per
+// key) cover whole lines, and streaming (non-temporal) loads fetch each line
+// once.  d_h is 32, 64 or 128 (checked at creation).
+constexpr int kKTile = 32;
+__host__ __device__ inline int64_t k_off(int key, int dim, int d_head) {
+  return ((int64_t)(key / kKTile) * d_head + (dim / 32) * kKTile) * 32 + (key % kKTile) * 32 + dim % 32;
+}
+
 // Element offset of (key, dim) in a head's V plane.  The plane is cut into
 // tiles of kVTile keys, each stored [d_h][kVTile]: the kVTile keys of every
 // dimension that one attention wave reads form a single contiguous block

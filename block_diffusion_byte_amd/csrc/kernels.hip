@@ -237,9 +237,8 @@ __device__ __forceinline__ void qkv_rope_store(const GemmArgs &a, int r, int i0,
   const int64_t head = (((int64_t)e.slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
   T *kv = (T *)a.kv;
   if (sec == 1) {
-    const int64_t base = head * plane + (int64_t)e.pos * a.d_head + j;
-    kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
-    kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
+    kv[head * plane + k_off(e.pos, j, a.d_head)] = from_f<T>(y0 * cs.x - y1 * cs.y);
+    kv[head * plane + k_off(e.pos, j + half, a.d_head)] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
     kv[head * plane + v_off(e.pos, j, a.d_head)] = from_f<T>(y0);
     kv[head * plane + v_off(e.pos, j + half, a.d_head)] = from_f<T>(y1);
@@ -266,9 +265,8 @@ __device__ __forceinline__ void qkv_rope_store_col(const GemmArgs &a, int r, int
   const int64_t head = (((int64_t)slot * a.n_layers + a.layer) * 2 + (sec - 1)) * a.n_heads + hh;
   T *kv = (T *)a.kv;
   if (sec == 1) {
-    const int64_t base = head * plane + (int64_t)pos * a.d_head + j;
-    kv[base] = from_f<T>(y0 * cs.x - y1 * cs.y);
-    kv[base + half] = from_f<T>(y1 * cs.x + y0 * cs.y);
+    kv[head * plane + k_off(pos, j, a.d_head)] = from_f<T>(y0 * cs.x - y1 * cs.y);
+    kv[head * plane + k_off(pos, j + half, a.d_head)] = from_f<T>(y1 * cs.x + y0 * cs.y);
   } else {
     kv[head * plane + v_off(pos, j, a.d_head)] = from_f<T>(y0);
     kv[head * plane + v_off(pos, j + half, a.d_head)] = from_f<T>(y1);
@@ -793,11 +791,10 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
     q_out[(int64_t)r * d + hi] = q2 * cs.x + q1 * cs.y;
     if (rd.keep_kv) continue;
     const float k1 = src[d + lo], k2 = src[d + hi];
-    const int64_t kb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + hh) * plane +
-                       (int64_t)rd.pos * dh;
+    const int64_t kb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + hh) * plane;
     const int64_t vb = ((((int64_t)rd.slot * g.n_layers + layer) * 2 + 1) * g.n_heads + hh) * plane;
-    kv[kb + j] = from_f<T>(k1 * cs.x - k2 * cs.y);
-    kv[kb + j + half] = from_f<T>(k2 * cs.x + k1 * cs.y);
+    kv[kb + k_off(rd.pos, j, dh)] = from_f<T>(k1 * cs.x - k2 * cs.y);
+    kv[kb + k_off(rd.pos, j + half, dh)] = from_f<T>(k2 * cs.x + k1 * cs.y);
     kv[vb + v_off(rd.pos, j, dh)] = from_f<T>(src[2 * d + lo]);
     kv[vb + v_off(rd.pos, j + half, dh)] = from_f<T>(src[2 * d + hi]);
   }
@@ -806,11 +803,14 @@ __global__ __launch_bounds__(256) void k_rope_kv(const float *qkv, const RowDesc
 // ---------------------------------------------------------------------------
 // Split-K attention partials.
 //
-// Cache layout per (sequence, layer, head): K as [position][d_head] and V
-// transposed in tiles of 32 positions, [max_ctx / 32][d_head][32] (v_off), so
-// that both products below read their operands straight from HBM with 8- or
-// 16-byte loads, and a wave's 32 keys of K and of V are each one contiguous
-// block.
+// Cache layout per (sequence, layer, head): K in tiles of 32 positions,
+// [max_ctx / 32][d_head / 32][32][32] (k_off: 32-dimension slices of the
+// tile's keys), and V transposed in tiles of 32 positions,
+// [max_ctx / 32][d_head][32] (v_off), so that both products below read
+// their operands straight from HBM with 16-byte loads that cover whole
+// 128-byte lines, and a wave's 32 keys of K and of V are each one
+// contiguous block.  The bf16 kernel streams both with non-temporal loads:
+// every line is read once per pass.
 //
 // Workgroup (chunk c, head h, sequence b) owns keys [c*128, c*128+128) of
 // that sequence, for every row of the sequence in the pass; row r reads keys
@@ -1023,14 +1023,16 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
   auto load = [&](int kw0, bf16x8_t (&ka)[2][KS], u32x4_t (&vg)[DT]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const uint16_t *kr = Kp + (int64_t)min(kw0 + 8 * (lr >> 2) + 4 * kt + (lr & 3), klast) * DH + 8 * lq;
+      const int key = min(kw0 + 8 * (lr >> 2) + 4 * kt + (lr & 3), klast);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[kt][ks] = *(const bf16x8_t *)(kr + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks)
+        ka[kt][ks] = __builtin_bit_cast(
+            bf16x8_t, __builtin_nontemporal_load((const u32x4_t *)(Kp + k_off(key, 32 * ks + 8 * lq, DH))));
     }
     const int va = min(kw0 + 8 * lq, klast & ~7);   // a group clamped here lies wholly past kmax
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      vg[dt] = *(const u32x4_t *)(Vt + v_off(va, 16 * dt + lr, DH));
+      vg[dt] = __builtin_nontemporal_load((const u32x4_t *)(Vt + v_off(va, 16 * dt + lr, DH)));
   };
   int nr = min(16, sd.nrows);
   float4 qf[KS][2];
@@ -1272,21 +1274,24 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
   // operand of a lane is one 16-byte piece.
   auto kperm = [](int k16, int m) { return 32 * (k16 >> 1) + 8 * (m >> 2) + 4 * (k16 & 1) + (m & 3); };
 
-  // staging: thread t moves NK 16-byte pieces of K ([key][dim]) and of V^T
-  // ([dim][key]) per tile; pieces past kmax become zeros.  V piece i is
+  // staging: thread t moves NK 16-byte pieces of K (stored [key][dim] in
+  // LDS) and of V^T ([dim][key]) per tile; pieces past kmax become zeros.  V piece i is
   // dimension vdim(i), keys 8 vpiece(i)..+8 of the tile: consecutive pieces
   // run through the V plane's memory in order (its 32-key tiles are
   // [dim][32 keys])
   auto vdim = [](int i) { return (i % (DH * 4)) >> 2; };
   auto vpiece = [](int i) { return 4 * (i / (DH * 4)) + (i & 3); };
+  // K piece i is the i-th 16-byte piece of the tile's K memory (whole 32-key
+  // tiles of k_off): key kkey(i), dimensions kdim(i)..+8
+  auto kkey = [](int i) { return 32 * (i / (4 * DH)) + (i % 128) / 4; };
+  auto kdim = [](int i) { return 32 * ((i % (4 * DH)) / 128) + 8 * (i % 4); };
   u32x4_t kr[NK], vr[NK];
   auto load = [&](int tk) {
     const int key0 = tk * KT;
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int i = t + 256 * j;
-      const int kk = i / (DH / 8), kp = i % (DH / 8);
-      kr[j] = *(const u32x4_t *)(Kp + (int64_t)(key0 + kk) * DH + 8 * kp);
+      kr[j] = *(const u32x4_t *)(Kp + (int64_t)key0 * DH + 8 * i);
       const int dd = vdim(i), vp = vpiece(i);
       vr[j] = *(const u32x4_t *)(Vt + v_off(key0 + 8 * vp, dd, DH));
     }
@@ -1297,8 +1302,7 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
 #pragma unroll
       for (int j = 0; j < NK; ++j) {
         const int i = t + 256 * j;
-        const int kk = i / (DH / 8), kp = i % (DH / 8);
-        *(u32x4_t *)(kt_s(kg, buf) + kk * KST + 8 * kp) = kr[j];
+        *(u32x4_t *)(kt_s(kg, buf) + kkey(i) * KST + kdim(i)) = kr[j];
         *(u32x4_t *)(vt_s(kg, buf) + vdim(i) * VST + 8 * vpiece(i)) = vr[j];
       }
       return;
@@ -1306,10 +1310,10 @@ __global__ __launch_bounds__(256 * KG) void k_attn_flash(const float *q, const v
 #pragma unroll
     for (int j = 0; j < NK; ++j) {
       const int i = t + 256 * j;
-      const int kk = i / (DH / 8), kp = i % (DH / 8);
+      const int kk = kkey(i);
       u32x4_t kv = kr[j];
       if (key0 + kk >= kmax) kv = u32x4_t{0u, 0u, 0u, 0u};
-      *(u32x4_t *)(kt_s(kg, buf) + kk * KST + 8 * kp) = kv;
+      *(u32x4_t *)(kt_s(kg, buf) + kk * KST + kdim(i)) = kv;
       const int dd = vdim(i), vp = vpiece(i);
       u32x4_t vv = vr[j];
       const int k0 = key0 + 8 * vp;
@@ -1554,7 +1558,6 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
   const int64_t plane = (int64_t)g.max_ctx * DH;
   const float *Kp = (const float *)kvp + ((((int64_t)sd.slot * g.n_layers + layer) * 2 + 0) * g.n_heads + h) * plane;
   const float *Vt = Kp + (int64_t)g.n_heads * plane;
-  const char *Kb = (const char *)(Kp + (int64_t)key0 * DH);
   const int nkeys = min(kCK, sd.kmax - key0);
 
   int nr = min(RG, sd.nrows);
@@ -1569,7 +1572,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
-    kr[u] = *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
+    kr[u] = *(const uint4 *)(Kp + k_off(key0 + min(key, nkeys - 1), 4 * cc, DH));   // 4 floats
   }
   const int kk = t >> 1, hf = t & 1;                  // score phase: key kk, half hf
   const int e = t % DH, kp = t / DH;                  // P.V phase: dim e, partition kp
@@ -1687,7 +1690,7 @@ __global__ __launch_bounds__(256) void k_attn_f32(const float *q, const void *kv
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int idx = t + u * 256, key = idx / CPR, cc = idx - key * CPR;
-      *(uint4 *)(ks + key * LDB + cc * 16) = *(const uint4 *)(Kb + (int64_t)min(key, nkeys - 1) * ROWB + cc * 16);
+      *(uint4 *)(ks + key * LDB + cc * 16) = *(const uint4 *)(Kp + k_off(key0 + min(key, nkeys - 1), 4 * cc, DH));
     }
     __syncthreads();
   }

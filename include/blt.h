@@ -112,9 +112,11 @@ typedef struct {
 
 /* Caller-owned decode state (device), sized by blt_state_size:
  *   kv    : keys (after RoPE) and values of cached rows, per
- *           [max_batch][n_layers] a K plane [n_heads][ctx][d_model/n_heads]
- *           and a V plane [n_heads][ctx/32][d_model/n_heads][32] (V
- *           transposed in tiles of 32 positions), dtype, with ctx = max_ctx
+ *           [max_batch][n_layers] a K plane [n_heads][ctx/32][d_h/32][32][32]
+ *           (tiles of 32 positions, each holding the tile's keys one
+ *           32-dimension slice at a time) and a V plane
+ *           [n_heads][ctx/32][d_h][32] (V transposed in tiles of 32
+ *           positions), dtype, with d_h = d_model/n_heads and ctx = max_ctx
  *           rounded up to a multiple of 128;
  *   cross : per-latent cross-attention contributions W_o^c W_v^c W_lat o_m,
  *           [max_batch][max_latents][n_layers][d_model], float32.
