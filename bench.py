@@ -86,6 +86,9 @@ def parse():
                          "no CPU baseline (the program that hardware-counter runs profile)")
     ap.add_argument("--no-graphs", action="store_true",
                     help="launch every decoder pass directly instead of replaying HIP graphs")
+    ap.add_argument("--gemm-form", type=int, default=0, choices=(0, 1, 2),
+                    help="MFMA GEMM kernel of passes of 16 rows or more: 0 by shape, 1 staged "
+                         "operand tiles, 2 streamed weights (blt_gemm_form)")
     return ap.parse_args()
 
 
@@ -109,7 +112,7 @@ FAMILIES = {
 
 
 def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_report=False,
-            device_blocks=False, compare=False):
+            device_blocks=False, compare=False, gemm_form=0):
     """Time `steps` generations of workload `wl` (after `warmup` untimed ones),
     then one event-timed generation per kernel family.  device_blocks: BLT-D
     blocks after the first run on the device (blt_session_device_blocks);
@@ -128,6 +131,7 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
     del w
     if no_graphs:
         blt.blt_graphs_enable(dec.ctx, False)
+    blt.blt_gemm_form(dec.ctx, gemm_form)
     table = torch.empty((wl.batch, wl.n_latents, wl.d_global), dtype=dec.torch_dtype, device=dev)
     for b, inp in enumerate(inps):
         table[b].copy_(torch.from_numpy(inp["latents"]))
@@ -356,7 +360,7 @@ def main():
     fams = [] if args.no_prof else (small if wl.batch * (wl.block + 1) < 16 else ["k_attn_mfma", "k_gemm_mfma"])
     main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs,
                        prefill_report=not args.plain, device_blocks=args.device_blocks,
-                       compare=not args.plain)
+                       compare=not args.plain, gemm_form=args.gemm_form)
     out = {
         "metric": "decoded bytes/sec",
         "value": main_leg["value"],
@@ -381,10 +385,11 @@ def main():
     if not args.no_legs and args.workload == 1:
         legs = {}
         legs["batch64"] = run_leg(blt, torch, bltgen.WORKLOADS[4], 1, 1,
-                                  [] if args.no_prof else ["k_attn_mfma", "k_gemm_mfma"], args.no_graphs)
+                                  [] if args.no_prof else ["k_attn_mfma", "k_gemm_mfma"], args.no_graphs,
+                                  gemm_form=args.gemm_form)
         legs["peaked"] = run_leg(blt, torch, wl.replace(head_scale=12.0), max(1, args.steps // 2), 1,
                                  [] if args.no_prof else ["k_attn_mfma"], args.no_graphs,
-                                 device_blocks=args.device_blocks, compare=True)
+                                 device_blocks=args.device_blocks, compare=True, gemm_form=args.gemm_form)
         out["legs"] = legs
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_bytes, max(1, args.cpu_bytes // 2))

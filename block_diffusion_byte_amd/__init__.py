@@ -42,7 +42,7 @@ EXPORTS = [
     "blt_session_create", "blt_session_prefill", "blt_session_generate", "blt_session_result",
     "blt_session_destroy", "blt_profile_enable", "blt_profile_read", "blt_graphs_enable",
     "blt_attention_chunks", "blt_kv_append_noalloc", "blt_session_device_blocks",
-    "blt_flash_key_groups",
+    "blt_flash_key_groups", "blt_gemm_form",
 ]
 
 
@@ -129,6 +129,7 @@ def lib():
             "blt_graphs_enable": [P, I32],
             "blt_attention_chunks": [P, I32],
             "blt_flash_key_groups": [P, I32],
+            "blt_gemm_form": [P, I32],
         }
         for name, args in sig.items():
             f = getattr(L, name)
@@ -283,6 +284,10 @@ def blt_attention_chunks(ctx, chunks):
 
 def blt_flash_key_groups(ctx, groups):
     _check("blt_flash_key_groups", lib().blt_flash_key_groups(ctx, groups), ctx)
+
+
+def blt_gemm_form(ctx, form):
+    _check("blt_gemm_form", lib().blt_gemm_form(ctx, form), ctx)
 
 
 def blt_profile_enable(ctx, family):

@@ -250,7 +250,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
     }
     GemmArgs ag = a;
     ag.gate = p.gate;
-    HIP_TRY(c, launch_gemm(bf, ag, w.xb, &c->split, s, e0, e1));
+    HIP_TRY(c, launch_gemm(bf, ag, w.xb, &c->split, s, e0, e1, c->gemm_form));
     return BLT_OK;
   };
 #define BLT_GEMM_TRY(a)                 \
@@ -260,11 +260,12 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
   } while (0)
   for (int l = 0; l < L; ++l) {
     const blt_layer_weights &lw = c->layers[l];
+    const blt_ctx::FragLayer *fl = c->frag ? &c->frag_layers[l] : nullptr;
     GemmArgs a = base_args(c);
     a.R = R;
     a.rows = w.rows;
     // q, k, v = W_qkv RMSNorm(h)
-    a.W = lw.wqkv; a.N = 3 * d; a.K = d;
+    a.W = lw.wqkv; a.Wf = fl ? fl->wqkv : nullptr; a.N = 3 * d; a.K = d;
     a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = lw.g_attn;
     a.ep = EP_STORE_F32; a.out_f32 = w.qkv; a.ldo = 3 * d;
     // RoPE and the KV write happen in the projection's epilogue (on the
@@ -290,19 +291,19 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
                                 c->flash_kg));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = w.rows;
-    a.W = lw.wo; a.N = d; a.K = d;
+    a.W = lw.wo; a.Wf = fl ? fl->wo : nullptr; a.N = d; a.K = d;
     a.pro = PRO_PLAIN; a.X = w.xa; a.ldx = d;
     a.ep = EP_RESID; a.resid = w.h; a.ldo = d;
     BLT_GEMM_TRY(a);
     // f = SiLU(W1 RMSNorm(h))
     a = base_args(c); a.R = R; a.rows = w.rows;
-    a.W = lw.w1; a.N = F; a.K = d;
+    a.W = lw.w1; a.Wf = fl ? fl->w1 : nullptr; a.N = F; a.K = d;
     a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = lw.g_ffn;
     a.ep = EP_SILU_ACT; a.out_act = w.xa; a.ldo = F;
     BLT_GEMM_TRY(a);
     // h += W2 f (+ the next layer's cross-attention contribution)
     a = base_args(c); a.R = R; a.rows = w.rows;
-    a.W = lw.w2; a.N = d; a.K = F;
+    a.W = lw.w2; a.Wf = fl ? fl->w2 : nullptr; a.N = d; a.K = F;
     a.pro = PRO_PLAIN; a.X = w.xa; a.ldx = F;
     a.ep = EP_RESID; a.resid = w.h; a.ldo = d;
     if (l + 1 < L) { a.cross = cross; a.cross_layer = l + 1; }
@@ -310,7 +311,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
   }
   GemmArgs a = base_args(c);
   a.R = R; a.rows = w.rows;
-  a.W = c->w.w_out; a.N = kVocab; a.K = d;
+  a.W = c->w.w_out; a.Wf = c->frag_out; a.N = kVocab; a.K = d;
   a.pro = PRO_NORM; a.H = w.h; a.ldh = d; a.gain = c->w.g_out;
   a.ep = EP_STORE_F32; a.out_f32 = w.logits; a.ldo = kVocab;
   BLT_GEMM_TRY(a);
@@ -461,15 +462,15 @@ blt_status latents_from_device(blt_ctx *c, const blt_state *st, int m, const int
   if (m > g.max_rows) return fail(c, BLT_ECAPACITY, "latents_from_device: more latents than max_rows");
   const int d = g.d_model, L = g.n_layers;
   GemmArgs a = base_args(c);
-  a.R = m; a.W = c->w.w_lat; a.N = d; a.K = g.d_global;
+  a.R = m; a.W = c->w.w_lat; a.Wf = c->frag_lat; a.N = d; a.K = g.d_global;
   a.pro = PRO_PLAIN; a.X = table; a.x_row_off = offs;
   a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
-  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s));
+  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s, nullptr, nullptr, c->gemm_form));
   a = base_args(c);
-  a.R = m; a.W = c->cross_w; a.N = L * d; a.K = d;
+  a.R = m; a.W = c->cross_w; a.Wf = c->frag_cross; a.N = L * d; a.K = d;
   a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
   a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = offs + m;
-  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s));
+  HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, s, nullptr, nullptr, c->gemm_form));
   return BLT_OK;
 }
 
@@ -582,10 +583,47 @@ blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_str
       a.R = d; a.W = tmp; a.N = d; a.K = d;
       a.pro = PRO_PLAIN; a.X = lw.wo_c; a.ldx = d;
       a.ep = EP_STORE_ACT; a.out_act = (char *)c->cross_w + (size_t)l * d * d * e; a.ldo = d;
-      chk(launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
+      chk(launch_gemm(c->bf16, a, c->xb, nullptr, c->stream, nullptr, nullptr, c->gemm_form));
     }
     chk(hipStreamSynchronize(c->stream));
     if (tmp) (void)hipFree(tmp);
+  }
+  if (he == hipSuccess && c->bf16 && cfg->max_rows >= kGemvRows) {
+    // Fragment-ordered copies of the projection weights, read by the
+    // weight-streaming GEMM of passes of 16 rows or more (an extra 2 bytes
+    // per parameter of the decoder, W_lat and C)
+    const int L = cfg->n_layers, F = cfg->d_ffn, dg = cfg->d_global;
+    struct Job {
+      const void *src;
+      int N, K;
+      const void **dst;
+    };
+    std::vector<Job> jobs;
+    c->frag_layers.assign(L, blt_ctx::FragLayer{});
+    for (int l = 0; l < L; ++l) {
+      const blt_layer_weights &lw = c->layers[l];
+      blt_ctx::FragLayer &fl = c->frag_layers[l];
+      jobs.push_back({lw.wqkv, 3 * d, d, &fl.wqkv});
+      jobs.push_back({lw.wo, d, d, &fl.wo});
+      jobs.push_back({lw.w1, F, d, &fl.w1});
+      jobs.push_back({lw.w2, d, F, &fl.w2});
+    }
+    jobs.push_back({c->w.w_out, kVocab, d, &c->frag_out});
+    jobs.push_back({c->w.w_lat, d, dg, &c->frag_lat});
+    jobs.push_back({c->cross_w, L * d, d, &c->frag_cross});
+    size_t total = 0;
+    for (const Job &j : jobs)
+      if (j.K % 32 == 0) total += frag_elems(j.N, j.K);
+    chk(hipMalloc(&c->frag, total * e));
+    size_t off = 0;
+    for (const Job &j : jobs) {
+      if (he != hipSuccess || j.K % 32) continue;
+      void *dst = (char *)c->frag + off * e;
+      chk(launch_frag_pack(j.src, j.N, j.K, dst, c->stream));
+      *j.dst = dst;
+      off += frag_elems(j.N, j.K);
+    }
+    chk(hipStreamSynchronize(c->stream));
   }
   if (he != hipSuccess) {
     blt_destroy(c);
@@ -601,7 +639,7 @@ blt_status blt_destroy(blt_ctx *c) {
   drop_graphs(c);
   if (c->cap_stream) (void)hipStreamDestroy(c->cap_stream);
   void *bufs[] = {c->h, c->qkv, c->q, c->part, c->logits, c->split.ws, c->conf_ws, c->ent_ws, c->argmax_ws,
-                  c->xa, c->xb, c->desc_d, c->rope_tab, c->cross_w};
+                  c->xa, c->xb, c->desc_d, c->rope_tab, c->cross_w, c->frag};
   for (void *p : bufs)
     if (p) (void)hipFree(p);
   for (int i = 0; i < kRing; ++i) {
@@ -641,16 +679,16 @@ blt_status blt_latents_put(blt_ctx *c, const blt_state *st, int32_t n, const int
     if (bs != BLT_OK) return bs;
     // o~ = W_lat o  -> xb
     GemmArgs a = base_args(c);
-    a.R = m; a.W = c->w.w_lat; a.N = d; a.K = g.d_global;
+    a.R = m; a.W = c->w.w_lat; a.Wf = c->frag_lat; a.N = d; a.K = g.d_global;
     a.pro = PRO_PLAIN; a.X = table; a.x_row_off = c->offs_d;
     a.ep = EP_STORE_ACT; a.out_act = c->xb; a.ldo = d;
-    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream, nullptr, nullptr, c->gemm_form));
     // cross[slot][idx][l][:] = C_l o~ for every layer at once (N = L*d)
     a = base_args(c);
-    a.R = m; a.W = c->cross_w; a.N = L * d; a.K = d;
+    a.R = m; a.W = c->cross_w; a.Wf = c->frag_cross; a.N = L * d; a.K = d;
     a.pro = PRO_PLAIN; a.X = c->xb; a.ldx = d;
     a.ep = EP_ROWOFF_F32; a.out_f32 = (float *)st->cross; a.row_off = c->offs_d + m;
-    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream));
+    HIP_TRY(c, launch_gemm(c->bf16, a, c->xb, nullptr, c->stream, nullptr, nullptr, c->gemm_form));
   }
   return BLT_OK;
 }
@@ -934,6 +972,14 @@ blt_status blt_flash_key_groups(blt_ctx *c, int32_t groups) {
   if (groups < 0 || groups > 2) return fail(c, BLT_EINVAL, "blt_flash_key_groups: groups must be 0, 1 or 2");
   if (groups != c->flash_kg) drop_graphs(c);   // captured passes keep the form they were captured with
   c->flash_kg = groups;
+  return BLT_OK;
+}
+
+blt_status blt_gemm_form(blt_ctx *c, int32_t form) {
+  if (!c) return BLT_EINVAL;
+  if (form < 0 || form > 2) return fail(c, BLT_EINVAL, "blt_gemm_form: form must be 0, 1 or 2");
+  if (form != c->gemm_form) drop_graphs(c);   // captured passes keep the kernels they were captured with
+  c->gemm_form = form;
   return BLT_OK;
 }
 

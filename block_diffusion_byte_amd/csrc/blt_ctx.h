@@ -71,6 +71,15 @@ struct blt_ctx {
   void *xa = nullptr;         // GEMM activations [R][max(d, F)]
   void *xb = nullptr;         // GEMM activations [R][max(d, d_global)]
   void *cross_w = nullptr;    // [L*d][d]: W_o^c_l W_v^c_l of every layer, stacked (set-up)
+  // bf16 projection weights in fragment order for the weight-streaming GEMM
+  // of passes of 16 rows or more (one allocation, made at set-up; null when
+  // no pass can reach 16 rows): per layer, the byte head, W_lat and C
+  struct FragLayer {
+    const void *wqkv = nullptr, *wo = nullptr, *w1 = nullptr, *w2 = nullptr;
+  };
+  void *frag = nullptr;
+  std::vector<FragLayer> frag_layers;
+  const void *frag_out = nullptr, *frag_lat = nullptr, *frag_cross = nullptr;
   void *desc_d = nullptr;      // per-pass descriptors: sequences, rows, row offsets
   blt::SeqDesc *seqs_d = nullptr;
   blt::RowDesc *rows_d = nullptr;
@@ -87,6 +96,8 @@ struct blt_ctx {
   int attn_chunks = 0;
   // key groups of the causal attention kernel forced by blt_flash_key_groups (0: per pass)
   int flash_kg = 0;
+  // MFMA GEMM kernel forced by blt_gemm_form (0: by shape)
+  int gemm_form = 0;
   hipStream_t cap_stream = nullptr;
   std::unordered_map<blt::PassKey, blt::GraphEntry, blt::PassKeyHash> graph_cache;
   // profiling: family being timed, event pool, pending and accumulated figures

@@ -38,6 +38,7 @@ enum Prologue { PRO_PLAIN = 0, PRO_NORM = 1 };
 // y[r][o] = sum_i W[o][i] * x[r][i] for r < R, o < N.
 struct GemmArgs {
   const void *W;
+  const void *Wf;          // W in fragment order (launch_frag_pack; nullable): the weight-streaming GEMM
   int N, K;
   int R;
   int pro;
@@ -155,8 +156,12 @@ struct SplitResid {
 // normalised activations of the MFMA path.
 // ev0/ev1 (nullable): stamped by the dispatch of the product kernel itself
 // (not of the RMSNorm launch that precedes an MFMA GEMM with a norm prologue).
+// form: 0 chooses the MFMA GEMM kernel by shape (the weight-streaming kernel
+// where the staged-tile kernel's 128x128 tiles would be too few, at most
+// 1024 rows), 1 forces the staged-tile kernel, 2 the weight-streaming kernel
+// wherever it applies.
 hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr, hipStream_t s,
-                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr);
+                       hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, int form = 0);
 enum GemmKind { GEMM_KIND_GEMV_MFMA = 0, GEMM_KIND_GEMV = 1, GEMM_KIND_MFMA = 2 };
 GemmKind gemm_kind(bool bf16, const GemmArgs &a);
 // gate (nullable, every launcher below): see GemmArgs::gate.
@@ -217,6 +222,10 @@ hipError_t launch_verify_sample(int batch, const SeqDesc *seqs, const int64_t *d
                                 int32_t *accept_len, int32_t *next_byte, hipStream_t s);
 // dst = src^T, n x n elements of the context's dtype (set-up only).
 hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStream_t s);
+// bf16 W[N][K] -> its fragment order for the weight-streaming GEMM
+// (frag_elems(N, K) elements: rows padded to a multiple of 16 with zeros).
+size_t frag_elems(int N, int K);
+hipError_t launch_frag_pack(const void *src, int N, int K, void *dst, hipStream_t s);
 hipError_t launch_verify(int batch, const SeqDesc *seqs, int r, const int32_t *draft,
                          int ld_draft, const int32_t *pred, int ld_pred, int32_t *accept_len,
                          int32_t *next_byte, hipStream_t s);

@@ -677,6 +677,174 @@ __global__ __launch_bounds__(512) void k_gemm_mfma(GemmArgs a) {
       }
 }
 
+// ---------------------------------------------------------------------------
+// Weight-streaming MFMA GEMM for decode passes (16 to 1024 rows):
+// Y[R][N] = X[R][K] W[N][K]^T, bf16 x bf16 -> f32.
+//
+// A workgroup of 4 waves takes a 16*TM-row x 64*TN-column tile; wave w owns
+// columns [16*TN*w, 16*TN*(w+1)) of it over all 16*TM rows, so every weight
+// fragment is used by exactly one wave and is loaded straight from memory
+// into the B-operand registers (lane l: column l%16, the 8 consecutive k of
+// group l/16), PB 64-wide K steps ahead of the MFMAs that use them, from a
+// copy of the weights in fragment order (`k_frag_pack`) where each wave's
+// load instruction covers 1 KB of consecutive memory.  Only the
+// activations, which all four waves use, go through LDS: chunks of KCS K
+// steps, two buffers, rows padded by 16 bytes (the 16 lanes that read one
+// k-piece of 16 rows hit distinct banks), one barrier per chunk; the next
+// chunk's activations are loaded into registers while the current one is
+// computed.  Each output element is one fixed-order chain of MFMAs over its
+// K range; split-K (gridDim.y > 1) writes partial products as the staged-tile
+// kernel does.  Workgroups of one XCD take consecutive tiles, row tiles
+// fastest, so the row tiles of a column tile share its weights in that XCD's
+// L2.  Launched as 64x64 tiles with four steps in flight and two-step chunks
+// (170 registers, 35 KB of LDS: three workgroups per CU).  Measured at 576
+// rows (batch-64 decode): the L2 serves about 85% of the requests and the
+// weights are fetched from HBM about once, so these products are bound by how
+// fast the L2 delivers re-read tiles to the CUs, which grows with the
+// workgroups resident per CU (3.5 TB/s with one 64x256 tile per CU, 7-9
+// TB/s with two or three 64x64 tiles); wider tiles (64x128, 64x256), deeper
+// prefetch (8 steps) and four-step chunks were slower.  In row-major weight
+// order (each load instruction half of 16 lines) it ran about 2x slower.
+template <int TM, int TN, int PB, int KCS, bool GT>
+__global__ __launch_bounds__(256) void k_gemm_bs(GemmArgs a) {
+  if (gate_closed<GT>(a.gate)) return;
+  constexpr int NT = 256, BM = 16 * TM, BN = 64 * TN;
+  constexpr int CP = KCS * 8;                  // 16-byte k-pieces per row of a chunk
+  constexpr int PR = CP + 1;                   // LDS row pitch in pieces (one of padding)
+  constexpr int LA = BM * CP / NT;             // chunk pieces loaded per thread
+  constexpr int ABUF = BM * PR;                // pieces per chunk buffer
+  constexpr int SMEM = (2 * ABUF * 16 > BM * BN * 4 ? 2 * ABUF * 16 : BM * BN * 4) / 16;
+  static_assert(PB % KCS == 0 && (BM * CP) % NT == 0 && LA >= 1, "tile shape");
+  __shared__ __align__(16) u32x4_t smem[SMEM];
+  const int t = threadIdx.x, w = t >> 6, l = t & 63;
+  const int mt = (a.R + BM - 1) / BM, nt = (a.N + BN - 1) / BN, ntiles = mt * nt;
+  const int xcd = (int)blockIdx.x & 7;
+  const int tile = xcd * (ntiles >> 3) + min(xcd, ntiles & 7) + ((int)blockIdx.x >> 3);
+  const int m0 = (tile % mt) * BM, n0 = (tile / mt) * BN;
+  const int nk = a.K / kGemmBK / (int)gridDim.y;   // a multiple of PB (checked at launch)
+  const int nch = nk / KCS;
+  const int64_t k0 = (int64_t)blockIdx.y * nk * kGemmBK;
+  const uint16_t *X = (const uint16_t *)a.X + k0;
+  // chunk piece q = t + NT i of this thread: row q / CP, piece q % CP;
+  // rows past the matrix edge re-read its last row (their results are dropped)
+  const uint16_t *ga[LA];
+  int sla[LA];
+#pragma unroll
+  for (int i = 0; i < LA; ++i) {
+    const int q = t + NT * i, r = q / CP, p = q % CP, rr = min(m0 + r, a.R - 1);
+    ga[i] = X + (a.x_row_off ? a.x_row_off[rr] : (int64_t)rr * a.ldx) + p * 8;
+    sla[i] = r * PR + p;
+  }
+  // weights in fragment order (a.Wf): the B operand of column block ct and
+  // 32-deep k block kb is the 1 KB at ((ct * K/32 + kb) * 64) * 8 elements;
+  // blocks past the matrix edge re-read its last block
+  const int wc = w * 16 * TN, nct = (a.N + 15) / 16;
+  const uint16_t *gb[TN];
+#pragma unroll
+  for (int j = 0; j < TN; ++j) {
+    const int ct = min((n0 + wc) / 16 + j, nct - 1);
+    gb[j] = (const uint16_t *)a.Wf + ((int64_t)ct * (a.K / 32) + k0 / 32) * 512 + l * 8;
+  }
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  u32x4_t ra[LA];                              // the next chunk's activations
+  u32x4_t rb[PB][TN][2];                       // weights of steps kt .. kt+PB-1, slot kt % PB
+
+  auto load_a = [&](int c) {
+    c = min(c, nch - 1);                       // past the end: harmless re-reads
+    static_for<0, LA>([&](auto i) { ra[i] = *(const u32x4_t *)(ga[i] + (int64_t)c * KCS * kGemmBK); });
+  };
+  auto store_a = [&](int buf) {
+    static_for<0, LA>([&](auto i) { smem[buf * ABUF + sla[i]] = ra[i]; });
+  };
+  auto load_b = [&](auto slot, int kt) {
+    kt = min(kt, nk - 1);
+    static_for<0, TN>([&](auto j) {
+      rb[slot][j][0] = *(const u32x4_t *)(gb[j] + (int64_t)kt * 1024);
+      rb[slot][j][1] = *(const u32x4_t *)(gb[j] + (int64_t)kt * 1024 + 512);
+    });
+  };
+  auto compute = [&](int buf, int s, auto slot) {
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      bf16x8_t af[TM];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = __builtin_bit_cast(bf16x8_t, smem[buf * ABUF + (16 * i + (l & 15)) * PR + s * 8 + ss * 4 + (l >> 4)]);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              af[i], __builtin_bit_cast(bf16x8_t, rb[slot][j][ss]), acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // chunk 0's activations first, so staging them waits for nothing else
+  load_a(0);
+  static_for<0, PB>([&](auto j) { load_b(j, decltype(j)::value); });
+  store_a(0);
+  load_a(1);
+  __syncthreads();
+  for (int kt0 = 0; kt0 < nk; kt0 += PB) {
+    static_for<0, PB>([&](auto j) {
+      constexpr int s = decltype(j)::value;
+      const int c = kt0 / KCS + s / KCS;       // chunk of step kt0 + s
+      compute(c & 1, s % KCS, j);
+      load_b(j, kt0 + s + PB);
+      if constexpr (s % KCS == KCS - 1) {
+        // chunk c is done: chunk c+1 goes to the other buffer (last read by
+        // chunk c-1, before the previous barrier), chunk c+2 is fetched
+        store_a((c + 1) & 1);
+        load_a(c + 2);
+        __syncthreads();
+      }
+    });
+  }
+  // acc[i][j][v]: row 16i+4(l/16)+v, column wc+16j+l%16 of the tile
+  if (a.qkv_rope) {
+    // QKV projection with RoPE and the KV write through an f32 tile in LDS
+    // (the tile's columns start on a head boundary: BN is a multiple of d_h)
+    float *ct = reinterpret_cast<float *>(smem);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ct[(i * 16 + 4 * (l >> 4) + v) * BN + wc + j * 16 + (l & 15)] = acc[i][j][v];
+    __syncthreads();
+    const int half = a.d_head >> 1;
+    for (int it = t; it < BM * (BN / 2); it += NT) {
+      const int rr = it / (BN / 2), pc = it - rr * (BN / 2);
+      const int c = (pc / half) * a.d_head + pc % half;   // first column of the pair
+      const int m = m0 + rr, n = n0 + c;
+      if (m >= a.R || n >= a.N) continue;
+      const RowDesc rd = a.rows[m];
+      qkv_rope_store_col<true>(a, m, n, ct[rr * BN + c], ct[rr * BN + c + half], rd.pos, rd.slot,
+                               a.rope_tab[(int64_t)rd.pos * half + (n % a.d_head)], rd.keep_kv);
+    }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int m = m0 + i * 16 + 4 * (l >> 4) + v;
+        const int n = n0 + wc + j * 16 + (l & 15);
+        if (m >= a.R || n >= a.N) continue;
+        if (a.ep == EP_PART)                 // this split's partial product
+          a.out_f32[((int64_t)blockIdx.y * a.R + m) * a.N + n] = acc[i][j][v];
+        else
+          epilogue<true>(a, m, n, acc[i][j][v],
+                         a.ep == EP_RESID ? resid_operands(a, m, n) : ResidEpi{0.f, 0.f});
+      }
+}
+
 // RMSNorm rows into an activation buffer (MFMA path prologue).  SPLITS > 0:
 // a split-K residual product is pending (partial products p.out_f32[split][R][K],
 // its cross term per p.cross): the row first takes h += (sum + cross), the
@@ -2231,8 +2399,25 @@ GemmKind gemm_kind(bool bf16, const GemmArgs &a) {
   return GEMM_KIND_MFMA;
 }
 
+// K splits of a product on the weight-streaming GEMM (64x64 tiles, four K
+// steps of weights in flight): a residual product takes the fewest that give
+// at least 400 workgroups, within the partials' workspace; 0 where the kernel
+// does not apply (no fragment-ordered weights, over 1024 rows unless forced,
+// K splits not in whole groups of four steps).
+static int bs_splits(const GemmArgs &a, bool may_split, size_t cap, bool forced) {
+  if (!a.Wf || (a.R > 1024 && !forced) || a.K % (4 * kGemmBK)) return 0;
+  const int tiles = ((a.R + 63) / 64) * ((a.N + 63) / 64);
+  int best = 1;
+  for (int sp = 2; sp <= (may_split ? 8 : 1) && tiles * best < 400; ++sp) {
+    if (a.K % (sp * 4 * kGemmBK)) continue;
+    if ((size_t)sp * a.R * a.N > cap) break;
+    best = sp;
+  }
+  return best;
+}
+
 hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid *sr,
-                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+                       hipStream_t s, hipEvent_t ev0, hipEvent_t ev1, int form) {
   if (a.R <= 0) return hipSuccess;
   const bool pending = sr && sr->splits > 0;
   // a pending sum is taken only by the RMSNorm prologue over its residual,
@@ -2299,7 +2484,30 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
   const int t64 = ((a.R + 63) / 64) * ((a.N + 63) / 64);
   // A residual product with too few tiles to fill the chip splits K; its
   // sum is left to the RMSNorm prologue that follows it
-  const int splits = (sr && sr->ws && a.ep == EP_RESID) ? resid_splits(a, t64, sr->cap) : 1;
+  const bool may_split = sr && sr->ws && a.ep == EP_RESID;
+  int splits = may_split ? resid_splits(a, t64, sr->cap) : 1;
+  const int t128 = ((a.R + 127) / 128) * ((a.N + 127) / 128);
+  const int t64w = ((a.R + 63) / 64) * ((a.N + 127) / 128);
+  // Where the staged-tile kernel would take 128x128 tiles but get fewer
+  // than 200 workgroups (decode passes of 512-1024 rows), the weight-
+  // streaming kernel's 64x64 tiles run about 3.5x as many and finish
+  // sooner (576 rows: QKV 36.0 -> 29.3 us, W_o and W2 25.2 -> 17.7 us;
+  // W1, with 240 such tiles, stays: 26.1 us against 32.3).  form 2 forces
+  // it wherever it applies, form 1 never takes it.
+  const bool big = t128 * splits >= 176;
+  const int bsp = form == 1 ? 0 : bs_splits(a, may_split, may_split ? sr->cap : 0, form == 2);
+  if (bsp > 0 && (form == 2 || (big && t128 * splits < 200))) {
+    if (bsp > 1) {
+      b.ep = EP_PART;
+      b.out_f32 = sr->ws;
+      sr->a = b;
+      sr->splits = bsp;
+    }
+    const dim3 g(((a.R + 63) / 64) * ((a.N + 63) / 64), bsp);
+    if (b.gate) hipExtLaunchKernelGGL((k_gemm_bs<4, 1, 4, 2, true>), g, dim3(256), 0, s, ev0, ev1, 0, b);
+    else hipExtLaunchKernelGGL((k_gemm_bs<4, 1, 4, 2, false>), g, dim3(256), 0, s, ev0, ev1, 0, b);
+    return hipGetLastError();
+  }
   if (b.K % (splits * 2 * kGemmBK)) return hipErrorInvalidValue;  // K steps in pairs per split
   if (splits > 1) {
     b.ep = EP_PART;
@@ -2309,8 +2517,6 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
   }
   // the largest tile that still gives about 150-180 workgroups (measured at
   // the batch-16, batch-64 and prefill shapes)
-  const int t128 = ((a.R + 127) / 128) * ((a.N + 127) / 128);
-  const int t64w = ((a.R + 63) / 64) * ((a.N + 127) / 128);
 #define BLT_GEMM(BM, BN, WM, WN, KH, T)                                                           \
   if (b.gate)                                                                                     \
     hipExtLaunchKernelGGL((k_gemm_mfma<BM, BN, WM, WN, KH, true>), dim3(T, splits), dim3(512), 0, \
@@ -2516,6 +2722,35 @@ hipError_t launch_transpose(bool bf16, const void *src, void *dst, int n, hipStr
   else
     hipLaunchKernelGGL(k_transpose<float>, dim3(blocks), dim3(256), 0, s, (const float *)src,
                        (float *)dst, n);
+  return hipGetLastError();
+}
+
+// Fragment order of a bf16 matrix W[N][K] for the weight-streaming GEMM:
+// piece p = (ct * K/32 + kb) * 64 + l holds W[16 ct + l % 16][32 kb + 8 (l / 16) + e],
+// e = 0..7 (zeros past row N), so the B operand of one 16-column, 32-deep
+// MFMA block is 1 KB of consecutive memory, lane l's 16 bytes at 16 l.
+__global__ void k_frag_pack(const uint16_t *src, int N, int K, uint16_t *dst, int64_t pieces) {
+  const int KB = K / 32;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces;
+       p += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(p & 63);
+    const int64_t rest = p >> 6;
+    const int kb = (int)(rest % KB), ct = (int)(rest / KB);
+    const int n = 16 * ct + (l & 15), k = 32 * kb + 8 * (l >> 4);
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (n < N) v = *(const uint4 *)(src + (int64_t)n * K + k);
+    *(uint4 *)(dst + p * 8) = v;
+  }
+}
+
+size_t frag_elems(int N, int K) { return (size_t)((N + 15) / 16) * 16 * K; }
+
+hipError_t launch_frag_pack(const void *src, int N, int K, void *dst, hipStream_t s) {
+  if (K % 32) return hipErrorInvalidValue;
+  const int64_t pieces = (int64_t)((N + 15) / 16) * (K / 32) * 64;
+  const int blocks = (int)std::min<int64_t>((pieces + 255) / 256, 8192);
+  hipLaunchKernelGGL(k_frag_pack, dim3(blocks), dim3(256), 0, s, (const uint16_t *)src, N, K,
+                     (uint16_t *)dst, pieces);
   return hipGetLastError();
 }
 

@@ -134,7 +134,12 @@ blt_status blt_state_size(const blt_config *cfg, size_t *kv_bytes, size_t *cross
 
 /* Create a context bound to `hip_stream` (a hipStream_t, 0 = null stream)
  * and to the weights, which must stay alive and unchanged while the context
- * lives.  Allocates the library's workspace on the current device. */
+ * lives.  Allocates the library's workspace on the current device; for a
+ * bfloat16 context with max_rows >= 16 that includes a copy of the
+ * projection weights (every layer's W_qkv, W_o, W1, W2, the byte head,
+ * W_lat and the combined cross matrices, about 2 bytes per decoder
+ * parameter) in the fragment order that the matrix-core GEMM of passes of
+ * 16 rows or more streams, made here from the caller's weights. */
 blt_status blt_create(const blt_config *cfg, const blt_weights *w, void *hip_stream,
                       blt_ctx **out);
 blt_status blt_destroy(blt_ctx *ctx);
@@ -364,6 +369,20 @@ blt_status blt_attention_chunks(blt_ctx *ctx, int32_t chunks);
  * changes the rounding of the softmax sums, not what is computed.
  * BLT_EINVAL for other values. */
 blt_status blt_flash_key_groups(blt_ctx *ctx, int32_t groups);
+
+/* Kernel of the bfloat16 projections of passes of 16 rows or more (the MFMA
+ * GEMM path; passes of fewer rows use the GEMVs).  Two kernels: one stages
+ * both operand tiles through LDS (64x64 to 128x128 tiles); the other takes
+ * 64x64 tiles whose weights stream from a fragment-ordered copy straight
+ * into the matrix-core operands of the one wave that uses them, with only
+ * the activations staged through LDS.  form = 0 (the default) chooses by
+ * shape: the weight-streaming kernel for products of at most 1024 rows
+ * where the staged-tile kernel would take 128x128 tiles but fewer than 200
+ * workgroups, else the staged-tile kernel.  form = 1 forces the staged-tile
+ * kernel, form = 2 the weight-streaming kernel wherever it applies (K a
+ * multiple of 256).  The form changes the rounding of the sums (tile and K
+ * split), not what is computed.  BLT_EINVAL for other values. */
+blt_status blt_gemm_form(blt_ctx *ctx, int32_t form);
 
 /* Bandwidth proxy (wangzhan123.com Fast-BLT article, section six):
  * bytes_total = bytes_per_param * (n_dec * p_dec + n_encglob * (p_enc + p_glob)),

@@ -84,6 +84,7 @@ def test_null_context_and_weights():
     # the tuning controls and the session switches refuse a NULL context or session
     assert L.blt_attention_chunks(None, 1) == blt.BLT_EINVAL
     assert L.blt_flash_key_groups(None, 2) == blt.BLT_EINVAL
+    assert L.blt_gemm_form(None, 1) == blt.BLT_EINVAL
     assert L.blt_graphs_enable(None, 1) == blt.BLT_EINVAL
     assert L.blt_profile_enable(None, 1) == blt.BLT_EINVAL
     assert L.blt_session_device_blocks(None, 1) == blt.BLT_EINVAL
