@@ -107,7 +107,8 @@ FAMILIES = {
     "k_attn_mfma": ("BLT_PROF_ATTENTION", "hbm", "split-K decode self-attention (MFMA)"),
     "k_gemv_mfma": ("BLT_PROF_GEMV_MFMA", "hbm", "GEMV on MFMA (QKV, W1 of passes < 16 rows)"),
     "k_gemv": ("BLT_PROF_GEMV", "hbm", "dot-product GEMV (W_o, W2, head of passes < 16 rows)"),
-    "k_gemm_mfma": ("BLT_PROF_GEMM", "mfma", "MFMA GEMM (projections of passes >= 16 rows)"),
+    "k_gemm_mfma": ("BLT_PROF_GEMM", "mfma",
+                    "MFMA GEMMs (k_gemm_mfma, k_gemm_bs: projections of passes >= 16 rows)"),
 }
 
 
