@@ -78,8 +78,10 @@ def parse():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB ten times (the "
                          "reference kernel for scaling HBM traffic counters) and exit")
-    ap.add_argument("--device-blocks", action="store_true",
-                    help="time BLT-D with device-resident blocks (the host-driven blocks are timed beside them)")
+    ap.add_argument("--blocks", choices=("auto", "host", "device"), default="auto",
+                    help="how BLT-D blocks are driven (blt_session_device_blocks): chosen by the "
+                         "driver from the first blocks (auto), host-driven, or device-resident; "
+                         "the other ways are timed beside the main one")
     ap.add_argument("--plain", action="store_true",
                     help="only the timed generations of the main workload: no prefill timing, no "
                          "comparison with the other block driver, no event-timed passes, no legs, "
@@ -112,12 +114,16 @@ FAMILIES = {
 }
 
 
+BLOCK_MODES = {"host": 0, "device": 1, "auto": 2}
+
+
 def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_report=False,
-            device_blocks=False, compare=False, gemm_form=0):
+            blocks="auto", compare=False, gemm_form=0):
     """Time `steps` generations of workload `wl` (after `warmup` untimed ones),
-    then one event-timed generation per kernel family.  device_blocks: BLT-D
-    blocks after the first run on the device (blt_session_device_blocks);
-    compare: also time the same steps with the other way of driving blocks."""
+    then one event-timed generation per kernel family.  blocks: how BLT-D
+    blocks after the first are driven (blt_session_device_blocks: host-driven,
+    device-resident, or chosen by the driver from the first blocks); compare:
+    also time the same steps with the blocks driven each other way."""
     import bltgen
     dev = "cuda:0"
     w = bltgen.make_weights(wl)
@@ -165,8 +171,8 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
         unmask = {"one_step": blt.BLT_UNMASK_ONE_STEP, "entropy": blt.BLT_UNMASK_ENTROPY}.get(
             wl.unmask, blt.BLT_UNMASK_THRESHOLD)
         pid = policy_id(blt, wl)
-        use_dev = device_blocks and wl.policy == "blt_d"
-        blt.blt_session_device_blocks(dec.ctx, sess, use_dev)
+        mode = BLOCK_MODES[blocks] if wl.policy == "blt_d" else 0
+        blt.blt_session_device_blocks(dec.ctx, sess, mode)
 
         def step():
             blt.blt_session_generate(dec.ctx, sess, pid, wl.block, wl.alpha, wl.n_gen, unmask)
@@ -183,20 +189,23 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
         elapsed = sum(times)
         res = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
         if compare and wl.policy == "blt_d":
-            # the same steps with the blocks driven the other way
-            blt.blt_session_device_blocks(dec.ctx, sess, not use_dev)
-            step()
-            t0 = time.perf_counter()
-            for _ in range(steps):
+            # the same steps with the blocks driven each other way
+            for other in ("host", "device"):
+                if other == blocks:
+                    continue
+                blt.blt_session_device_blocks(dec.ctx, sess, BLOCK_MODES[other])
                 step()
-            torch.cuda.synchronize()
-            th = (time.perf_counter() - t0) / steps
-            hres = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
-            out["host_driven_blocks" if use_dev else "device_resident_blocks"] = {
-                "value": sum(r["n"] for r in hres) / th, "ms_per_step": 1e3 * th,
-                "same_bytes_and_counts": all(h["out"] == r["out"] and h["n_dec"] == r["n_dec"] and
-                                             h["n_eg"] == r["n_eg"] for h, r in zip(hres, res))}
-            blt.blt_session_device_blocks(dec.ctx, sess, use_dev)
+                t0 = time.perf_counter()
+                for _ in range(steps):
+                    step()
+                torch.cuda.synchronize()
+                th = (time.perf_counter() - t0) / steps
+                hres = [blt.blt_session_result(sess, b, wl.n_gen) for b in range(wl.batch)]
+                out["host_driven_blocks" if other == "host" else "device_resident_blocks"] = {
+                    "value": sum(r["n"] for r in hres) / th, "ms_per_step": 1e3 * th,
+                    "same_bytes_and_counts": all(h["out"] == r["out"] and h["n_dec"] == r["n_dec"] and
+                                                 h["n_eg"] == r["n_eg"] for h, r in zip(hres, res))}
+            blt.blt_session_device_blocks(dec.ctx, sess, mode)
         n_bytes = sum(r["n"] for r in res)
         n_dec = sum(r["n_dec"] for r in res)
         n_eg = sum(r["n_eg"] for r in res)
@@ -265,7 +274,7 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
                                                                      wl.p_enc, wl.p_glob)[1],
                 "proxy_gb_per_seq_pages_params": blt.blt_bw_model(n_dec, n_eg, wl.batch, PAGES_P_DEC,
                                                                    wl.p_enc, wl.p_glob)[1]},
-            "device_blocks": use_dev,
+            "blocks": blocks if wl.policy == "blt_d" else None,
             "config": {"workload": wl.name, "policy": wl.policy, "batch": wl.batch, "block": wl.block,
                        "alpha": wl.alpha, "unmask": wl.unmask, "layers": wl.n_layers,
                        "d_local": wl.d_model, "heads": wl.n_heads, "ffn": wl.d_ffn,
@@ -360,7 +369,7 @@ def main():
     small = ["k_attn_mfma", "k_gemv_mfma", "k_gemv"]
     fams = [] if args.no_prof else (small if wl.batch * (wl.block + 1) < 16 else ["k_attn_mfma", "k_gemm_mfma"])
     main_leg = run_leg(blt, torch, wl, args.steps, args.warmup, fams, args.no_graphs,
-                       prefill_report=not args.plain, device_blocks=args.device_blocks,
+                       prefill_report=not args.plain, blocks=args.blocks,
                        compare=not args.plain, gemm_form=args.gemm_form)
     out = {
         "metric": "decoded bytes/sec",
@@ -379,7 +388,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) decoder weights, N(0,1) latents, Zipf/uniform byte prompts)",
         "config": main_leg["config"],
     }
-    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill", "device_blocks",
+    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill", "blocks",
               "host_driven_blocks", "device_resident_blocks"):
         if k in main_leg:
             out[k] = main_leg[k]
@@ -390,7 +399,7 @@ def main():
                                   gemm_form=args.gemm_form)
         legs["peaked"] = run_leg(blt, torch, wl.replace(head_scale=12.0), max(1, args.steps // 2), 1,
                                  [] if args.no_prof else ["k_attn_mfma"], args.no_graphs,
-                                 device_blocks=args.device_blocks, compare=True, gemm_form=args.gemm_form)
+                                 blocks=args.blocks, compare=True, gemm_form=args.gemm_form)
         out["legs"] = legs
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_bytes, max(1, args.cpu_bytes // 2))

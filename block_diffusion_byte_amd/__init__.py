@@ -335,9 +335,10 @@ def blt_session_generate(ctx, sess, policy, block, alpha, n_gen, unmask=BLT_UNMA
     _check("blt_session_generate", lib().blt_session_generate(sess, C.byref(a)), ctx)
 
 
-def blt_session_device_blocks(ctx, sess, enable=True):
-    """Run the BLT-D blocks after the first one on the device (see blt.h)."""
-    _check("blt_session_device_blocks", lib().blt_session_device_blocks(sess, 1 if enable else 0), ctx)
+def blt_session_device_blocks(ctx, sess, mode=1):
+    """BLT-D blocks after the first one: 0 (or False) host-driven, 1 (or True)
+    on the device, 2 chosen from the first blocks (see blt.h)."""
+    _check("blt_session_device_blocks", lib().blt_session_device_blocks(sess, int(mode)), ctx)
 
 
 def blt_session_result(sess, b, cap):

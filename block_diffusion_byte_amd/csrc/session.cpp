@@ -74,8 +74,9 @@ struct blt_session {
   // sampling of the current generate call (temperature 0: greedy)
   blt_sampling smp{0.f, 1.f, 0};
   bool sampled = false;
-  // device-resident BLT-D blocks (blt_session_device_blocks)
-  bool device_blocks = false;
+  // device-resident BLT-D blocks (blt_session_device_blocks): 0 off, 1 on,
+  // 2 chosen from the first host-driven blocks
+  int device_blocks = 0;
   struct DevBufs {
     int B = 0;                       // block size the buffers were laid out for
     DevSeq *st = nullptr;
@@ -340,8 +341,19 @@ blt_status block_draft(blt_session *s, const std::vector<int> &act, const blt_po
 
 blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa);
 
+// Host-driven blocks the automatic choice of device-resident blocks watches
+// before it decides.
+constexpr int kAutoBlocks = 4;
+
 blt_status run_blt_d(blt_session *s, const blt_policy_args &pa) {
   bool first = true;
+  // automatic choice: device-resident blocks pay for every one of a block's B
+  // passes, including those a block no longer needs (their kernels return at
+  // once, but are still launched), so they are taken only when every watched
+  // block needed all B passes in every sequence (one byte committed per pass)
+  int watched = 0;
+  bool every_pass_needed = true;
+  std::vector<uint64_t> n_dec0(s->batch);
   while (true) {
     std::vector<int> act;
     for (int b = 0; b < s->batch; ++b)
@@ -351,12 +363,22 @@ blt_status run_blt_d(blt_session *s, const blt_policy_args &pa) {
     // after the first block (which appends the prompt's pending byte alone),
     // every block of every sequence has the same shape: the rest runs on the
     // device when it fits the context's rows
-    if (!first && s->device_blocks && !s->sampled && (int)act.size() == s->batch &&
+    const bool dev = s->device_blocks == 1 ||
+                     (s->device_blocks == 2 && watched >= kAutoBlocks && every_pass_needed);
+    if (!first && dev && !s->sampled && (int)act.size() == s->batch &&
         s->ctx->prof_family == BLT_PROF_OFF && s->batch * (2 * pa.block + 1) <= g.max_rows &&
         s->batch * (pa.block + 1) <= g.max_rows)
       return run_blt_d_device(s, pa);
-    first = false;
+    for (int b : act) n_dec0[b] = s->seqs[b].n_dec;
     S_TRY(block_draft(s, act, pa));
+    // the first block may be shorter (the prompt's pending byte); later ones
+    // are watched
+    if (!first) {
+      for (int b : act)
+        if (s->seqs[b].n_dec - n_dec0[b] != (uint64_t)pa.block) every_pass_needed = false;
+      ++watched;
+    }
+    first = false;
     for (int b : act)
       for (int j = 0; j < pa.block; ++j)
         commit(s->seqs[b], (uint8_t)s->host[s->o_blk + (size_t)b * pa.block + j], pa.n_gen);
@@ -773,9 +795,10 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
   return BLT_OK;
 }
 
-blt_status blt_session_device_blocks(blt_session *s, int32_t enable) {
+blt_status blt_session_device_blocks(blt_session *s, int32_t mode) {
   if (!s) return BLT_EINVAL;
-  s->device_blocks = enable != 0;
+  if (mode < 0 || mode > 2) return sfail(s, BLT_EINVAL, "blt_session_device_blocks: mode must be 0, 1 or 2");
+  s->device_blocks = mode;
   return BLT_OK;
 }
 

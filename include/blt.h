@@ -458,7 +458,7 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
                               int32_t *n_out, uint64_t *n_dec, uint64_t *n_encglob,
                               uint64_t *n_rounds, uint64_t *n_accepted);
 /* Device-resident BLT-D blocks (pytorch.kr summary, "BLT-D inference"):
- * with enable != 0, a BLT-D generation (greedy, any unmask rule, either block
+ * with mode 1, a BLT-D generation (greedy, any unmask rule, either block
  * mask) runs its first block as above and every later block with no host
  * round trip.  On the device, per block: the stand-in patcher's state and
  * the committed bytes decide the block's encoder/global pass (the latents of
@@ -471,9 +471,16 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
  * block is committed and the patcher runs over its bytes.  The block's
  * launches are captured once as a HIP graph (when graphs are enabled) and
  * replayed; the bytes and counters are read back at the end.  Results and
- * counts equal the host-driven path's.  Sampled generation and the other
- * policies are unaffected.  Default off. */
-blt_status blt_session_device_blocks(blt_session *s, int32_t enable);
+ * counts equal the host-driven path's.  A device-resident block always
+ * launches its B passes (those after the block is filled return at once but
+ * are still launched), so it pays off when every pass is needed.  Mode 2
+ * chooses: the first blocks run host-driven, and if each of the four after
+ * the first took all B decoder passes in every sequence (one byte committed
+ * per pass), the rest of the generation runs device-resident; else it stays
+ * host-driven.  Mode 0 (the default): host-driven blocks.  Sampled
+ * generation and the other policies are unaffected.  BLT_EINVAL for other
+ * modes. */
+blt_status blt_session_device_blocks(blt_session *s, int32_t mode);
 blt_status blt_session_destroy(blt_session *s);
 
 #ifdef __cplusplus

@@ -159,7 +159,7 @@ def _session(wl, w, inps, policy, n_gen, block, alpha, unmask=0, mask=0, max_row
     runs = []
     try:
         if device:
-            blt.blt_session_device_blocks(dec.ctx, sess, True)
+            blt.blt_session_device_blocks(dec.ctx, sess, int(device))
         blt.blt_session_prefill(dec.ctx, sess)
         for k in range(repeats):
             if k and between:
@@ -315,6 +315,45 @@ def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
         assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
         assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
     say(f"device blocks ({case}): 3 x {n_gen} bytes identical to the oracle; n_dec {[g['n_dec'] for g in got]}")
+
+
+@pytest.mark.parametrize("case", ["threshold", "peaked"])
+def test_tiny_fp32_auto_blocks_match_oracle_exactly(case):
+    """Blocks driven by the driver's own choice (mode 2): the first blocks run
+    host-driven; with the threshold rule every pass commits one byte, so after
+    four watched blocks the rest of the 10-block generation runs
+    device-resident; with the peaked head passes commit several bytes and the
+    blocks stay host-driven.  Either way, 3 sequences' bytes and pass counts
+    equal the oracle's; a mode outside 0..2 is refused."""
+    import block_diffusion_byte_amd as blt
+    wl = bltgen.WORKLOADS[0]
+    if case == "peaked":
+        wl = wl.replace(head_scale=12.0)
+    w = bltgen.make_weights(wl, gains="random")
+    n_gen, B, alpha = 40, 4, 0.7
+    inps, refs = [], []
+    for seq in range(3):
+        W, inp, inp64 = oracle_inputs(wl, w, seq)
+        inps.append(inp)
+        refs.append(loops.blt_d(W, wl, inp64, n_gen, B, alpha))
+    got = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, n_gen, B, alpha, device=2)
+    for b, (g, r) in enumerate(zip(got, refs)):
+        assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
+        assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
+    say(f"auto blocks ({case}): 3 x {n_gen} bytes identical to the oracle; n_dec {[g['n_dec'] for g in got]}")
+    import torch
+    dec = decoder_for(wl, w, max_batch=1, max_rows=64)
+    try:
+        table = torch.from_numpy(np.stack([inps[0]["latents"]])).to("cuda:0", dec.torch_dtype)
+        sess = blt.blt_session_create(dec.ctx, dec.state, [inps[0]["prompt"]], [inps[0]["prompt_patches"]],
+                                      [inps[0]["salt"]], table, wl.n_latents)
+        try:
+            with pytest.raises(blt.BltError):
+                blt.blt_session_device_blocks(dec.ctx, sess, 3)
+        finally:
+            blt.blt_session_destroy(sess)
+    finally:
+        dec.close()
 
 
 @pytest.mark.parametrize("graphs", [True, False])
