@@ -350,7 +350,10 @@ blt_status run_blt_d(blt_session *s, const blt_policy_args &pa) {
   // automatic choice: device-resident blocks pay for every one of a block's B
   // passes, including those a block no longer needs (their kernels return at
   // once, but are still launched), so they are taken only when every watched
-  // block needed all B passes in every sequence (one byte committed per pass)
+  // block needed all B passes (one byte committed per pass); and only for one
+  // sequence, whose short passes make the host's turn-around between them a
+  // visible share (with 16 sequences a pass is long, and the device block's
+  // extra work, B+1 rows recomputed and B+1 latent requests, outweighs it)
   int watched = 0;
   bool every_pass_needed = true;
   std::vector<uint64_t> n_dec0(s->batch);
@@ -363,8 +366,8 @@ blt_status run_blt_d(blt_session *s, const blt_policy_args &pa) {
     // after the first block (which appends the prompt's pending byte alone),
     // every block of every sequence has the same shape: the rest runs on the
     // device when it fits the context's rows
-    const bool dev = s->device_blocks == 1 ||
-                     (s->device_blocks == 2 && watched >= kAutoBlocks && every_pass_needed);
+    const bool dev = s->device_blocks == 1 || (s->device_blocks == 2 && s->batch == 1 &&
+                                               watched >= kAutoBlocks && every_pass_needed);
     if (!first && dev && !s->sampled && (int)act.size() == s->batch &&
         s->ctx->prof_family == BLT_PROF_OFF && s->batch * (2 * pa.block + 1) <= g.max_rows &&
         s->batch * (pa.block + 1) <= g.max_rows)

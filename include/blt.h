@@ -470,14 +470,18 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
  * a [MASK] (a pass in which no sequence has one does no work); the filled
  * block is committed and the patcher runs over its bytes.  The block's
  * launches are captured once as a HIP graph (when graphs are enabled) and
- * replayed; the bytes and counters are read back at the end.  Results and
- * counts equal the host-driven path's.  A device-resident block always
- * launches its B passes (those after the block is filled return at once but
- * are still launched), so it pays off when every pass is needed.  Mode 2
- * chooses: the first blocks run host-driven, and if each of the four after
- * the first took all B decoder passes in every sequence (one byte committed
- * per pass), the rest of the generation runs device-resident; else it stays
- * host-driven.  Mode 0 (the default): host-driven blocks.  Sampled
+ * replayed; the bytes and counters are read back at the end.  Where every
+ * pass has fewer than 16 rows (the GEMV path, whose row results do not
+ * depend on the pass) results and counts equal the host-driven path's; with
+ * 16 rows or more the first pass of a block holds other rows than the host
+ * driver's, the matrix-core GEMMs tile and round differently, and bytes may
+ * differ where two bytes tie within the rounding.  A device-resident block
+ * always launches its B passes (those after the block is filled return at
+ * once but are still launched), so it pays off when every pass is needed
+ * and passes are short.  Mode 2 chooses: for one sequence, the first blocks
+ * run host-driven, and if each of the four after the first took all B
+ * decoder passes (one byte committed per pass), the rest of the generation
+ * runs device-resident; else, and for more sequences, host-driven.  Mode 0 (the default): host-driven blocks.  Sampled
  * generation and the other policies are unaffected.  BLT_EINVAL for other
  * modes. */
 blt_status blt_session_device_blocks(blt_session *s, int32_t mode);

@@ -319,12 +319,13 @@ def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
 
 @pytest.mark.parametrize("case", ["threshold", "peaked"])
 def test_tiny_fp32_auto_blocks_match_oracle_exactly(case):
-    """Blocks driven by the driver's own choice (mode 2): the first blocks run
-    host-driven; with the threshold rule every pass commits one byte, so after
-    four watched blocks the rest of the 10-block generation runs
-    device-resident; with the peaked head passes commit several bytes and the
-    blocks stay host-driven.  Either way, 3 sequences' bytes and pass counts
-    equal the oracle's; a mode outside 0..2 is refused."""
+    """Blocks driven by the driver's own choice (mode 2), one sequence per
+    session: the first blocks run host-driven; with the threshold rule every
+    pass commits one byte, so after four watched blocks the rest of the
+    10-block generation runs device-resident; with the peaked head passes
+    commit several bytes and the blocks stay host-driven.  Either way each of
+    3 sequences' bytes and pass counts equal the oracle's; a mode outside 0..2
+    is refused."""
     import block_diffusion_byte_amd as blt
     wl = bltgen.WORKLOADS[0]
     if case == "peaked":
@@ -336,7 +337,7 @@ def test_tiny_fp32_auto_blocks_match_oracle_exactly(case):
         W, inp, inp64 = oracle_inputs(wl, w, seq)
         inps.append(inp)
         refs.append(loops.blt_d(W, wl, inp64, n_gen, B, alpha))
-    got = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, n_gen, B, alpha, device=2)
+    got = [_session(wl, w, [inp], blt.BLT_POLICY_BLT_D, n_gen, B, alpha, device=2)[0] for inp in inps]
     for b, (g, r) in enumerate(zip(got, refs)):
         assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
         assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
