@@ -180,6 +180,7 @@ struct PassLaunch {
   int attn_wg = 1;                   // 2: eight-wave workgroups, one per (sequence, head)
   const SeqDesc *seq1 = nullptr;     // host copy of a one-sequence pass's descriptor (direct launches)
   int32_t *gate = nullptr;           // device-resident passes: sequences with masks left (0: skip)
+  int gate_late = 0;                 // 1: the streaming kernels test the gate before their stores
   int32_t *pass_count = nullptr;     // device-resident passes: decoder passes per slot
 };
 
@@ -250,6 +251,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
     }
     GemmArgs ag = a;
     ag.gate = p.gate;
+    ag.gate_late = p.gate_late;
     HIP_TRY(c, launch_gemm(bf, ag, w.xb, &c->split, s, e0, e1, c->gemm_form));
     return BLT_OK;
   };
@@ -288,7 +290,7 @@ blt_status enqueue_pass(blt_ctx *c, const PassLaunch &p, hipStream_t s, const Pa
     HIP_TRY(c, launch_attention(bf, w.q, st->kv, geo, l, w.seqs, S, p.seq1, p.grid_chunks,
                                 p.attn_sub, p.attn_wg, c->max_chunks,
                                 p.flash_tiles, w.rows, R, w.part, w.xa, e0, e1, ev_flash, s, p.gate,
-                                c->flash_kg));
+                                c->flash_kg, p.gate_late));
     // h += W_o a
     a = base_args(c); a.R = R; a.rows = w.rows;
     a.W = lw.wo; a.Wf = fl ? fl->wo : nullptr; a.N = d; a.K = d;
@@ -441,10 +443,11 @@ blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,
 blt_status enqueue_device_pass(blt_ctx *c, const blt_state *st, int R, int S, int grid_chunks,
                                RowDesc *rows, SeqDesc *seqs, int32_t *block_tok, float alpha,
                                int mode, int32_t *masked_left, int32_t *gate, int32_t *pass_count,
-                               int rows_per_seq, hipStream_t s) {
+                               int rows_per_seq, hipStream_t s, bool gate_late) {
   PassLaunch p{R, S, grid_chunks, 0, st, block_tok, nullptr, true, alpha, mode, masked_left,
                nullptr, nullptr, nullptr, 0.0, 0.0, false, SampleArgs{0.f, 0.f, 0}};
   p.gate = gate;
+  p.gate_late = gate_late ? 1 : 0;
   p.pass_count = pass_count;
   choose_attention(c, p, grid_chunks, rows_per_seq);
   PassWs w = c->ws;

@@ -146,7 +146,7 @@ blt_status prof_collect(blt_ctx *c);
 blt_status enqueue_device_pass(blt_ctx *c, const blt_state *st, int R, int S, int grid_chunks,
                                RowDesc *rows, SeqDesc *seqs, int32_t *block_tok, float alpha,
                                int mode, int32_t *masked_left, int32_t *gate, int32_t *pass_count,
-                               int rows_per_seq, hipStream_t s);
+                               int rows_per_seq, hipStream_t s, bool gate_late);
 blt_status latents_from_device(blt_ctx *c, const blt_state *st, int m, const int64_t *offs,
                                const void *table, hipStream_t s);
 blt_status run_pass(blt_ctx *c, const blt_state *st, std::vector<RowDesc> &rows,

@@ -70,6 +70,9 @@ struct GemmArgs {
   // device-resident passes: the number of sequences that still have masked
   // positions; when it reads 0 the kernel returns at once (nullptr: always run)
   const int32_t *gate;
+  // with a gate: 1 tests it only before the kernel's first store (the GEMVs),
+  // for passes the driver expects to have work
+  int gate_late;
 };
 
 // Cache rows per sequence and head: max_ctx rounded up to whole attention
@@ -189,7 +192,8 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
                             int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
-                            hipStream_t s, const int32_t *gate = nullptr, int flash_kg = 0);
+                            hipStream_t s, const int32_t *gate = nullptr, int flash_kg = 0,
+                            int gate_late = 0);
 bool gemv_supported(bool bf16, int K);
 // report_entropy: conf_out receives each row's entropy instead of its confidence.
 // smp (nullable): rows with ctr >= 0 draw their byte by temperature / top-p

@@ -45,6 +45,25 @@ template <bool GT> __device__ __forceinline__ bool gate_closed(const int32_t *ga
   else return false;
 }
 
+// The same gate read late, for the kernels of a decoder pass that stream
+// large operands (the GEMVs and the split-K attention) when the driver
+// expects every pass to have work: GT = 2 loads the gate at entry but tests
+// it only after the kernel's loads and products, before its first global
+// store, so its round trip overlaps theirs instead of holding them back
+// (measured 0.2-0.4 us per launch).  A closed pass then loads and computes
+// (its operands are valid: the pass's descriptors stay in place) and stores
+// nothing.  GT = 1 tests at entry, GT = 0 has no gate.
+template <int GT> __device__ __forceinline__ bool gate_closed_entry(const int32_t *gate) {
+  if constexpr (GT == 1) return *gate == 0;
+  else return false;
+}
+template <int GT> __device__ __forceinline__ int gate_open_late(const int32_t *gate) {
+  // a scalar load among the kernel-argument loads (as a vector load the
+  // compiler moved it to a scalar register at once and waited for it there)
+  if constexpr (GT == 2) return *gate;
+  else return 1;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __device__ __forceinline__ uint16_t f2bf(float f) {
@@ -324,9 +343,10 @@ __device__ __forceinline__ uint4 stage_value(const StageRaw<BF, PRO> &st, uint4 
   }
 }
 
-template <bool BF, int G, int NC, int RB, int PRO, bool GT>
+template <bool BF, int G, int NC, int RB, int PRO, int GT>
 __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
-  if (gate_closed<GT>(a.gate)) return;
+  if (gate_closed_entry<GT>(a.gate)) return;
+  const int open = gate_open_late<GT>(a.gate);   // GT = 2: tested before the first store
   constexpr int EPC = Act<BF>::EPC;
   constexpr int RPW = 64 / G;
   constexpr int Q = NC * G, KC = 4 * Q;      // chunks per wave quarter, per row
@@ -436,6 +456,7 @@ __global__ __launch_bounds__(256) void k_gemv(GemmArgs a) {
       }
     }
     __syncthreads();
+    if (!open) return;                       // uniform: a closed device-resident pass
     // one epilogue item per thread; the first row block uses the operands
     // loaded at entry, later blocks load their own
     if (a.qkv_rope) {
@@ -1020,9 +1041,10 @@ __device__ __forceinline__ float sum_lane_groups(float x) {
 // the pass: the MFMA keeps rows apart and no order depends on the row count.
 // Its cost hardly grows with the row count (a cold pass of 1 to 9 rows at the
 // 1B-class shapes runs in the time of a plain read of the weights).
-template <int PRO, int SB, bool GT>
+template <int PRO, int SB, int GT>
 __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
-  if (gate_closed<GT>(a.gate)) return;
+  if (gate_closed_entry<GT>(a.gate)) return;
+  const int open = gate_open_late<GT>(a.gate);   // GT = 2: tested before the first store
   const int t = threadIdx.x, w = t >> 6, l = t & 63, lr = l & 15, lq = l >> 4;
   const int n0 = blockIdx.x * 16;
   const int kq = a.K / 4, steps = kq / 32;  // this wave's K range in 32-wide steps (a multiple of SB)
@@ -1106,6 +1128,7 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
     if (lq == 0) ssq[w][lr] = ss;
   }
   __syncthreads();
+  if (!open) return;                        // uniform: a closed device-resident pass
   const int r = t >> 4, c = t & 15;         // one output per thread: row r, column n0 + c
   if (r >= a.R) return;
   float rinv = 1.f;
@@ -1150,14 +1173,15 @@ __global__ __launch_bounds__(256) void k_gemv_mfma(GemmArgs a) {
 // eight waves in two groups that take alternate chunks (group 0 the even
 // ones), so one workgroup covers a (sequence, head) with twice the loads in
 // flight; their eight (o, m, l) are combined the same way.
-template <int DH, bool PIPE, int WG, bool GT>
+template <int DH, bool PIPE, int WG, int GT>
 __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const void *kvp, KVGeom g,
                                                         int layer, const SeqDesc *seqs,
                                                         const RowDesc *rows, float *part,
                                                         int max_chunks, int chunks_per_wg,
                                                         int direct, void *a_out, SeqDesc sd_arg,
                                                         int use_sd_arg, const int32_t *gate) {
-  if (gate_closed<GT>(gate)) return;   // device-resident pass with nothing left to do
+  if (gate_closed_entry<GT>(gate)) return;
+  const int open = gate_open_late<GT>(gate);  // GT = 2: tested before the first store
   constexpr int NSUB = PIPE ? 2 : 1;          // > 1: the prefetching loop
   constexpr int NWV = 4 * WG;                 // waves
   constexpr int KS = DH / 32;                 // k-steps of the score product
@@ -1313,6 +1337,7 @@ __global__ __launch_bounds__(256 * WG) void k_attn_mfma(const float *q, const vo
       lw[w][lr] = l;
     }
     __syncthreads();
+    if (!open) return;                        // uniform: a closed device-resident pass
     for (int i = t; i < nr * DH; i += 256 * WG) {
       const int r = i / DH, e = i - r * DH;
       if (kends[r] <= key0) continue;
@@ -2307,10 +2332,13 @@ hipError_t gemv_launch(const GemmArgs &a, hipStream_t s, hipEvent_t ev0, hipEven
   constexpr int KC = 4 * NC * G;
   if (a.K != KC * Act<BF>::EPC) return hipErrorInvalidValue;
   const size_t lds = (size_t)RB * KC * 16;
-  const bool gt = a.gate != nullptr;
-  const void *fn = gt ? (const void *)k_gemv<BF, G, NC, RB, PRO, true>
-                      : (const void *)k_gemv<BF, G, NC, RB, PRO, false>;
-  static bool attr[2] = {false, false};
+  // gate form: 0 none, 1 tested at entry, 2 tested before the stores (bf16
+  // passes the driver expects to have work)
+  const int gt = a.gate == nullptr ? 0 : (BF && a.gate_late ? 2 : 1);
+  const void *fn = gt == 2   ? (const void *)k_gemv<BF, G, NC, RB, PRO, BF ? 2 : 1>
+                   : gt == 1 ? (const void *)k_gemv<BF, G, NC, RB, PRO, 1>
+                             : (const void *)k_gemv<BF, G, NC, RB, PRO, 0>;
+  static bool attr[3] = {false, false, false};
   if (!attr[gt]) {
     // allow dynamic LDS up to the 160 KB of a gfx950 CU, less the static part
     hipFuncAttributes fa;
@@ -2323,10 +2351,12 @@ hipError_t gemv_launch(const GemmArgs &a, hipStream_t s, hipEvent_t ev0, hipEven
   }
   constexpr int RPW = 64 / G;
   const dim3 grid((a.N + RPW - 1) / RPW);
-  if (gt)
-    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, true>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
+  if (gt == 2)
+    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, BF ? 2 : 1>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
+  else if (gt == 1)
+    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, 1>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
   else
-    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, false>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
+    hipExtLaunchKernelGGL((k_gemv<BF, G, NC, RB, PRO, 0>), grid, dim3(256), lds, s, ev0, ev1, 0, a);
   return hipGetLastError();
 }
 
@@ -2441,7 +2471,8 @@ hipError_t launch_gemm(bool bf16, const GemmArgs &a, void *xnorm_ws, SplitResid 
     hipExtLaunchKernelGGL((k_gemv_mfma<PRO_NORM, SB, GT>), g, dim3(256), 0, s, ev0, ev1, 0, a);  \
   else hipExtLaunchKernelGGL((k_gemv_mfma<PRO_PLAIN, SB, GT>), g, dim3(256), 0, s, ev0, ev1, 0, a);
 #define BLT_GEMV_MFMA(SB)                                                                        \
-  if (a.gate) { BLT_GEMV_MFMA_GT(SB, true) } else { BLT_GEMV_MFMA_GT(SB, false) }
+  if (a.gate && a.gate_late) { BLT_GEMV_MFMA_GT(SB, 2) }                                       \
+  else if (a.gate) { BLT_GEMV_MFMA_GT(SB, 1) } else { BLT_GEMV_MFMA_GT(SB, 0) }
       if (steps % 8 == 0) { BLT_GEMV_MFMA(8) }
       else if (steps % 4 == 0) { BLT_GEMV_MFMA(4) }
       else if (steps % 2 == 0) { BLT_GEMV_MFMA(2) }
@@ -2567,7 +2598,7 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                         int max_chunks, int flash_tiles,
                         const RowDesc *rows, int R, float *part, void *a_out, hipEvent_t ev0,
                         hipEvent_t ev1, bool ev_flash, hipStream_t s, const int32_t *gate,
-                        int flash_kg) {
+                        int flash_kg, int gate_late) {
   if constexpr (BF) {
     if (flash_tiles > 0) {
       const dim3 fg((flash_tiles + 1) / 2, g.n_heads, n_seq);   // pairs of row tiles
@@ -2612,7 +2643,8 @@ static void attn_launch(const float *q, const void *kv, KVGeom g, int layer, con
                        layer, seqs, rows, part, max_chunks, nsub, direct, a_out, sd_arg,          \
                        use_sd_arg, gate);
 #define BLT_SPLITK(PIPE, WG)                                                                      \
-  if (gate) { BLT_SPLITK_GT(PIPE, WG, true) } else { BLT_SPLITK_GT(PIPE, WG, false) }
+  if (gate && gate_late) { BLT_SPLITK_GT(PIPE, WG, 2) }                                            \
+  else if (gate) { BLT_SPLITK_GT(PIPE, WG, 1) } else { BLT_SPLITK_GT(PIPE, WG, 0) }
     if constexpr (DH <= 64) {
       if (wg == 2) { BLT_SPLITK(true, 2) }
       else if (nsub > 1) { BLT_SPLITK(true, 1) }
@@ -2651,15 +2683,15 @@ hipError_t launch_attention(bool bf16, const float *q, const void *kv, KVGeom g,
                             const SeqDesc *seqs, int n_seq, const SeqDesc *sd_host,
                             int grid_chunks, int nsub, int wg, int max_chunks, int flash_tiles, const RowDesc *rows, int R,
                             float *part, void *a_out, hipEvent_t ev0, hipEvent_t ev1, bool ev_flash,
-                            hipStream_t s, const int32_t *gate, int flash_kg) {
+                            hipStream_t s, const int32_t *gate, int flash_kg, int gate_late) {
   if (flash_tiles > 0 && !bf16) return hipErrorInvalidValue;   // the causal kernel is bf16 only
 #define BLT_ATTN(dh)                                                                              \
   if (bf16) attn_launch<true, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,   \
                                   max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1,        \
-                                  ev_flash, s, gate, flash_kg);                                   \
+                                  ev_flash, s, gate, flash_kg, gate_late);                        \
   else attn_launch<false, dh>(q, kv, g, layer, seqs, n_seq, sd_host, grid_chunks, nsub, wg,       \
                               max_chunks, flash_tiles, rows, R, part, a_out, ev0, ev1, ev_flash, s, \
-                              gate, flash_kg);
+                              gate, flash_kg, gate_late);
   switch (g.d_head) {
     case 32: BLT_ATTN(32) break;
     case 64: BLT_ATTN(64) break;

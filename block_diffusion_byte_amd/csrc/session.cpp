@@ -454,13 +454,17 @@ blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa) {
                  g.max_latents, s->n_lat, g.d_global, g.n_layers, g.d_model, (int64_t)s->n_lat};
   // attention over the longest context of the last block
   const int grid_chunks = (n_max + nb * B + kAttnChunk - 1) / kAttnChunk;
+  // chosen automatically, the blocks are known to need all their passes: the
+  // streaming kernels then test the gate only before their stores
+  const bool late = s->device_blocks == 2;
   auto enqueue_block = [&](hipStream_t q) -> blt_status {
     S_HIP(s, launch_block_plan(a, q));
     S_TRY(latents_from_device(c, &s->st, S * (B + 1), db.lat_offs, s->table, q));
     for (int p = 0; p < B; ++p)
       S_TRY(enqueue_device_pass(c, &s->st, S * (p ? B : 2 * B + 1), S, grid_chunks, p ? db.rows1 : db.rows0,
                                 p ? db.seqs1 : db.seqs0, s->dev + s->o_blk, pa.alpha, (int)pa.unmask,
-                                mapped(s, s->o_masked), gate, pass_count, p ? B : 2 * B + 1, q));
+                                mapped(s, s->o_masked), gate, pass_count, p ? B : 2 * B + 1, q,
+                                late));
     S_HIP(s, launch_block_commit(a, q));
     return BLT_OK;
   };
