@@ -84,7 +84,7 @@ struct blt_session {
     RowDesc *rows0 = nullptr, *rows1 = nullptr;
     SeqDesc *seqs0 = nullptr, *seqs1 = nullptr;
     int64_t *lat_offs = nullptr;
-    int32_t *ints = nullptr;         // gate, then pass counts [batch], then n_eg [batch]
+    int32_t *ints = nullptr;         // gate, then pass counts, n_eg and masked counts [batch] each
   } db;
 };
 
@@ -411,7 +411,7 @@ blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa) {
         !ok(hipMalloc(&db.rows1, sizeof(RowDesc) * (size_t)S * B)) ||
         !ok(hipMalloc(&db.seqs0, sizeof(SeqDesc) * S)) || !ok(hipMalloc(&db.seqs1, sizeof(SeqDesc) * S)) ||
         !ok(hipMalloc(&db.lat_offs, sizeof(int64_t) * 2 * (size_t)S * (B + 1))) ||
-        !ok(hipMalloc(&db.ints, sizeof(int32_t) * (1 + 2 * (size_t)S)))) {
+        !ok(hipMalloc(&db.ints, sizeof(int32_t) * (1 + 3 * (size_t)S)))) {
       free_dev_blocks(s);
       return sfail(s, BLT_EHIP, "session: device block buffers could not be allocated");
     }
@@ -449,8 +449,11 @@ blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa) {
   S_HIP(s, hipMemcpyAsync(db.x, xs.data(), sizeof(int32_t) * xs.size(), hipMemcpyHostToDevice, hs));
   S_HIP(s, hipMemcpyAsync(db.ints, ints.data(), sizeof(int32_t) * ints.size(), hipMemcpyHostToDevice, hs));
   int32_t *gate = db.ints, *pass_count = db.ints + 1, *n_eg = db.ints + 1 + S;
+  // the per-pass masked counts stay on the device (no host reads them here;
+  // in host-mapped memory every unmask kernel would wait for its PCIe write)
+  int32_t *masked_dev = db.ints + 1 + 2 * S;
   DevBlockArgs a{db.st, db.x, X, S, B, pa.block_mask == BLT_BLOCK_CAUSAL ? 1 : 0, db.rows0, db.seqs0,
-                 db.rows1, db.seqs1, db.lat_offs, s->dev + s->o_blk, mapped(s, s->o_masked), gate, n_eg,
+                 db.rows1, db.seqs1, db.lat_offs, s->dev + s->o_blk, masked_dev, gate, n_eg,
                  g.max_latents, s->n_lat, g.d_global, g.n_layers, g.d_model, (int64_t)s->n_lat};
   // attention over the longest context of the last block
   const int grid_chunks = (n_max + nb * B + kAttnChunk - 1) / kAttnChunk;
@@ -463,7 +466,7 @@ blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa) {
     for (int p = 0; p < B; ++p)
       S_TRY(enqueue_device_pass(c, &s->st, S * (p ? B : 2 * B + 1), S, grid_chunks, p ? db.rows1 : db.rows0,
                                 p ? db.seqs1 : db.seqs0, s->dev + s->o_blk, pa.alpha, (int)pa.unmask,
-                                mapped(s, s->o_masked), gate, pass_count, p ? B : 2 * B + 1, q,
+                                masked_dev, gate, pass_count, p ? B : 2 * B + 1, q,
                                 late));
     S_HIP(s, launch_block_commit(a, q));
     return BLT_OK;
