@@ -75,7 +75,8 @@ struct blt_session {
   blt_sampling smp{0.f, 1.f, 0};
   bool sampled = false;
   // device-resident BLT-D blocks (blt_session_device_blocks): 0 off, 1 on,
-  // 2 chosen from the first host-driven blocks
+  // 2 chosen from the first host-driven blocks, 3 on with the streaming
+  // kernels testing the gate late
   int device_blocks = 0;
   struct DevBufs {
     int B = 0;                       // block size the buffers were laid out for
@@ -366,8 +367,9 @@ blt_status run_blt_d(blt_session *s, const blt_policy_args &pa) {
     // after the first block (which appends the prompt's pending byte alone),
     // every block of every sequence has the same shape: the rest runs on the
     // device when it fits the context's rows
-    const bool dev = s->device_blocks == 1 || (s->device_blocks == 2 && s->batch == 1 &&
-                                               watched >= kAutoBlocks && every_pass_needed);
+    const bool dev = s->device_blocks == 1 || s->device_blocks == 3 ||
+                     (s->device_blocks == 2 && s->batch == 1 && watched >= kAutoBlocks &&
+                      every_pass_needed);
     if (!first && dev && !s->sampled && (int)act.size() == s->batch &&
         s->ctx->prof_family == BLT_PROF_OFF && s->batch * (2 * pa.block + 1) <= g.max_rows &&
         s->batch * (pa.block + 1) <= g.max_rows)
@@ -457,9 +459,10 @@ blt_status run_blt_d_device(blt_session *s, const blt_policy_args &pa) {
                  g.max_latents, s->n_lat, g.d_global, g.n_layers, g.d_model, (int64_t)s->n_lat};
   // attention over the longest context of the last block
   const int grid_chunks = (n_max + nb * B + kAttnChunk - 1) / kAttnChunk;
-  // chosen automatically, the blocks are known to need all their passes: the
-  // streaming kernels then test the gate only before their stores
-  const bool late = s->device_blocks == 2;
+  // chosen automatically, the blocks are known to need all their passes (or
+  // the caller says so, mode 3): the streaming kernels then test the gate
+  // only before their stores
+  const bool late = s->device_blocks == 2 || s->device_blocks == 3;
   auto enqueue_block = [&](hipStream_t q) -> blt_status {
     S_HIP(s, launch_block_plan(a, q));
     S_TRY(latents_from_device(c, &s->st, S * (B + 1), db.lat_offs, s->table, q));
@@ -807,7 +810,7 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
 
 blt_status blt_session_device_blocks(blt_session *s, int32_t mode) {
   if (!s) return BLT_EINVAL;
-  if (mode < 0 || mode > 2) return sfail(s, BLT_EINVAL, "blt_session_device_blocks: mode must be 0, 1 or 2");
+  if (mode < 0 || mode > 3) return sfail(s, BLT_EINVAL, "blt_session_device_blocks: mode must be 0..3");
   s->device_blocks = mode;
   return BLT_OK;
 }

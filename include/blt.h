@@ -481,7 +481,13 @@ blt_status blt_session_result(const blt_session *s, int32_t b, uint8_t *out, int
  * and passes are short.  Mode 2 chooses: for one sequence, the first blocks
  * run host-driven, and if each of the four after the first took all B
  * decoder passes (one byte committed per pass), the rest of the generation
- * runs device-resident; else, and for more sequences, host-driven.  Mode 0 (the default): host-driven blocks.  Sampled
+ * runs device-resident; else, and for more sequences, host-driven.  In
+ * blocks run device-resident by mode 2, the GEMVs and the split-K attention
+ * test the gate only before their first store (a closed pass still loads
+ * and computes, and stores nothing), which saves the gate's round trip
+ * where every pass has work.  Mode 3: device-resident after the first
+ * block, like mode 1, with that late test (for callers whose passes all
+ * have work).  Mode 0 (the default): host-driven blocks.  Sampled
  * generation and the other policies are unaffected.  BLT_EINVAL for other
  * modes. */
 blt_status blt_session_device_blocks(blt_session *s, int32_t mode);

@@ -283,14 +283,18 @@ def test_tiny_fp32_degenerate_and_largest_blocks_match_oracle(case):
     say(f"{case}: 3 sequences x {n_gen} bytes identical; n_dec {[g['n_dec'] for g in got]}")
 
 
+@pytest.mark.parametrize("dmode", [1, 3])
 @pytest.mark.parametrize("case", ["threshold", "peaked", "entropy", "one_step", "causal"])
-def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
+def test_tiny_fp32_device_blocks_match_oracle_exactly(case, dmode):
     """BLT-D with every block after the first planned, decoded, committed and
     patched on the device (one captured graph per block, one readback at the
     end): 3 sequences, bytes and decoder / encoder-global pass counts equal
     to the oracle's, for the threshold rule (one commit per pass), the peaked
     head (several commits per pass, so later passes of a block do no work),
-    entropy-bounded and one-step unmasking, and the causal block mask."""
+    entropy-bounded and one-step unmasking, and the causal block mask.  Device
+    mode 3 runs the same with the streaming kernels testing the gate only before
+    their stores: the passes of a block that no longer needs them (peaked,
+    entropy, one-step) load and compute and must store nothing."""
     import block_diffusion_byte_amd as blt
     wl = bltgen.WORKLOADS[0]
     B, alpha, unmask, mode, causal = 4, 0.7, None, blt.BLT_UNMASK_THRESHOLD, False
@@ -310,11 +314,12 @@ def test_tiny_fp32_device_blocks_match_oracle_exactly(case):
         inps.append(inp)
         refs.append(loops.blt_d(W, wl, inp64, n_gen, B, alpha, block_causal=causal, unmask=unmask))
     got = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, n_gen, B, alpha, mode,
-                   blt.BLT_BLOCK_CAUSAL if causal else blt.BLT_BLOCK_BIDIR, device=True)
+                   blt.BLT_BLOCK_CAUSAL if causal else blt.BLT_BLOCK_BIDIR, device=dmode)
     for b, (g, r) in enumerate(zip(got, refs)):
         assert list(g["out"]) == r.out, f"seq {b}: bytes differ"
         assert (g["n_dec"], g["n_eg"]) == (r.n_dec, r.n_eg), f"seq {b}: counts differ"
-    say(f"device blocks ({case}): 3 x {n_gen} bytes identical to the oracle; n_dec {[g['n_dec'] for g in got]}")
+    say(f"device blocks mode {dmode} ({case}): 3 x {n_gen} bytes identical to the oracle; "
+        f"n_dec {[g['n_dec'] for g in got]}")
 
 
 @pytest.mark.parametrize("case", ["threshold", "peaked"])
@@ -324,7 +329,7 @@ def test_tiny_fp32_auto_blocks_match_oracle_exactly(case):
     pass commits one byte, so after four watched blocks the rest of the
     10-block generation runs device-resident; with the peaked head passes
     commit several bytes and the blocks stay host-driven.  Either way each of
-    3 sequences' bytes and pass counts equal the oracle's; a mode outside 0..2
+    3 sequences' bytes and pass counts equal the oracle's; a mode outside 0..3
     is refused."""
     import block_diffusion_byte_amd as blt
     wl = bltgen.WORKLOADS[0]
@@ -350,29 +355,34 @@ def test_tiny_fp32_auto_blocks_match_oracle_exactly(case):
                                       [inps[0]["salt"]], table, wl.n_latents)
         try:
             with pytest.raises(blt.BltError):
-                blt.blt_session_device_blocks(dec.ctx, sess, 3)
+                blt.blt_session_device_blocks(dec.ctx, sess, 4)
         finally:
             blt.blt_session_destroy(sess)
     finally:
         dec.close()
 
 
+@pytest.mark.parametrize("mode", [1, 3])
 @pytest.mark.parametrize("graphs", [True, False])
-def test_bf16_device_blocks_equal_host_blocks(graphs):
+def test_bf16_device_blocks_equal_host_blocks(graphs, mode):
     """bfloat16 decoder, 2 sequences: the device-resident blocks give exactly
     the bytes and counts of the host-driven blocks (the recomputed prefix row
     reads the same latent through the same kernels, and a row's result does
-    not depend on the rows beside it)."""
+    not depend on the rows beside it).  The peaked head commits several bytes
+    per pass, so blocks end before their last passes: mode 3 runs those
+    closed passes through the bf16 GEMVs and split-K attention that test the
+    gate only before their stores, which must leave every result as mode 1
+    and the host driver do."""
     import block_diffusion_byte_amd as blt
     wl = MINI_BF16.replace(head_scale=12.0)
     w = bltgen.make_weights(wl)
     inps = [bltgen.make_sequence_inputs(wl, b) for b in range(2)]
     host = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 4, 0.5, graphs=graphs)
-    dev = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 4, 0.5, graphs=graphs, device=True)
+    dev = _session(wl, w, inps, blt.BLT_POLICY_BLT_D, 40, 4, 0.5, graphs=graphs, device=mode)
     for b in range(2):
         assert dev[b]["out"] == host[b]["out"], f"seq {b}: bytes differ"
         assert (dev[b]["n_dec"], dev[b]["n_eg"]) == (host[b]["n_dec"], host[b]["n_eg"])
-    say(f"bf16 device blocks (graphs {graphs}) equal host blocks; n_dec {[r['n_dec'] for r in dev]}")
+    say(f"bf16 device blocks mode {mode} (graphs {graphs}) equal host blocks; n_dec {[r['n_dec'] for r in dev]}")
 
 
 def test_tiny_fp32_entropy_bounded_session_exact():
