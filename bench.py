@@ -275,6 +275,10 @@ def run_leg(blt, torch, wl, steps, warmup, families, no_graphs=False, prefill_re
                 "proxy_gb_per_seq_pages_params": blt.blt_bw_model(n_dec, n_eg, wl.batch, PAGES_P_DEC,
                                                                    wl.p_enc, wl.p_glob)[1]},
             "blocks": blocks if wl.policy == "blt_d" else None,
+            "blocks_note": ("auto: one sequence whose watched blocks took every pass runs the rest "
+                            "device-resident with the gate tested before each store; "
+                            "device_resident_blocks: mode 1, the gate tested at entry")
+            if wl.policy == "blt_d" else None,
             "config": {"workload": wl.name, "policy": wl.policy, "batch": wl.batch, "block": wl.block,
                        "alpha": wl.alpha, "unmask": wl.unmask, "layers": wl.n_layers,
                        "d_local": wl.d_model, "heads": wl.n_heads, "ffn": wl.d_ffn,
@@ -388,7 +392,7 @@ def main():
         "data": "synthetic (seeded N(0,0.02) decoder weights, N(0,1) latents, Zipf/uniform byte prompts)",
         "config": main_leg["config"],
     }
-    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill", "blocks",
+    for k in ("roofline", "step_roofline", "kernels", "counters", "prefill", "blocks", "blocks_note",
               "host_driven_blocks", "device_resident_blocks"):
         if k in main_leg:
             out[k] = main_leg[k]
